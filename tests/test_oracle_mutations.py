@@ -1,0 +1,57 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case copies ``oracle/``, ``workloads/`` and the oracle pin tests into a
+temporary directory, plants one mistake in the copied oracle (a wrong index,
+a dropped term, a swapped operand, an off-by-one), and runs the pin tests on
+the copy in a child process.  The pins must fail.  Nothing here touches the
+GPU or the HIP path; the mistakes live only in the temporary copy.
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = [
+    # (id, file, original text, planted mistake, pin files to run)
+    ("gqa-map", "attention.py", "g = h // group", "g = h % num_kv_heads", ["test_oracle_attention.py"]),
+    ("causal-off-by-one", "attention.py", "(t <= pos)", "(t < pos)", ["test_oracle_attention.py"]),
+    ("drop-cached-offset", "attention.py", "pos = c + np.arange(n)[:, None]", "pos = np.arange(n)[:, None]", ["test_oracle_attention.py"]),
+    ("drop-scale", "attention.py", "s = scale * (Q[:, h, :] @ K[:, g, :].T)", "s = (Q[:, h, :] @ K[:, g, :].T)", ["test_oracle_attention.py"]),
+    ("values-from-keys", "attention.py", "(w @ V[:, g, :])", "(w @ K[:, g, :])", ["test_oracle_attention.py"]),
+    ("normalise-over-all-rows", "attention.py", "/ w.sum(axis=1, keepdims=True)", "/ w.sum()", ["test_oracle_attention.py"]),
+    ("row-in-block", "attention.py", "cache[blocks, :, t % block_size, :]", "cache[blocks, :, (t + 1) % block_size, :]", ["test_oracle_cache.py"]),
+    ("merge-unscaled-sum", "attention.py", "np.exp(m - M) * l for", "l for", ["test_oracle_attention.py"]),
+    ("block-count", "blocks.py", "return -(-n_tokens // block_size)", "return n_tokens // block_size + 1", ["test_oracle_blocks.py"]),
+    ("cow-private-block", "alloc.py", "j not in copied and self.refcount[table[j]] > 1:\n                old", "j not in copied and self.refcount[table[j]] >= 1:\n                old", ["test_oracle_alloc.py"]),
+    ("cow-keeps-ref", "alloc.py", "self.refcount[old] -= 1", "pass", ["test_oracle_alloc.py"]),
+    ("fork-drops-partial-block", "alloc.py", "[: blocks_needed(share_tokens, self.block_size)]", "[: share_tokens // self.block_size]", ["test_oracle_alloc.py"]),
+    ("lifo-reuse", "alloc.py", "self.free.append(b)", "self.free.appendleft(b)", ["test_oracle_alloc.py"]),
+    ("v-from-k", "cache.py", "v_cache[blocks, :, rows, :] = np.asarray(v)[keep]", "v_cache[blocks, :, rows, :] = np.asarray(k)[keep]", ["test_oracle_cache.py"]),
+]
+
+
+@pytest.mark.parametrize("mid,fname,old,new,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, mid, fname, old, new, pins):
+    for d in ("oracle", "workloads"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "tests").mkdir()
+    for f in ["conftest.py", "helpers.py"] + pins:
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    target = tmp_path / "oracle" / fname
+    src = target.read_text()
+    assert src.count(old) >= 1, f"mutation site for {mid} not found; update the mutation list"
+    target.write_text(src.replace(old, new))
+    env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
+    res = subprocess.run(
+        [sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+         *[f"tests/{p}" for p in pins]],
+        cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
+    assert res.returncode != 0, f"planted mistake {mid} passed every pin:\n{res.stdout[-2000:]}"
+    assert "failed" in res.stdout or "error" in res.stdout.lower()
