@@ -1,0 +1,259 @@
+/*
+ * libpagedattn — paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; no C++ or framework types cross it.
+ *
+ * Pages whose description of the method these calls follow (cited by title
+ * and section):
+ *   [SLAVA] "Was ändert PagedAttention an der KV-Speicherzuweisung für LLMs?"
+ *           (slavadubrov.com): lead paragraph; section "Ungenutzten Platz in
+ *           Blöcken berechnen"; section "Gemeinsame Nutzung erfordert mehr als
+ *           Speicherzuweisung".
+ *   [AIU]   "PagedAttention et vLLM" (aiunderstanding.org): section "Plongée
+ *           profonde"; "Questions fréquemment posées".
+ *   [ART]   "Внутреннее устройство vLLM: как работает высокопроизводительный
+ *           инференс LLM" (artificials.ru): paragraphs on paged attention,
+ *           chunked prefill and the forward pass.
+ *   [HADA]  "vLLM PagedAttention: eine Revolution für den Durchsatz bei der
+ *           LLM-Inferenz" (de.news.hada.io): bullet "Chunked Prefill".
+ *
+ * Conventions for every call:
+ *   - Every call returns pa_status; no exception or abort crosses the ABI.
+ *     After a non-OK status, pa_last_error() gives a message (per thread).
+ *   - Device calls take device pointers owned by the caller and a HIP stream
+ *     (hipStream_t passed as void*, NULL = the null stream).  They enqueue
+ *     work and return without synchronising (except in check mode, below).
+ *     The library never allocates device memory: split-KV scratch is the
+ *     caller's `workspace`.
+ *   - Host arguments (sizes, descriptors, null pointers, supported shapes)
+ *     are checked before anything is enqueued: PA_ERR_ARG / PA_ERR_UNSUPPORTED.
+ *   - Device-resident metadata (slots, block tables, lengths) is not read by
+ *     the host on the fast path.  Out-of-range block ids and slots are made
+ *     harmless on the device (a slot outside the pool is skipped; a block id
+ *     outside the pool is clamped into it), so a bad table gives wrong values,
+ *     never a fault.  With the environment variable PA_CHECK=1 the host copies
+ *     the metadata back, synchronises the stream and validates every
+ *     precondition first, returning PA_ERR_RANGE on a violation.
+ *   - HIP launch failures return PA_ERR_HIP with the runtime's message.
+ *
+ * Cache layout ([SLAVA] section "Ungenutzten Platz in Blöcken berechnen":
+ * block size and layout are the runtime's choice; [ART] paged-attention
+ * paragraph: blocks of 16 tokens): separate K and V pools, each
+ *     [num_blocks][num_kv_heads][block_size = 16][head_dim]   row-major,
+ * so one (block, KV head) tile of 16 tokens is contiguous.  Slot s of the
+ * pool is row s % 16 of block s / 16.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_ARG = 1,          /* bad host argument (null pointer, size, descriptor) */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not built: dtype / head_dim / group size / block size */
+  PA_ERR_OOM = 3,          /* allocator: not enough free blocks (state unchanged) */
+  PA_ERR_RANGE = 4,        /* check mode: device metadata violates a precondition */
+  PA_ERR_HIP = 5           /* HIP runtime error */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shape of one K (or V) pool.  block_size must be 16 for device calls. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t dtype;           /* pa_dtype: element type of pools, k/v, q and out */
+} pa_cache_desc;
+
+/* Library version string (static storage). */
+const char* pa_version(void);
+
+/* Message for the last non-OK status returned on this thread (static storage). */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device operations                                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * pa_write_kv — store new tokens' keys and values into their cache slots.
+ *
+ * [SLAVA] lead paragraph: a block table maps a request's logical positions to
+ * physical blocks; the per-token slot is that mapping, flattened.  The new
+ * tokens are written before attention reads them.
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim], contiguous, c->dtype
+ *   k_cache,
+ *   v_cache       device pools (layout above), modified in place
+ *   slot_mapping  device int64 [num_tokens]; slot < 0 means "skip this token"
+ *                 (padding); a slot >= num_blocks*16 is also skipped.
+ *                 Precondition: no two tokens name the same slot.
+ *   num_tokens    >= 0 (0 is a no-op)
+ *
+ * A bit copy: the stored bytes equal the input bytes exactly.
+ * Errors: PA_ERR_ARG, PA_ERR_UNSUPPORTED (block_size != 16 or head_dim*elem
+ * not a multiple of 16 bytes), PA_ERR_RANGE (check mode: duplicate or
+ * out-of-pool slot), PA_ERR_HIP.
+ */
+pa_status pa_write_kv(const void* k, const void* v, void* k_cache, void* v_cache,
+                      const int64_t* slot_mapping, int32_t num_tokens,
+                      const pa_cache_desc* c, void* stream);
+
+/*
+ * pa_copy_blocks — whole-block copies for copy-on-write.
+ *
+ * [SLAVA] section "Gemeinsame Nutzung erfordert mehr als Speicherzuweisung"
+ * and [AIU] FAQ (sharing question): a block several requests share is copied
+ * only when one of them diverges, so the shared original stays intact.
+ *
+ *   pairs      device int32 [num_pairs][2] = (src block, dst block); each
+ *              copy moves the block's K and V, all KV heads, all 16 rows.
+ *              Precondition: no dst appears twice or as any pair's src.
+ *              Pairs naming a block outside [0, num_blocks) are skipped.
+ *   num_pairs  >= 0 (0 is a no-op)
+ *
+ * Enqueue it before the pa_write_kv that writes into the copies (same stream).
+ * Errors: PA_ERR_ARG, PA_ERR_RANGE (check mode), PA_ERR_HIP.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
+                         int32_t num_pairs, const pa_cache_desc* c, void* stream);
+
+/*
+ * pa_forward_workspace_size — bytes of device scratch pa_forward needs for the
+ * same host arguments (0 when the call needs none).  Depends only on its
+ * arguments and the PA_SPLIT environment variable (see pa_forward).
+ */
+size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                 int32_t max_seq_len, int32_t max_query_len,
+                                 const pa_cache_desc* c);
+
+/*
+ * pa_forward — attention for a flattened variable-length super-batch.
+ *
+ * [ART] forward-pass paragraph: every sequence of the step sits in one batch
+ * with no padding; masks and exact positions keep each to its own tokens.
+ * [AIU] "Plongée profonde": each query attends to its sequence's whole cached
+ * context, read through the block table from blocks anywhere in memory.
+ * [HADA] "Chunked Prefill" / [ART] chunked-prefill paragraph: a prompt's
+ * prefill may arrive in chunks on top of tokens already cached.
+ *
+ * For sequence i (rows query_start_loc[i] .. query_start_loc[i+1]-1, n_i of
+ * them), query row j (absolute position cached_lens[i] + j) and query head h,
+ * with KV head g = h / (num_q_heads / num_kv_heads):
+ *   visible keys t:  t <= cached_lens[i] + j   if causal, else t < seq_lens[i]
+ *   out = sum_t softmax_t(scale * <q, K_t>) V_t
+ * where K_t / V_t is token t of sequence i, in block block_tables[i][t / 16]
+ * at row t % 16.  Accumulation is fp32; out is rounded once (nearest-even for
+ * bf16).  Sequences with n_i = 1 run the split-KV decode path (partitions of
+ * a few hundred tokens merged by log-sum-exp); sequences with n_i > 1 run
+ * the chunked-prefill path (bf16: matrix cores).
+ *
+ *   out, q           device, [num_tokens][num_q_heads][head_dim], c->dtype
+ *   k_cache, v_cache device pools (read only)
+ *   block_tables     device int32 [num_seqs][block_table_stride]
+ *   seq_lens         device int32 [num_seqs]   L_i: tokens in cache after this step's write
+ *   query_start_loc  device int32 [num_seqs+1] non-decreasing, [0] = 0, [num_seqs] = num_tokens
+ *   cached_lens      device int32 [num_seqs]   c_i; precondition L_i = c_i + n_i
+ *   max_seq_len      host, >= every L_i       (sizes the grid without a device->host sync)
+ *   max_query_len    host, >= every n_i
+ *   scale            softmax scale (typically 1/sqrt(head_dim))
+ *   causal           0 or 1
+ *   workspace        device scratch of >= pa_forward_workspace_size(...) bytes
+ *                    (may be NULL when that size is 0); contents need no init
+ *
+ * Supported: dtype f32 or bf16; head_dim 64 or 128; num_q_heads/num_kv_heads
+ * in {1, 2, 4, 8}; block_size 16.  Environment PA_SPLIT=auto (default) |
+ * off | <tokens> (a multiple of 16, <= 1024) sets the decode partition size.
+ * Errors: PA_ERR_ARG (incl. a workspace smaller than required),
+ * PA_ERR_UNSUPPORTED, PA_ERR_RANGE (check mode), PA_ERR_HIP.
+ */
+pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t block_table_stride,
+                     const int32_t* seq_lens, const int32_t* query_start_loc,
+                     const int32_t* cached_lens, int32_t num_seqs, int32_t num_tokens,
+                     int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                     const pa_cache_desc* c, float scale, int32_t causal,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator (no GPU calls; one thread at a time per allocator)   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [SLAVA] section "Ungenutzten Platz in Blöcken berechnen": blocks are added
+ * as a sequence grows and returned when the request ends; only the last one
+ * is partly filled.  [SLAVA] section "Gemeinsame Nutzung ..." / [AIU] FAQ:
+ * requests may share blocks; a shared block is copied only on divergence.
+ * [ART] paged-attention paragraph: 16-token blocks; exhausting them is the
+ * signal for preemption (here PA_ERR_OOM, with nothing changed).
+ *
+ * Rules (exact; the same op sequence always yields the same tables, slots
+ * and copy pairs):
+ *   - Free blocks are taken from the head of a free list whose initial order
+ *     the caller gives; a block whose refcount falls to 0 joins its tail.
+ *   - Sequence ids are 0, 1, 2, ... in creation order, never reused.
+ *   - fork(parent, k): the child shares the parent's first ceil(k/B) blocks
+ *     (refcount + 1 each) and has length k (k <= parent length).
+ *   - append(seq, n): positions p = len .. len+n-1 in order; at p % B == 0 a
+ *     fresh block is appended; otherwise, the first time the append writes
+ *     into a block with refcount > 1, that block is copied: a fresh block
+ *     replaces it in the table, the pair (old, fresh) is emitted and the old
+ *     refcount drops by one.  slot(p) = table[p / B] * B + p % B.
+ *     All-or-nothing: PA_ERR_OOM (not enough free blocks) and PA_ERR_ARG
+ *     (cow_cap too small) leave every table, refcount and list unchanged.
+ *   - free(seq): refcount - 1 for each of its blocks in table order; blocks
+ *     reaching 0 go to the free-list tail.
+ */
+typedef struct pa_alloc pa_alloc;
+
+typedef struct {
+  int64_t blocks_total;
+  int64_t blocks_free;
+  int64_t blocks_used;     /* refcount > 0 */
+  int64_t blocks_shared;   /* refcount > 1 */
+  int64_t tokens_logical;  /* sum of sequence lengths */
+  int64_t slots_logical;   /* sum over sequences of table length * block_size */
+  int64_t slots_physical;  /* blocks_used * block_size */
+} pa_alloc_stats_t;
+
+/* free_order: host int32 permutation of 0..num_blocks-1, or NULL for 0..num_blocks-1.
+ * *out receives a handle owned by the caller, released with pa_alloc_destroy. */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                          pa_alloc** out);
+void pa_alloc_destroy(pa_alloc* a);
+
+pa_status pa_seq_create(pa_alloc* a, int32_t* seq_id);
+pa_status pa_seq_fork(pa_alloc* a, int32_t parent, int32_t share_tokens, int32_t* child);
+
+/* slots_out: host int64 [n_tokens]; cow_pairs_out: host int32 [2*cow_cap] (src, dst) pairs;
+ * *n_cow receives the number of pairs written.  n_tokens == 0 is a no-op. */
+pa_status pa_seq_append(pa_alloc* a, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                        int32_t* cow_pairs_out, int32_t cow_cap, int32_t* n_cow);
+pa_status pa_seq_free(pa_alloc* a, int32_t seq);
+
+/* Copies up to cap block ids (logical order) into out; *n_blocks and *len
+ * always receive the table length and token count.  out may be NULL to query
+ * the size; a non-NULL out with cap < table length is PA_ERR_ARG. */
+pa_status pa_seq_block_table(const pa_alloc* a, int32_t seq, int32_t* out, int32_t cap,
+                             int32_t* n_blocks, int32_t* len);
+pa_status pa_alloc_stats(const pa_alloc* a, pa_alloc_stats_t* s);
+
+/* Refcount of one block, or -1 for an id outside the pool. */
+int32_t pa_block_refcount(const pa_alloc* a, int32_t block);
+
+/* Free list, head first: copies up to cap ids into out; *n receives its length. */
+pa_status pa_alloc_free_list(const pa_alloc* a, int32_t* out, int32_t cap, int32_t* n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,266 @@
+"""Python binding for libpagedattn (argument marshalling only).
+
+Every computation runs in the HIP library; this module turns torch tensors
+into device pointers and shapes, passes the current HIP stream, and raises on
+a non-OK status.  It never computes attention, slots or block tables itself,
+and there is no fallback: if ``libpagedattn.so`` is missing, importing the
+binding fails.
+
+Functions carry the C names: ``pa_write_kv``, ``pa_copy_blocks``,
+``pa_forward_workspace_size``, ``pa_forward``; ``BlockAllocator`` wraps the
+``pa_alloc_*`` / ``pa_seq_*`` calls.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_RANGE, PA_ERR_HIP = range(6)
+PA_F32, PA_BF16 = 0, 1
+_STATUS = {1: "PA_ERR_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM", 4: "PA_ERR_RANGE", 5: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class OutOfBlocks(PagedAttnError):
+    pass
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class AllocStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("blocks_total", "blocks_free", "blocks_used", "blocks_shared",
+                 "tokens_logical", "slots_logical", "slots_physical")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run paged_kv_cache_forward_amd.build.build()")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+_pdesc = ctypes.POINTER(CacheDesc)
+
+_SIGS = {
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_write_kv": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _pdesc, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _pdesc, _vp]),
+    "pa_forward_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
+    "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                          _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_alloc_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_seq_create": (_i32, [_vp, _pi32]),
+    "pa_seq_fork": (_i32, [_vp, _i32, _i32, _pi32]),
+    "pa_seq_append": (_i32, [_vp, _i32, _i32, _pi64, _pi32, _i32, _pi32]),
+    "pa_seq_free": (_i32, [_vp, _i32]),
+    "pa_seq_block_table": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
+    "pa_alloc_stats": (_i32, [_vp, ctypes.POINTER(AllocStats)]),
+    "pa_block_refcount": (_i32, [_vp, _i32]),
+    "pa_alloc_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def _check(status):
+    if status != PA_OK:
+        msg = lib.pa_last_error().decode()
+        if status == PA_ERR_OOM:
+            raise OutOfBlocks(status, msg)
+        raise PagedAttnError(status, msg)
+
+
+def version():
+    return lib.pa_version().decode()
+
+
+# -- device calls (torch tensors) ---------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def cache_desc(k_cache):
+    """Descriptor of a pool tensor shaped [num_blocks][num_kv_heads][16][head_dim]."""
+    nb, hkv, bs, d = k_cache.shape
+    return CacheDesc(nb, hkv, d, bs, _dtype_code(k_cache))
+
+
+def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype")
+    if v_cache.shape != k_cache.shape or v.shape != k.shape:
+        raise ValueError("K and V shapes differ")
+    T = k.shape[0]
+    if k.dim() != 3 or k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or slot_mapping.shape != (T,):
+        raise ValueError("k/v must be [T][num_kv_heads][head_dim] and slot_mapping [T]")
+    _check(lib.pa_write_kv(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(slot_mapping, "slot_mapping", torch.int64), T, ctypes.byref(desc),
+                           _stream(stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n][2]")
+    _check(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                              _dev(pairs, "pairs", torch.int32), pairs.shape[0], ctypes.byref(desc),
+                              _stream(stream)))
+
+
+def pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):
+    desc = cache_desc(k_cache)
+    return int(lib.pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len,
+                                             max_query_len, ctypes.byref(desc)))
+
+
+def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
+               max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+    """Attention for the super-batch; ``out`` is written in place.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``pa_forward_workspace_size(...)`` bytes; when omitted, one is allocated
+    here from torch's caching allocator.
+    """
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    T, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
+        raise ValueError("out must match q, and q the cache dtype")
+    S = seq_lens.shape[0]
+    if query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes do not match num_seqs")
+    need = pa_forward_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_forward(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                          _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+                          _dev(seq_lens, "seq_lens", torch.int32),
+                          _dev(query_start_loc, "query_start_loc", torch.int32),
+                          _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
+                          int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
+                          ws_ptr, ws_bytes, _stream(stream)))
+
+
+# -- host allocator -------------------------------------------------------------
+
+class BlockAllocator:
+    """The library's host block allocator (refcounts, sharing, copy-on-write)."""
+
+    def __init__(self, num_blocks, block_size=16, free_order=None):
+        self._h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            self._order = np.ascontiguousarray(free_order, dtype=np.int32)
+            order = self._order.ctypes.data_as(_pi32)
+        _check(lib.pa_alloc_create(num_blocks, block_size, order, ctypes.byref(self._h)))
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and h.value:
+            lib.pa_alloc_destroy(h)
+            self._h = ctypes.c_void_p()
+
+    def create(self):
+        sid = ctypes.c_int32()
+        _check(lib.pa_seq_create(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def fork(self, parent, share_tokens):
+        sid = ctypes.c_int32()
+        _check(lib.pa_seq_fork(self._h, parent, share_tokens, ctypes.byref(sid)))
+        return sid.value
+
+    def append(self, seq, n_tokens, cow_cap=4):
+        """Returns (slots int64 array, list of (src, dst) copy-on-write pairs)."""
+        slots = np.empty(max(n_tokens, 1), dtype=np.int64)
+        pairs = np.empty(2 * cow_cap, dtype=np.int32)
+        n_cow = ctypes.c_int32()
+        _check(lib.pa_seq_append(self._h, seq, n_tokens, slots.ctypes.data_as(_pi64),
+                                 pairs.ctypes.data_as(_pi32), cow_cap, ctypes.byref(n_cow)))
+        return slots[:n_tokens], [(int(pairs[2 * k]), int(pairs[2 * k + 1])) for k in range(n_cow.value)]
+
+    def free_seq(self, seq):
+        _check(lib.pa_seq_free(self._h, seq))
+
+    def block_table(self, seq):
+        nb, ln = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
+        out = np.empty(max(nb.value, 1), dtype=np.int32)
+        _check(lib.pa_seq_block_table(self._h, seq, out.ctypes.data_as(_pi32), nb.value,
+                                      ctypes.byref(nb), ctypes.byref(ln)))
+        return out[:nb.value].tolist()
+
+    def length(self, seq):
+        nb, ln = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
+        return ln.value
+
+    def stats(self):
+        st = AllocStats()
+        _check(lib.pa_alloc_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in AllocStats._fields_}
+
+    def refcount(self, block):
+        return int(lib.pa_block_refcount(self._h, block))
+
+    def free_list(self):
+        n = ctypes.c_int32()
+        _check(lib.pa_alloc_free_list(self._h, None, 0, ctypes.byref(n)))
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(lib.pa_alloc_free_list(self._h, out.ctypes.data_as(_pi32), n.value, ctypes.byref(n)))
+        return out[:n.value].tolist()

@@ -1,0 +1,464 @@
+// Decode attention over paged K/V (one query token per sequence), split-KV.
+//
+// What is computed: "PagedAttention et vLLM" (aiunderstanding.org), section
+// "Plongée profonde": the new token attends to every cached key/value of its
+// sequence, and those live in fixed-size blocks anywhere in memory, found
+// through a table from logical positions to physical blocks.  "Внутреннее
+// устройство vLLM" (artificials.ru), forward-pass paragraph: each sequence of
+// the super-batch sees only its own tokens.  "vLLM PagedAttention: eine
+// Revolution ..." (de.news.hada.io), bullet on disaggregation: decode is bound
+// by memory bandwidth, so this kernel is built around the K/V stream.
+//
+// Work item = one wavefront for (partition p of sequence i, KV head g), serving
+// all G query heads of that KV head, so each K/V byte is read once per KV head.
+// A partition is `part_tokens` consecutive logical tokens (a multiple of 16).
+//
+// Lane layout for one 16-token block tile of one KV head (16 rows x D elems,
+// contiguous): the tile is CPL consecutive 1 KiB (for bf16 D128) runs; run u
+// is loaded by all 64 lanes with one 16-byte load each (fully coalesced).  Lane
+// l holds chunk `col = l % CPR` (E elements of the head dim) of token row
+// `u * R + rg`, rg = l / CPR.  So the R lane groups ("row groups") each own a
+// fixed subset of every block's tokens.
+//
+// Scores: per-lane partial dot products (bf16 pairs through v_dot2_f32_bf16, or
+// fp32 FMAs) summed across the CPR lanes of a row group with DPP row ops.
+// Each row group keeps its own online-softmax state (running max m, sum l,
+// fp32 accumulator for its E output columns per query head); the R states are
+// combined once at the end of the item with the log-sum-exp rule, so no
+// cross-row-group traffic happens per block.  Scores are in base-2 units
+// (scale * log2 e folded in) so the exponentials are single v_exp_f32.
+//
+// Masking selects (never multiplies): keys past the partition end get score
+// -inf and their V chunks are zeroed, so stale or NaN slots in a sequence's
+// last block never reach an accumulator.
+//
+// Output: a sequence with one partition writes its normalised result directly;
+// otherwise each partition writes (m, l, acc) to the workspace and the merge
+// kernel below combines them in ascending partition order.
+#include <cstdlib>
+#include <cstring>
+
+#include "device.h"
+#include "ops.h"
+#include "status.h"
+
+namespace pa {
+
+constexpr int kMaxParts = 4096;   // merge keeps one weight per partition in LDS
+
+struct DecodeKernelArgs {
+  AttnArgs a;
+  int32_t part_tokens;
+  int32_t max_parts;
+  float* p_acc;   // [num_seqs][Hq][max_parts][D]
+  float* p_ml;    // [num_seqs][Hq][max_parts][2]  (m in base-2 units, l)
+  int32_t rows_mode;
+};
+
+template <typename T, int D>
+struct Tile {
+  static constexpr int E = Elem<T>::per16;   // elements per 16-byte chunk
+  static constexpr int CPR = D / E;          // chunks per token row
+  static constexpr int R = 64 / CPR;         // row groups
+  static constexpr int CPL = kBlock / R;     // chunks each lane loads per block tile
+  static constexpr int ROW_BYTES = D * Elem<T>::bytes;
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "head_dim / dtype combination");
+};
+
+// Widen one 16-byte chunk to E floats.
+template <typename T>
+__device__ __forceinline__ void widen(uint4 w, float* f);
+template <>
+__device__ __forceinline__ void widen<float>(uint4 w, float* f) {
+  f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y);
+  f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+template <>
+__device__ __forceinline__ void widen<uint16_t>(uint4 w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+
+// Partial dot product of one query chunk with one key chunk.
+template <typename T>
+__device__ __forceinline__ float chunk_dot(uint4 q, uint4 k);
+template <>
+__device__ __forceinline__ float chunk_dot<uint16_t>(uint4 q, uint4 k) {
+  float d = dot2_bf16(q.x, k.x, 0.0f);
+  d = dot2_bf16(q.y, k.y, d);
+  d = dot2_bf16(q.z, k.z, d);
+  return dot2_bf16(q.w, k.w, d);
+}
+template <>
+__device__ __forceinline__ float chunk_dot<float>(uint4 q, uint4 k) {
+  float d = __uint_as_float(q.x) * __uint_as_float(k.x);
+  d = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), d);
+  d = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), d);
+  return fmaf(__uint_as_float(q.w), __uint_as_float(k.w), d);
+}
+
+// Store E floats as one 16-byte chunk of T.
+template <typename T>
+__device__ __forceinline__ void store_chunk(void* p, const float* f);
+template <>
+__device__ __forceinline__ void store_chunk<float>(void* p, const float* f) {
+  st16(p, make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                     __float_as_uint(f[3])));
+}
+template <>
+__device__ __forceinline__ void store_chunk<uint16_t>(void* p, const float* f) {
+  st16(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                     pack_bf16x2(f[6], f[7])));
+}
+
+// Online-softmax state of one row group for the G query heads.
+template <int G, int E>
+struct RowState {
+  float m[G];
+  float l[G];
+  float acc[G][E];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = kNegBig;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[h][e] = 0.0f;
+    }
+  }
+};
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void load_tile(const uint8_t* kbase, const uint8_t* vbase, int lane_off,
+                                          uint4 (&kq)[Tile<T, D>::CPL], uint4 (&vq)[Tile<T, D>::CPL]) {
+  using TL = Tile<T, D>;
+#pragma unroll
+  for (int u = 0; u < TL::CPL; ++u) {
+    kq[u] = ld16(kbase + lane_off + u * TL::R * TL::ROW_BYTES);
+    vq[u] = ld16(vbase + lane_off + u * TL::R * TL::ROW_BYTES);
+  }
+}
+
+// Fold one block tile (tokens tok0 .. tok0+15) into the row group's state.
+template <typename T, int D, int G>
+__device__ __forceinline__ void fold_tile(const uint4 (&kq)[Tile<T, D>::CPL], uint4 (&vq)[Tile<T, D>::CPL],
+                                          const uint4 (&qv)[G], int tok0, int t_end, int rg,
+                                          float scale_log2, RowState<G, Tile<T, D>::E>& st) {
+  using TL = Tile<T, D>;
+  constexpr int CPL = TL::CPL, E = TL::E;
+  float s[CPL][G];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[u][h] = group_sum<TL::CPR>(chunk_dot<T>(qv[h], kq[u]));
+
+  const bool tail = tok0 + kBlock > t_end;  // wave-uniform
+  float vf[CPL][E];
+#pragma unroll
+  for (int u = 0; u < CPL; ++u) {
+    const bool valid = tok0 + u * TL::R + rg < t_end;
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[u][h] = valid ? s[u][h] * scale_log2 : -INFINITY;
+    uint4 w = vq[u];
+    if (tail && !valid) w = make_uint4(0u, 0u, 0u, 0u);
+    widen<T>(w, vf[u]);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float bm = s[0][h];
+#pragma unroll
+    for (int u = 1; u < CPL; ++u) bm = fmaxf(bm, s[u][h]);
+    const float mn = fmaxf(st.m[h], bm);
+    const float alpha = fast_exp2(st.m[h] - mn);
+    st.m[h] = mn;
+    float p[CPL];
+    float ps = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      p[u] = fast_exp2(s[u][h] - mn);
+      ps += p[u];
+    }
+    st.l[h] = fmaf(st.l[h], alpha, ps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float a = st.acc[h][e] * alpha;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) a = fmaf(p[u], vf[u][e], a);
+      st.acc[h][e] = a;
+    }
+  }
+}
+
+// Attend query row `row` of sequence i (KV head g) over logical tokens [t0, t1);
+// t0 is a multiple of 16 and t1 > t0.
+template <typename T, int D, int G>
+__device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, int row, int t0, int t1,
+                                             RowState<G, Tile<T, D>::E>& st) {
+  using TL = Tile<T, D>;
+  const int lane = threadIdx.x;
+  const int col = lane % TL::CPR;
+  const int rg = lane / TL::CPR;
+  const int lane_off = rg * TL::ROW_BYTES + col * 16;
+
+  uint4 qv[G];
+  const uint8_t* qrow = (const uint8_t*)a.q + ((size_t)row * a.num_q_heads + (size_t)g * G) * TL::ROW_BYTES;
+#pragma unroll
+  for (int h = 0; h < G; ++h) qv[h] = ld16(qrow + h * TL::ROW_BYTES + col * 16);
+
+  const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
+  const size_t tile_bytes = (size_t)kBlock * TL::ROW_BYTES;
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * tile_bytes;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * tile_bytes;
+  const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
+
+  const int b_first = t0 / kBlock;
+  const int b_last = (t1 - 1) / kBlock;
+  for (int bb = b_first; bb <= b_last; bb += 64) {
+    const int nb = min(64, b_last - bb + 1);
+    const int my_bid = lane < nb ? clamp_block(bt_row[bb + lane], a.num_blocks) : 0;
+    uint4 kq[TL::CPL], vq[TL::CPL];
+    {
+      const int bid = __builtin_amdgcn_readfirstlane(my_bid);
+      load_tile<T, D, G>(kc + bid * block_stride, vc + bid * block_stride, lane_off, kq, vq);
+    }
+    for (int j = 0; j < nb; ++j) {
+      uint4 kn[TL::CPL], vn[TL::CPL];
+      const bool more = j + 1 < nb;
+      if (more) {
+        const int bid = __builtin_amdgcn_readlane(my_bid, j + 1);
+        load_tile<T, D, G>(kc + bid * block_stride, vc + bid * block_stride, lane_off, kn, vn);
+      }
+      fold_tile<T, D, G>(kq, vq, qv, (bb + j) * kBlock, t1, rg, a.scale_log2, st);
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < TL::CPL; ++u) {
+          kq[u] = kn[u];
+          vq[u] = vn[u];
+        }
+      }
+    }
+  }
+}
+
+// Combine the R row-group states; lanes of row group 0 end up with the totals
+// for their columns.  Returns per head: M (base-2 max), Lsum, and acc in `out`.
+template <typename T, int D, int G>
+__device__ __forceinline__ void combine_row_groups(RowState<G, Tile<T, D>::E>& st) {
+  using TL = Tile<T, D>;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = cross_group_max<TL::CPR>(st.m[h]);
+    const float f = fast_exp2(st.m[h] - M);
+    st.l[h] = cross_group_sum<TL::CPR>(st.l[h] * f);
+#pragma unroll
+    for (int e = 0; e < TL::E; ++e) st.acc[h][e] = cross_group_sum<TL::CPR>(st.acc[h][e] * f);
+    st.m[h] = M;
+  }
+}
+
+template <typename T, int D, int G>
+__device__ __forceinline__ void write_final(const AttnArgs& a, int row, int g, const RowState<G, Tile<T, D>::E>& st) {
+  using TL = Tile<T, D>;
+  const int lane = threadIdx.x;
+  if (lane >= TL::CPR) return;
+  uint8_t* orow = (uint8_t*)a.out + ((size_t)row * a.num_q_heads + (size_t)g * G) * TL::ROW_BYTES;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float inv = 1.0f / st.l[h];
+    float f[TL::E];
+#pragma unroll
+    for (int e = 0; e < TL::E; ++e) f[e] = st.acc[h][e] * inv;
+    store_chunk<T>(orow + h * TL::ROW_BYTES + lane * 16, f);
+  }
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64) void decode_kernel(DecodeKernelArgs k) {
+  using TL = Tile<T, D>;
+  const AttnArgs& a = k.a;
+  const int p = blockIdx.x, g = blockIdx.y, i = blockIdx.z;
+  const int q0 = a.qsl[i];
+  const int n = a.qsl[i + 1] - q0;
+  if (n <= 0 || q0 < 0 || q0 + n > a.num_tokens) return;  // rows outside q/out: nothing to do
+  const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
+  RowState<G, TL::E> st;
+
+  if (n == 1) {
+    const int t0 = p * k.part_tokens;
+    if (t0 >= L) return;
+    const int t1 = min(t0 + k.part_tokens, L);
+    st.init();
+    attend_range<T, D, G>(a, i, g, q0, t0, t1, st);
+    combine_row_groups<T, D, G>(st);
+    if (k.max_parts == 1 || L <= k.part_tokens) {
+      write_final<T, D, G>(a, q0, g, st);
+      return;
+    }
+    const int lane = threadIdx.x;
+    if (lane >= TL::CPR) return;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const size_t item = ((size_t)i * a.num_q_heads + (size_t)g * G + h) * k.max_parts + p;
+      float* dst = k.p_acc + item * D + lane * TL::E;
+#pragma unroll
+      for (int e = 0; e < TL::E; e += 4)
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
+      if (lane == 0) *reinterpret_cast<float2*>(k.p_ml + item * 2) = make_float2(st.m[h], st.l[h]);
+    }
+    return;
+  }
+
+  // Multi-token sequence on the vector path: one query row at a time, unsplit.
+  if (!k.rows_mode || p != 0) return;
+  const int c = a.cached_lens[i];
+  for (int j = 0; j < n; ++j) {
+    const int t1 = a.causal ? min(c + j + 1, L) : L;
+    if (t1 <= 0) continue;
+    st.init();
+    attend_range<T, D, G>(a, i, g, q0 + j, 0, t1, st);
+    combine_row_groups<T, D, G>(st);
+    write_final<T, D, G>(a, q0 + j, g, st);
+  }
+}
+
+// One block of 256 threads per (sequence, query head): weights exp2(m_p - M)
+// for every partition, then the weighted sum of the partial accumulators in
+// ascending partition order within each thread's share, reduced in LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int32_t part_tokens, int32_t max_parts,
+                                                    const float* __restrict__ p_acc,
+                                                    const float* __restrict__ p_ml) {
+  constexpr int TPP = D / 4;          // threads per partition row (4 floats each)
+  constexpr int NG = 256 / TPP;       // partition groups
+  __shared__ float w_s[kMaxParts];
+  __shared__ float red[NG][D];
+  __shared__ float wred[4];
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int q0 = a.qsl[i];
+  if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
+  const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
+  // The decode kernel wrote at most max_parts partitions (grid width).
+  const int P = min((L + part_tokens - 1) / part_tokens, max_parts);
+  if (P <= 1) return;
+  const size_t item0 = ((size_t)i * a.num_q_heads + h) * max_parts;
+  const float* ml = p_ml + item0 * 2;
+  const float* acc = p_acc + item0 * D;
+
+  float M = -INFINITY;
+  for (int p = tid; p < P; p += 256) M = fmaxf(M, ml[2 * p]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) wred[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+  __syncthreads();
+
+  float den = 0.0f;
+  for (int p = tid; p < P; p += 256) {
+    const float w = fast_exp2(ml[2 * p] - M);
+    w_s[p] = w;
+    den = fmaf(w, ml[2 * p + 1], den);
+  }
+  den = wave_sum(den);
+  if ((tid & 63) == 0) wred[tid >> 6] = den;
+  __syncthreads();
+  den = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+
+  const int d4 = tid % TPP, pg = tid / TPP;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = pg; p < P; p += NG) {
+    const float w = w_s[p];
+    const float4 v = *reinterpret_cast<const float4*>(acc + (size_t)p * D + d4 * 4);
+    s.x = fmaf(w, v.x, s.x); s.y = fmaf(w, v.y, s.y); s.z = fmaf(w, v.z, s.z); s.w = fmaf(w, v.w, s.w);
+  }
+  *reinterpret_cast<float4*>(&red[pg][d4 * 4]) = s;
+  __syncthreads();
+  if (tid < D) {
+    float t = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) t += red[q][tid];
+    red[0][tid] = t / den;
+  }
+  __syncthreads();
+  constexpr int E = Elem<T>::per16;
+  if (tid < D / E) {
+    uint8_t* orow = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + h) * D * Elem<T>::bytes;
+    store_chunk<T>(orow + tid * 16, &red[0][tid * E]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+
+DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seq_len) {
+  DecodePlan pl{};
+  const int32_t whole = max_seq_len > 0 ? ((max_seq_len + kBlock - 1) / kBlock) * kBlock : kBlock;
+  int32_t part = whole;
+  const char* env = std::getenv("PA_SPLIT");
+  if (env != nullptr && std::strcmp(env, "off") == 0) {
+    part = whole;
+  } else if (env != nullptr && std::strcmp(env, "auto") != 0 && env[0] != '\0') {
+    part = std::atoi(env);
+    if (part < kBlock || part % kBlock != 0 || part > 1024) part = 512;
+  } else {
+    // Enough independent (sequence, KV head, partition) waves to keep every
+    // SIMD streaming: split anything longer than 256 tokens.
+    if (max_seq_len > 256) {
+      const int64_t items = (int64_t)num_seqs * num_kv_heads;
+      part = items * ((max_seq_len + 255) / 256) <= 16384 ? 256 : 512;
+    }
+  }
+  while ((whole + part - 1) / part > kMaxParts) part *= 2;
+  pl.part_tokens = part;
+  pl.max_parts = (whole + part - 1) / part;
+  pl.partial_bytes = pl.max_parts > 1
+                         ? (size_t)num_seqs * num_q_heads * pl.max_parts * (head_dim + 2) * sizeof(float)
+                         : 0;
+  return pl;
+}
+
+template <typename T, int D>
+static pa_status launch_decode_d(const DecodeKernelArgs& k, int G, dim3 grid, hipStream_t s) {
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_kernel<T, D, 1>), grid, dim3(64), 0, s, k); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<T, D, 2>), grid, dim3(64), 0, s, k); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<T, D, 4>), grid, dim3(64), 0, s, k); break;
+    case 8: hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(64), 0, s, k); break;
+    default: return fail(PA_ERR_UNSUPPORTED, "pa_forward: query heads per KV head %d", G);
+  }
+  return launch_status("pa_forward (decode)");
+}
+
+pa_status launch_decode(const AttnArgs& a, int32_t dtype, const DecodePlan& plan, float* partial_acc,
+                        float* partial_ml, bool rows_mode, hipStream_t s) {
+  DecodeKernelArgs k{a, plan.part_tokens, plan.max_parts, partial_acc, partial_ml, rows_mode ? 1 : 0};
+  const int G = a.num_q_heads / a.num_kv_heads;
+  dim3 grid(plan.max_parts, a.num_kv_heads, a.num_seqs);
+  if (dtype == PA_BF16 && a.head_dim == 128) return launch_decode_d<uint16_t, 128>(k, G, grid, s);
+  if (dtype == PA_BF16 && a.head_dim == 64) return launch_decode_d<uint16_t, 64>(k, G, grid, s);
+  if (dtype == PA_F32 && a.head_dim == 128) return launch_decode_d<float, 128>(k, G, grid, s);
+  if (dtype == PA_F32 && a.head_dim == 64) return launch_decode_d<float, 64>(k, G, grid, s);
+  return fail(PA_ERR_UNSUPPORTED, "pa_forward: head_dim %d", a.head_dim);
+}
+
+pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
+                       const float* partial_acc, const float* partial_ml, hipStream_t s) {
+  dim3 grid(a.num_seqs, a.num_q_heads);
+  if (dtype == PA_BF16 && a.head_dim == 128)
+    hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a, plan.part_tokens,
+                       plan.max_parts, partial_acc, partial_ml);
+  else if (dtype == PA_BF16 && a.head_dim == 64)
+    hipLaunchKernelGGL((merge_kernel<uint16_t, 64>), grid, dim3(256), 0, s, a, plan.part_tokens,
+                       plan.max_parts, partial_acc, partial_ml);
+  else if (dtype == PA_F32 && a.head_dim == 128)
+    hipLaunchKernelGGL((merge_kernel<float, 128>), grid, dim3(256), 0, s, a, plan.part_tokens,
+                       plan.max_parts, partial_acc, partial_ml);
+  else if (dtype == PA_F32 && a.head_dim == 64)
+    hipLaunchKernelGGL((merge_kernel<float, 64>), grid, dim3(256), 0, s, a, plan.part_tokens,
+                       plan.max_parts, partial_acc, partial_ml);
+  else
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: head_dim %d", a.head_dim);
+  return launch_status("pa_forward (merge)");
+}
+
+}  // namespace pa

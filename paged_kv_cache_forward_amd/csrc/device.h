@@ -1,0 +1,97 @@
+// Device helpers for the gfx950 kernels of libpagedattn.
+//
+// CDNA4 facts relied on: 64-lane wavefronts; DPP row operations act inside
+// 16-lane rows; v_dot2_f32_bf16 multiplies two bf16 pairs and accumulates in
+// fp32; v_exp_f32 computes 2^x.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 16;          // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f; // running-max start: finite, so 2^(m_old - m_new) never sees inf - inf
+
+// bf16 <-> fp32.  Stored bf16 is the upper half of the fp32 bit pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane permutations inside 16-lane rows (all source lanes are in range).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xb1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4e;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+// Sum over aligned groups of W consecutive lanes; every lane of a group gets the total.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(W == 8 || W == 16 || W == 32 || W == 64, "group width");
+  x += dpp<kQuadXor1>(x);
+  x += dpp<kQuadXor2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  if constexpr (W >= 16) x += dpp<kRowMirror>(x);
+  if constexpr (W >= 32) x += __shfl_xor(x, 16);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Max / sum across lanes that differ only in bits >= log2(STRIDE) (i.e. across
+// groups of STRIDE lanes); every lane gets the result.
+template <int STRIDE>
+__device__ __forceinline__ float cross_group_max(float x) {
+#pragma unroll
+  for (int off = STRIDE; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float cross_group_sum(float x) {
+#pragma unroll
+  for (int off = STRIDE; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) { return cross_group_max<1>(x); }
+__device__ __forceinline__ float wave_sum(float x) { return cross_group_sum<1>(x); }
+
+// 16-byte global load / store.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Element-type traits: bytes per element and elements per 16-byte chunk.
+template <typename T> struct Elem;
+template <> struct Elem<float> { static constexpr int bytes = 4; static constexpr int per16 = 4; };
+template <> struct Elem<uint16_t> { static constexpr int bytes = 2; static constexpr int per16 = 8; };
+
+__device__ __forceinline__ int clamp_block(int b, int num_blocks) {
+  return (unsigned)b < (unsigned)num_blocks ? b : num_blocks - 1;
+}
+
+}  // namespace pa

@@ -1,0 +1,150 @@
+// pa_forward: the super-batch dispatcher.
+//
+// "Внутреннее устройство vLLM" (artificials.ru), forward-pass and engine
+// paragraphs: one step carries decode rows and prefill chunks together in a
+// single unpadded batch, each row restricted to its own sequence.  Rows of
+// sequences with one query token go to the split-KV decode kernel (plus the
+// log-sum-exp merge when a sequence spans several partitions); sequences with
+// more query tokens go to the chunked-prefill kernel.  Grids are sized from the
+// host scalars max_seq_len / max_query_len, so nothing waits on the device.
+#include <cmath>
+#include <vector>
+
+#include "device.h"
+#include "ops.h"
+#include "status.h"
+
+namespace pa {
+
+struct ForwardShape {
+  int32_t group;
+  DecodePlan plan;
+  bool use_mfma_prefill;
+  bool any_prefill;
+};
+
+static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                          int32_t max_query_len, const pa_cache_desc* c, const char* who, ForwardShape* fs) {
+  pa_status st = check_desc(c, who);
+  if (st != PA_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_seq_len < 0 || max_query_len < 0)
+    return fail(PA_ERR_ARG, "%s: negative size (seqs %d, tokens %d, max_seq_len %d, max_query_len %d)", who,
+                num_seqs, num_tokens, max_seq_len, max_query_len);
+  if (num_q_heads <= 0 || num_q_heads % c->num_kv_heads != 0)
+    return fail(PA_ERR_ARG, "%s: num_q_heads %d is not a positive multiple of num_kv_heads %d", who,
+                num_q_heads, c->num_kv_heads);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (built for 64 and 128)", who, c->head_dim);
+  fs->group = num_q_heads / c->num_kv_heads;
+  if (fs->group != 1 && fs->group != 2 && fs->group != 4 && fs->group != 8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (built for 1, 2, 4, 8)", who, fs->group);
+  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, max_seq_len);
+  fs->any_prefill = max_query_len > 1;
+  fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
+  return PA_OK;
+}
+
+// Check mode: copy the device metadata back and validate every precondition.
+static pa_status validate_metadata(const int32_t* block_tables, int32_t stride, const int32_t* seq_lens,
+                                   const int32_t* qsl, const int32_t* cached_lens, int32_t num_seqs,
+                                   int32_t num_tokens, int32_t max_seq_len, int32_t max_query_len,
+                                   int32_t num_blocks, hipStream_t s) {
+  std::vector<int32_t> L(num_seqs), C(num_seqs), Q(num_seqs + 1), BT((size_t)num_seqs * stride);
+  bool ok = hipMemcpyAsync(L.data(), seq_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(C.data(), cached_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(Q.data(), qsl, sizeof(int32_t) * (num_seqs + 1), hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(BT.data(), block_tables, sizeof(int32_t) * BT.size(), hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) return fail(PA_ERR_HIP, "pa_forward: check-mode copy failed");
+  if (Q[0] != 0 || Q[num_seqs] != num_tokens)
+    return fail(PA_ERR_RANGE, "pa_forward: query_start_loc[0]=%d, [num_seqs]=%d, num_tokens=%d", Q[0], Q[num_seqs],
+                num_tokens);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int32_t n = Q[i + 1] - Q[i];
+    if (n < 0) return fail(PA_ERR_RANGE, "pa_forward: query_start_loc decreases at %d", i);
+    if (n > max_query_len) return fail(PA_ERR_RANGE, "pa_forward: sequence %d has %d query tokens > max_query_len %d", i, n, max_query_len);
+    if (L[i] != C[i] + n) return fail(PA_ERR_RANGE, "pa_forward: sequence %d: seq_len %d != cached %d + new %d", i, L[i], C[i], n);
+    if (C[i] < 0) return fail(PA_ERR_RANGE, "pa_forward: sequence %d: cached_len %d < 0", i, C[i]);
+    if (L[i] > max_seq_len) return fail(PA_ERR_RANGE, "pa_forward: sequence %d: seq_len %d > max_seq_len %d", i, L[i], max_seq_len);
+    const int64_t nb = ((int64_t)L[i] + kBlock - 1) / kBlock;
+    if (nb > stride) return fail(PA_ERR_RANGE, "pa_forward: sequence %d needs %lld blocks > table stride %d", i, (long long)nb, stride);
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t b = BT[(size_t)i * stride + j];
+      if (b < 0 || b >= num_blocks) return fail(PA_ERR_RANGE, "pa_forward: sequence %d block %lld = %d outside the pool", i, (long long)j, b);
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                            int32_t max_seq_len, int32_t max_query_len, const pa_cache_desc* c) {
+  ForwardShape fs;
+  if (shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_workspace_size",
+               &fs) != PA_OK)
+    return 0;
+  return fs.plan.partial_bytes;
+}
+
+extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, const int32_t* cached_lens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  ForwardShape fs;
+  pa_status st = shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward", &fs);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !cached_lens)
+    return fail(PA_ERR_ARG, "pa_forward: NULL device pointer");
+  if (block_table_stride <= 0) return fail(PA_ERR_ARG, "pa_forward: block_table_stride %d", block_table_stride);
+  if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "pa_forward: scale is not finite");
+  if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "pa_forward: causal must be 0 or 1");
+  if (fs.plan.partial_bytes > 0 && (workspace == nullptr || workspace_bytes < fs.plan.partial_bytes))
+    return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", fs.plan.partial_bytes,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (check_mode()) {
+    st = validate_metadata(block_tables, block_table_stride, seq_lens, query_start_loc, cached_lens, num_seqs,
+                           num_tokens, max_seq_len, max_query_len, c->num_blocks, s);
+    if (st != PA_OK) return st;
+  }
+
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.bt_stride = block_table_stride;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.cached_lens = cached_lens;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.head_dim = c->head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal;
+
+  float* p_acc = nullptr;
+  float* p_ml = nullptr;
+  if (fs.plan.partial_bytes > 0) {
+    p_acc = (float*)workspace;
+    p_ml = p_acc + (size_t)num_seqs * num_q_heads * fs.plan.max_parts * c->head_dim;
+  }
+  if (fs.use_mfma_prefill) {
+    st = launch_prefill(a, max_query_len, s);
+    if (st != PA_OK) return st;
+  }
+  st = launch_decode(a, c->dtype, fs.plan, p_acc, p_ml, fs.any_prefill && !fs.use_mfma_prefill, s);
+  if (st != PA_OK) return st;
+  if (fs.plan.max_parts > 1) st = launch_merge(a, c->dtype, fs.plan, p_acc, p_ml, s);
+  return st;
+}

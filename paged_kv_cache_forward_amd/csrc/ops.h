@@ -1,0 +1,59 @@
+// Internal interface between the C-ABI entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+inline int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+
+pa_status check_desc(const pa_cache_desc* c, const char* who);
+pa_status launch_status(const char* who);
+
+// Arguments shared by the attention kernels (device pointers, host scalars).
+struct AttnArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t bt_stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;          // query_start_loc
+  const int32_t* cached_lens;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t head_dim;
+  float scale_log2;            // softmax scale * log2(e): scores are kept in base-2 units
+  int32_t causal;
+};
+
+// Split-KV plan for the decode path.
+struct DecodePlan {
+  int32_t part_tokens;   // tokens per partition (multiple of 16)
+  int32_t max_parts;     // partitions of the longest sequence; 1 = no split
+  size_t partial_bytes;  // workspace bytes for (m, l, acc) partials
+};
+
+DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t max_seq_len);
+
+// Decode (VALU) kernel: sequences with one query token; with `rows_mode` it
+// also handles multi-token sequences one query row at a time (no split).
+pa_status launch_decode(const AttnArgs& a, int32_t dtype, const DecodePlan& plan, float* partial_acc,
+                        float* partial_ml, bool rows_mode, hipStream_t s);
+pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
+                       const float* partial_acc, const float* partial_ml, hipStream_t s);
+
+// Chunked-prefill (MFMA) kernel for bf16 sequences with more than one query token.
+bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
+pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, hipStream_t s);
+
+}  // namespace pa

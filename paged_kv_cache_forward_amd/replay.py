@@ -1,0 +1,134 @@
+"""Run one engine step of a workload through the library on a GPU.
+
+Replays the workload's allocator trace on the library's host allocator, puts
+the pools, queries and metadata in device memory (torch tensors), stores the
+cached tokens with ``pa_write_kv``, and then performs the step itself:
+``pa_copy_blocks`` for copy-on-write pairs, ``pa_write_kv`` for the step's
+new tokens, ``pa_forward`` for attention.  Every step of the path runs in the
+HIP library; this module only marshals.
+"""
+
+import numpy as np
+
+import paged_kv_cache_forward_amd as pa
+
+BF16_NAN_BITS = 0x7FC0
+
+
+def _drive(wl, alloc):
+    """Replay wl.trace on ``alloc``: ids per handle, slots of cached and new rows, step copy pairs."""
+    ids = {}
+    ctx_slots = np.full(len(wl.ctx_k), -1, dtype=np.int64)
+    new_slots = np.full(len(wl.k_new), -1, dtype=np.int64)
+    cow = []
+    for op in wl.trace:
+        if op[0] == "create":
+            ids[op[1]] = alloc.create()
+        elif op[0] == "fork":
+            ids[op[1]] = alloc.fork(ids[op[2]], op[3])
+        else:
+            _, s, n, row0 = op
+            slots, pairs = alloc.append(ids[s], n)
+            if op[0] == "append_ctx":
+                if pairs:
+                    raise RuntimeError("cached-token append produced copy-on-write pairs")
+                ctx_slots[row0:row0 + n] = slots
+            else:
+                new_slots[row0:row0 + n] = slots
+                cow.extend(pairs)
+    return ids, ctx_slots, new_slots, cow
+
+
+class DeviceRun:
+    def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None):
+        import torch
+        self.torch = torch
+        self.wl = wl
+        self.dev = torch.device(device)
+        self.tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        order = wl.free_order if free_order is None else free_order
+        self.alloc = pa.BlockAllocator(wl.num_blocks, wl.block_size, order)
+        self.ids, self.ctx_slots, self.new_slots, self.cow = _drive(wl, self.alloc)
+
+        shape = (wl.pool_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        self.k_cache = self._pool(shape, fill)
+        self.v_cache = self._pool(shape, fill)
+        self.q = self.upload(wl.q)
+        self.k_new = self.upload(wl.k_new)
+        self.v_new = self.upload(wl.v_new)
+        self.new_slots_d = torch.from_numpy(self.new_slots).to(self.dev)
+        pairs = np.asarray(self.cow, dtype=np.int32).reshape(-1, 2)
+        self.pairs_d = torch.from_numpy(pairs).to(self.dev)
+
+        tables = [self.alloc.block_table(self.ids[h]) for h in wl.batch]
+        width = max([len(t) for t in tables] + [1]) if table_stride is None else table_stride
+        bt = np.full((len(tables), width), wl.guard_block, dtype=np.int32)
+        for i, t in enumerate(tables):
+            bt[i, :len(t)] = t
+        self.tables = tables
+        self.block_tables = torch.from_numpy(bt).to(self.dev)
+        self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(self.dev)
+        self.cached_lens = torch.from_numpy(wl.cached_lens.astype(np.int32)).to(self.dev)
+        self.qsl = torch.from_numpy(wl.query_start_loc.astype(np.int32)).to(self.dev)
+        self.out = torch.full_like(self.q, float("nan"))
+        self.workspace = None
+        ws = pa.pa_forward_workspace_size(wl.num_seqs, wl.num_tokens, wl.num_q_heads,
+                                          wl.max_seq_len, wl.max_query_len, self.k_cache)
+        if ws:
+            self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+        self.fill_context()
+
+    def _pool(self, shape, fill):
+        torch = self.torch
+        if fill == "zero":
+            return torch.zeros(shape, dtype=self.tdtype, device=self.dev)
+        if self.tdtype == torch.float32:
+            return torch.full(shape, float("nan"), dtype=torch.float32, device=self.dev)
+        return torch.full(shape, BF16_NAN_BITS, dtype=torch.int16, device=self.dev).view(torch.bfloat16)
+
+    def upload(self, arr):
+        torch = self.torch
+        if self.wl.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(arr)).to(self.dev)
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(self.dev).view(torch.bfloat16)
+
+    def fill_context(self, chunk_tokens=1 << 18):
+        """Store every cached token (the state before this step) with pa_write_kv."""
+        torch = self.torch
+        wl = self.wl
+        n = len(wl.ctx_k)
+        for a in range(0, n, chunk_tokens):
+            b = min(n, a + chunk_tokens)
+            k = self.upload(wl.ctx_k[a:b])
+            v = self.upload(wl.ctx_v[a:b])
+            s = torch.from_numpy(self.ctx_slots[a:b]).to(self.dev)
+            pa.pa_write_kv(k, v, self.k_cache, self.v_cache, s)
+            del k, v, s
+
+    def step_writes(self, stream=None):
+        """This step's cache updates: copy-on-write copies, then the new tokens' K/V."""
+        if self.pairs_d.shape[0]:
+            pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d, stream=stream)
+        pa.pa_write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.new_slots_d, stream=stream)
+
+    def forward(self, stream=None):
+        wl = self.wl
+        pa.pa_forward(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                      self.qsl, self.cached_lens, wl.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
+                      workspace=self.workspace, stream=stream)
+
+    def step(self, stream=None):
+        self.step_writes(stream)
+        self.forward(stream)
+
+    # -- host copies for checking -------------------------------------------
+    def host(self, t):
+        torch = self.torch
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    def out_f64(self):
+        torch = self.torch
+        return self.out.detach().to(torch.float64).cpu().numpy()

@@ -100,3 +100,13 @@ def compare(got, want, dtype):
     else:
         ok = max_abs <= 1e-4
     return ok, max_abs, mean_abs
+
+
+def ensure_library():
+    """Import the binding, building libpagedattn.so first if it is not there."""
+    import os
+    from paged_kv_cache_forward_amd import build as _build
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    import paged_kv_cache_forward_amd as pa
+    return pa

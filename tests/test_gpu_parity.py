@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Each case replays one seeded workload twice -- on the library (C++ allocator,
+device pools, pa_copy_blocks / pa_write_kv / pa_forward) and on the oracle
+(RefAllocator, NumPy pools, fp64 attention) -- and compares:
+  * slots, block tables and copy pairs: bit-exact;
+  * the whole K and V pools after the writes: bit-exact (NaN-poisoned
+    everywhere no write reaches);
+  * attention outputs: bf16 max-abs <= 2e-2 and mean-abs <= 2e-3, fp32
+    max-abs <= 1e-4, and every output finite.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import OracleRun, compare, ensure_library
+
+pytestmark = pytest.mark.gpu
+
+
+def _device_run(wl, **kw):
+    ensure_library()
+    from paged_kv_cache_forward_amd.replay import DeviceRun
+    run = DeviceRun(wl, **kw)
+    run.step()
+    import torch
+    torch.cuda.synchronize()
+    return run
+
+
+def check_parity(wl, seqs=None, pools=True):
+    ref = OracleRun(wl, seqs=seqs)
+    gpu = _device_run(wl)
+    # allocator results
+    assert np.array_equal(gpu.ctx_slots, ref.ctx_slots)
+    assert np.array_equal(gpu.new_slots, ref.new_slots)
+    assert [tuple(p) for p in gpu.cow] == [tuple(p) for p in ref.cow]
+    assert gpu.tables == ref.tables
+    # pools, bit for bit (allocator range; the extra guard block stays NaN on both sides)
+    if pools:
+        for dev_pool, ref_pool in ((gpu.k_cache, ref.k_cache), (gpu.v_cache, ref.v_cache)):
+            h = gpu.host(dev_pool)
+            assert h.shape == ref_pool.shape
+            assert np.array_equal(h.view(np.uint8), ref_pool.view(np.uint8))
+    got = gpu.out_f64()
+    want = ref.out
+    if seqs is not None:
+        qsl = wl.query_start_loc
+        rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in seqs])
+        got, want = got[rows], want[rows]
+    ok, max_abs, mean_abs = compare(got, want, wl.dtype)
+    print(f"[parity] {wl.name}: max_abs={max_abs:.3e} mean_abs={mean_abs:.3e}", flush=True)
+    assert ok, f"{wl.name}: max_abs={max_abs} mean_abs={mean_abs}"
+    return gpu, ref
+
+
+@pytest.mark.parametrize("name", workloads.MINI)
+def test_mini_workloads(name):
+    check_parity(workloads.mini(name))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_decode", "batched_decode", "mixed_superbatch", "shared_prefix_cow"])
+def test_named_workloads_full_size(name):
+    wl = workloads.named(name)
+    check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch"))
+
+
+@pytest.mark.timeout(1200)
+def test_long_context_sampled():
+    wl = workloads.long_context_decode()
+    L = wl.seq_lens
+    seqs = sorted({0, int(np.argmax(L)), int(np.argmin(L))})
+    check_parity(wl, seqs=seqs, pools=False)
+
+
+def _permuted_batch(wl, perm):
+    """Same trace and values, super-batch order permuted."""
+    import copy
+    w2 = copy.copy(wl)
+    qsl = wl.query_start_loc
+    w2.batch = [wl.batch[p] for p in perm]
+    w2.seq_lens = wl.seq_lens[perm]
+    w2.cached_lens = wl.cached_lens[perm]
+    w2.query_lens = wl.query_lens[perm]
+    w2.q = np.concatenate([wl.q[qsl[p]:qsl[p + 1]] for p in perm])
+    return w2, qsl
+
+
+@pytest.mark.parametrize("name", ["decode_bf16", "mixed_bf16", "decode_f32"])
+def test_bit_identical_invariances(name):
+    """Deterministic kernels: placement, batch order and stale-slot contents change no output bit."""
+    wl = workloads.mini(name)
+    base = _device_run(wl)
+    ref_bits = base.host(base.out)
+    # other physical placement
+    alt = np.random.default_rng(99).permutation(wl.num_blocks).astype(np.int32)
+    moved = _device_run(wl, free_order=alt)
+    assert moved.tables != base.tables
+    assert np.array_equal(moved.host(moved.out), ref_bits)
+    # zero-filled pool instead of NaN-filled: stale slots are never read
+    zero = _device_run(wl, fill="zero")
+    assert np.array_equal(zero.host(zero.out), ref_bits)
+    # reversed super-batch order
+    perm = np.arange(wl.num_seqs)[::-1]
+    w2, qsl = _permuted_batch(wl, perm)
+    rev = _device_run(w2)
+    rev_bits = rev.host(rev.out)
+    qsl2 = w2.query_start_loc
+    for k, p in enumerate(perm):
+        assert np.array_equal(rev_bits[qsl2[k]:qsl2[k + 1]], ref_bits[qsl[p]:qsl[p + 1]])
+    # a wider block table (more padding) changes nothing
+    wide = _device_run(wl, table_stride=max(len(t) for t in base.tables) + 7)
+    assert np.array_equal(wide.host(wide.out), ref_bits)
+
+
+@pytest.mark.parametrize("split", ["off", "16", "64", "256", "1024"])
+def test_split_sizes(split, monkeypatch):
+    """Every decode partition size meets the tolerance (the merge is exercised hard at 16)."""
+    monkeypatch.setenv("PA_SPLIT", split)
+    check_parity(workloads.mini("decode_gqa8"), pools=False)
+    check_parity(workloads.mini("decode_bf16"), pools=False)
+
+
+def test_degenerate_batches():
+    ensure_library()
+    # sequences with no query rows between others, a length-1 context, and a 1-token chunk
+    wl = workloads.independent("degenerate", 31, Hq=8, Hkv=2, D=128, dtype="bf16",
+                               cached=[5, 0, 33, 0, 16], new=[0, 1, 0, 2, 1], pool_extra=2)
+    check_parity(wl)
+    wl = workloads.independent("all_len1", 32, Hq=4, Hkv=4, D=64, dtype="f32",
+                               cached=[0] * 9, new=[1] * 9)
+    check_parity(wl)
+    # a lone long prefill with no decode rows (G = 1, D = 128)
+    wl = workloads.independent("lone_prefill", 33, Hq=2, Hkv=2, D=128, dtype="bf16",
+                               cached=[300], new=[333], pool_extra=1)
+    check_parity(wl)
+
+
+def test_write_kv_padding_and_out_of_pool_slots():
+    pa = ensure_library()
+    import torch
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(5)
+    nb, Hkv, D = 6, 2, 64
+    k = rng.standard_normal((5, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((5, Hkv, D)).astype(np.float32)
+    slots = np.array([3, -1, 95, nb * 16 + 4, 17], dtype=np.int64)   # pad, last slot, beyond pool
+    kc = np.zeros((nb, Hkv, 16, D), np.float32)
+    vc = np.zeros_like(kc)
+    keep = np.array([True, False, True, False, True])
+    oracle.ref_write_kv(kc, vc, k[keep], v[keep], slots[keep], 16)
+    kd = torch.zeros(kc.shape, dtype=torch.float32, device=dev)
+    vd = torch.zeros_like(kd)
+    pa.pa_write_kv(torch.from_numpy(k).to(dev), torch.from_numpy(v).to(dev), kd, vd,
+                   torch.from_numpy(slots).to(dev))
+    assert np.array_equal(kd.cpu().numpy(), kc) and np.array_equal(vd.cpu().numpy(), vc)
+    # zero tokens is a no-op
+    pa.pa_write_kv(torch.empty((0, Hkv, D), device=dev), torch.empty((0, Hkv, D), device=dev), kd, vd,
+                   torch.empty((0,), dtype=torch.int64, device=dev))
+    assert np.array_equal(kd.cpu().numpy(), kc)
+
+
+def test_copy_blocks_bit_exact():
+    pa = ensure_library()
+    import torch
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(6)
+    kc = rng.integers(0, 2**16, size=(9, 8, 16, 128), dtype=np.uint16)
+    vc = rng.integers(0, 2**16, size=(9, 8, 16, 128), dtype=np.uint16)
+    pairs = [(1, 4), (2, 7), (8, 0)]
+    kd = torch.from_numpy(kc.view(np.int16)).to(dev).view(torch.bfloat16)
+    vd = torch.from_numpy(vc.view(np.int16)).to(dev).view(torch.bfloat16)
+    pa.pa_copy_blocks(kd, vd, torch.tensor(pairs, dtype=torch.int32, device=dev))
+    oracle.ref_copy_blocks(kc, vc, pairs)
+    assert np.array_equal(kd.view(torch.int16).cpu().numpy().view(np.uint16), kc)
+    assert np.array_equal(vd.view(torch.int16).cpu().numpy().view(np.uint16), vc)
+
+
+def test_error_paths(monkeypatch):
+    pa = ensure_library()
+    import torch
+    from paged_kv_cache_forward_amd.replay import DeviceRun
+    wl = workloads.mini("decode_bf16")
+    run = DeviceRun(wl)
+    run.step_writes()
+    # workspace smaller than required
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.pa_forward(run.out, run.q, run.k_cache, run.v_cache, run.block_tables, run.seq_lens, run.qsl,
+                      run.cached_lens, wl.max_seq_len, 1, wl.scale, True,
+                      workspace=torch.empty(16, dtype=torch.uint8, device=run.dev))
+    assert e.value.status == pa.PA_ERR_ARG
+    # check mode catches metadata violations before launching
+    monkeypatch.setenv("PA_CHECK", "1")
+    bad = run.block_tables.clone()
+    bad[0, 0] = wl.pool_blocks + 5
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.pa_forward(run.out, run.q, run.k_cache, run.v_cache, bad, run.seq_lens, run.qsl,
+                      run.cached_lens, wl.max_seq_len, 1, wl.scale, True, workspace=run.workspace)
+    assert e.value.status == pa.PA_ERR_RANGE
+    with pytest.raises(pa.PagedAttnError) as e:   # max_seq_len below a real length
+        pa.pa_forward(run.out, run.q, run.k_cache, run.v_cache, run.block_tables, run.seq_lens, run.qsl,
+                      run.cached_lens, 3, 1, wl.scale, True, workspace=run.workspace)
+    assert e.value.status == pa.PA_ERR_RANGE
+    dup = torch.tensor([7, 7], dtype=torch.int64, device=run.dev)
+    with pytest.raises(pa.PagedAttnError) as e:
+        pa.pa_write_kv(run.k_new[:2], run.v_new[:2], run.k_cache, run.v_cache, dup)
+    assert e.value.status == pa.PA_ERR_RANGE
+    # the valid call still passes in check mode
+    run.forward()
+    torch.cuda.synchronize()
+    # without check mode an out-of-range table entry is clamped: finite output, no fault
+    monkeypatch.setenv("PA_CHECK", "0")
+    pa.pa_forward(run.out, run.q, run.k_cache, run.v_cache, bad, run.seq_lens, run.qsl,
+                  run.cached_lens, wl.max_seq_len, 1, wl.scale, True, workspace=run.workspace)
+    torch.cuda.synchronize()

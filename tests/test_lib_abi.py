@@ -1,0 +1,73 @@
+"""The C-ABI library loads on a machine without a GPU and exports every call its header declares."""
+
+import os
+import re
+
+from helpers import ensure_library
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(pa_[a-z0-9_]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("pa_write_kv", "pa_copy_blocks", "pa_forward", "pa_forward_workspace_size",
+                     "pa_alloc_create", "pa_seq_append", "pa_seq_fork", "pa_seq_free", "pa_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    pa = ensure_library()
+    for name in declared_functions():
+        assert hasattr(pa.lib, name), f"{name} declared in the header but not exported"
+    assert set(declared_functions()) == set(pa.EXPORTED)
+
+
+def test_version_and_error_strings():
+    pa = ensure_library()
+    assert "gfx950" in pa.version()
+    assert isinstance(pa.lib.pa_last_error().decode(), str)
+
+
+def test_host_argument_errors_without_a_gpu():
+    # Argument checks run before any HIP call, so they work with no device present.
+    import ctypes
+    pa = ensure_library()
+    desc = pa.CacheDesc(32, 2, 64, 8, pa.PA_F32)          # block_size 8: not built
+    st = pa.lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(desc), None)
+    assert st == pa.PA_ERR_UNSUPPORTED and "block_size" in pa.lib.pa_last_error().decode()
+    desc = pa.CacheDesc(32, 2, 96, 16, pa.PA_BF16)        # head_dim 96: not built for attention
+    assert pa.lib.pa_forward_workspace_size(4, 4, 4, 100, 1, ctypes.byref(desc)) == 0
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 4, 4, 100, 1,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)
+    assert st == pa.PA_ERR_UNSUPPORTED
+    desc = pa.CacheDesc(32, 2, 64, 16, pa.PA_BF16)
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 4, 6, 100, 1,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)   # 6 q heads / 2 kv heads = 3
+    assert st == pa.PA_ERR_UNSUPPORTED
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 4, 5, 100, 1,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)   # not a multiple
+    assert st == pa.PA_ERR_ARG
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 4, 4, 100, 1,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)   # NULL device pointers
+    assert st == pa.PA_ERR_ARG
+    # empty batch is a no-op
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 0, 0, 4, 0, 0,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)
+    assert st == pa.PA_OK
+
+
+def test_workspace_size_follows_the_split():
+    import ctypes
+    pa = ensure_library()
+    desc = pa.CacheDesc(20000, 8, 128, 16, pa.PA_BF16)
+    small = pa.lib.pa_forward_workspace_size(64, 64, 32, 200, 1, ctypes.byref(desc))
+    big = pa.lib.pa_forward_workspace_size(64, 64, 32, 4096, 1, ctypes.byref(desc))
+    assert small == 0 and big > 0
+    assert big % (64 * 32 * (128 + 2) * 4) == 0
