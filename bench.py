@@ -49,8 +49,8 @@ def prefill_flops(wl):
     f = 0
     for c, n in zip(wl.cached_lens.astype(np.int64), wl.query_lens.astype(np.int64)):
         if n > 1:
-            f += 4 * wl.num_q_heads * wl.head_dim * (c * n + n * (n + 1) // 2)
-    return f
+            f += 4 * wl.num_q_heads * wl.head_dim * int(c * n + n * (n + 1) // 2)
+    return int(f)
 
 
 def time_steps(run, steps, warmup, stream, with_writes=True):

@@ -3,8 +3,9 @@
 Every computation runs in the HIP library; this module turns torch tensors
 into device pointers and shapes, passes the current HIP stream, and raises on
 a non-OK status.  It never computes attention, slots or block tables itself,
-and there is no fallback: if ``libpagedattn.so`` is missing, importing the
-binding fails.
+and there is no fallback: if ``libpagedattn.so`` is missing, the first call
+into the library raises ImportError (the module itself imports without it so
+that ``paged_kv_cache_forward_amd.build`` can create it).
 
 Functions carry the C names: ``pa_write_kv``, ``pa_copy_blocks``,
 ``pa_forward_workspace_size``, ``pa_forward``; ``BlockAllocator`` wraps the
@@ -46,11 +47,6 @@ class AllocStats(ctypes.Structure):
                  "tokens_logical", "slots_logical", "slots_physical")]
 
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run paged_kv_cache_forward_amd.build.build()")
-
-lib = ctypes.CDLL(LIB_PATH)
-
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
 _pdesc = ctypes.POINTER(CacheDesc)
@@ -74,24 +70,46 @@ _SIGS = {
     "pa_block_refcount": (_i32, [_vp, _i32]),
     "pa_alloc_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
 }
-for _name, (_res, _args) in _SIGS.items():
-    _fn = getattr(lib, _name)
-    _fn.restype = _res
-    _fn.argtypes = _args
+
+_LIB = None
+
+
+def _load():
+    """Load libpagedattn.so (once).  There is no fallback: a missing library is an error."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run paged_kv_cache_forward_amd.build.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def __getattr__(name):
+    # `paged_kv_cache_forward_amd.lib` is the loaded library; loading happens on
+    # first use so that the `build` submodule can be imported before it exists.
+    if name == "lib":
+        return _load()
+    raise AttributeError(name)
+
 
 EXPORTED = tuple(_SIGS)
 
 
 def _check(status):
     if status != PA_OK:
-        msg = lib.pa_last_error().decode()
+        msg = _load().pa_last_error().decode()
         if status == PA_ERR_OOM:
             raise OutOfBlocks(status, msg)
         raise PagedAttnError(status, msg)
 
 
 def version():
-    return lib.pa_version().decode()
+    return _load().pa_version().decode()
 
 
 # -- device calls (torch tensors) ---------------------------------------------
@@ -143,7 +161,7 @@ def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     T = k.shape[0]
     if k.dim() != 3 or k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or slot_mapping.shape != (T,):
         raise ValueError("k/v must be [T][num_kv_heads][head_dim] and slot_mapping [T]")
-    _check(lib.pa_write_kv(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    _check(_load().pa_write_kv(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(slot_mapping, "slot_mapping", torch.int64), T, ctypes.byref(desc),
                            _stream(stream)))
 
@@ -153,14 +171,14 @@ def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
     desc = cache_desc(k_cache)
     if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be [n][2]")
-    _check(lib.pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    _check(_load().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                               _dev(pairs, "pairs", torch.int32), pairs.shape[0], ctypes.byref(desc),
                               _stream(stream)))
 
 
 def pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):
     desc = cache_desc(k_cache)
-    return int(lib.pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len,
+    return int(_load().pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len,
                                              max_query_len, ctypes.byref(desc)))
 
 
@@ -185,7 +203,7 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.pa_forward(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    _check(_load().pa_forward(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                           _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
                           _dev(seq_lens, "seq_lens", torch.int32),
                           _dev(query_start_loc, "query_start_loc", torch.int32),
@@ -205,24 +223,24 @@ class BlockAllocator:
         if free_order is not None:
             self._order = np.ascontiguousarray(free_order, dtype=np.int32)
             order = self._order.ctypes.data_as(_pi32)
-        _check(lib.pa_alloc_create(num_blocks, block_size, order, ctypes.byref(self._h)))
+        _check(_load().pa_alloc_create(num_blocks, block_size, order, ctypes.byref(self._h)))
         self.num_blocks = num_blocks
         self.block_size = block_size
 
     def __del__(self):
         h = getattr(self, "_h", None)
         if h and h.value:
-            lib.pa_alloc_destroy(h)
+            _load().pa_alloc_destroy(h)
             self._h = ctypes.c_void_p()
 
     def create(self):
         sid = ctypes.c_int32()
-        _check(lib.pa_seq_create(self._h, ctypes.byref(sid)))
+        _check(_load().pa_seq_create(self._h, ctypes.byref(sid)))
         return sid.value
 
     def fork(self, parent, share_tokens):
         sid = ctypes.c_int32()
-        _check(lib.pa_seq_fork(self._h, parent, share_tokens, ctypes.byref(sid)))
+        _check(_load().pa_seq_fork(self._h, parent, share_tokens, ctypes.byref(sid)))
         return sid.value
 
     def append(self, seq, n_tokens, cow_cap=4):
@@ -230,37 +248,37 @@ class BlockAllocator:
         slots = np.empty(max(n_tokens, 1), dtype=np.int64)
         pairs = np.empty(2 * cow_cap, dtype=np.int32)
         n_cow = ctypes.c_int32()
-        _check(lib.pa_seq_append(self._h, seq, n_tokens, slots.ctypes.data_as(_pi64),
+        _check(_load().pa_seq_append(self._h, seq, n_tokens, slots.ctypes.data_as(_pi64),
                                  pairs.ctypes.data_as(_pi32), cow_cap, ctypes.byref(n_cow)))
         return slots[:n_tokens], [(int(pairs[2 * k]), int(pairs[2 * k + 1])) for k in range(n_cow.value)]
 
     def free_seq(self, seq):
-        _check(lib.pa_seq_free(self._h, seq))
+        _check(_load().pa_seq_free(self._h, seq))
 
     def block_table(self, seq):
         nb, ln = ctypes.c_int32(), ctypes.c_int32()
-        _check(lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
+        _check(_load().pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
         out = np.empty(max(nb.value, 1), dtype=np.int32)
-        _check(lib.pa_seq_block_table(self._h, seq, out.ctypes.data_as(_pi32), nb.value,
+        _check(_load().pa_seq_block_table(self._h, seq, out.ctypes.data_as(_pi32), nb.value,
                                       ctypes.byref(nb), ctypes.byref(ln)))
         return out[:nb.value].tolist()
 
     def length(self, seq):
         nb, ln = ctypes.c_int32(), ctypes.c_int32()
-        _check(lib.pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
+        _check(_load().pa_seq_block_table(self._h, seq, None, 0, ctypes.byref(nb), ctypes.byref(ln)))
         return ln.value
 
     def stats(self):
         st = AllocStats()
-        _check(lib.pa_alloc_stats(self._h, ctypes.byref(st)))
+        _check(_load().pa_alloc_stats(self._h, ctypes.byref(st)))
         return {name: getattr(st, name) for name, _ in AllocStats._fields_}
 
     def refcount(self, block):
-        return int(lib.pa_block_refcount(self._h, block))
+        return int(_load().pa_block_refcount(self._h, block))
 
     def free_list(self):
         n = ctypes.c_int32()
-        _check(lib.pa_alloc_free_list(self._h, None, 0, ctypes.byref(n)))
+        _check(_load().pa_alloc_free_list(self._h, None, 0, ctypes.byref(n)))
         out = np.empty(max(n.value, 1), dtype=np.int32)
-        _check(lib.pa_alloc_free_list(self._h, out.ctypes.data_as(_pi32), n.value, ctypes.byref(n)))
+        _check(_load().pa_alloc_free_list(self._h, out.ctypes.data_as(_pi32), n.value, ctypes.byref(n)))
         return out[:n.value].tolist()

@@ -128,16 +128,36 @@ struct RowState {
   }
 };
 
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_tile(const uint8_t* kbase, const uint8_t* vbase, int lane_off,
+// One (block, KV head) tile: 16 rows of ROW_BYTES, addressed through a buffer
+// descriptor built in SGPRs from the block's base pointer, so each lane's
+// offset inside the tile is a constant and no per-block vector address math is
+// needed.  The descriptor's range is exactly the tile.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int lane_off,
                                           uint4 (&kq)[Tile<T, D>::CPL], uint4 (&vq)[Tile<T, D>::CPL]) {
   using TL = Tile<T, D>;
 #pragma unroll
-  for (int u = 0; u < TL::CPL; ++u) {
-    kq[u] = ld16(kbase + lane_off + u * TL::R * TL::ROW_BYTES);
-    vq[u] = ld16(vbase + lane_off + u * TL::R * TL::ROW_BYTES);
-  }
+  for (int u = 0; u < TL::CPL; ++u) kq[u] = buf_ld16(rk, lane_off + u * TL::R * TL::ROW_BYTES);
+#pragma unroll
+  for (int u = 0; u < TL::CPL; ++u) vq[u] = buf_ld16(rv, lane_off + u * TL::R * TL::ROW_BYTES);
 }
+
+// The running max only moves when a score exceeds it by more than this (in
+// base-2 units); until then the weights exp2(s - m) stay below 2^8 and the
+// accumulators need no rescaling.  The result is the same softmax: l and acc
+// always share one reference max per row group.
+constexpr float kRescaleSlack = 8.0f;
 
 // Fold one block tile (tokens tok0 .. tok0+15) into the row group's state.
 template <typename T, int D, int G>
@@ -150,38 +170,43 @@ __device__ __forceinline__ void fold_tile(const uint4 (&kq)[Tile<T, D>::CPL], ui
 #pragma unroll
   for (int u = 0; u < CPL; ++u)
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[u][h] = group_sum<TL::CPR>(chunk_dot<T>(qv[h], kq[u]));
+    for (int h = 0; h < G; ++h) s[u][h] = group_sum<TL::CPR>(chunk_dot<T>(qv[h], kq[u])) * scale_log2;
 
-  const bool tail = tok0 + kBlock > t_end;  // wave-uniform
+  if (tok0 + kBlock > t_end) {  // wave-uniform: only a range's last block is partial
+#pragma unroll
+    for (int u = 0; u < CPL; ++u) {
+      const bool valid = tok0 + u * TL::R + rg < t_end;
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[u][h] = valid ? s[u][h] : -INFINITY;
+      if (!valid) vq[u] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   float vf[CPL][E];
 #pragma unroll
-  for (int u = 0; u < CPL; ++u) {
-    const bool valid = tok0 + u * TL::R + rg < t_end;
-#pragma unroll
-    for (int h = 0; h < G; ++h) s[u][h] = valid ? s[u][h] * scale_log2 : -INFINITY;
-    uint4 w = vq[u];
-    if (tail && !valid) w = make_uint4(0u, 0u, 0u, 0u);
-    widen<T>(w, vf[u]);
-  }
+  for (int u = 0; u < CPL; ++u) widen<T>(vq[u], vf[u]);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float bm = s[0][h];
 #pragma unroll
     for (int u = 1; u < CPL; ++u) bm = fmaxf(bm, s[u][h]);
-    const float mn = fmaxf(st.m[h], bm);
-    const float alpha = fast_exp2(st.m[h] - mn);
-    st.m[h] = mn;
+    const bool need = bm > st.m[h] + kRescaleSlack;
+    if (__any(need)) {  // wave-uniform branch; rare after a range's first block
+      const float mn = need ? bm : st.m[h];
+      const float alpha = fast_exp2(st.m[h] - mn);
+      st.m[h] = mn;
+      st.l[h] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[h][e] *= alpha;
+    }
     float p[CPL];
-    float ps = 0.0f;
 #pragma unroll
     for (int u = 0; u < CPL; ++u) {
-      p[u] = fast_exp2(s[u][h] - mn);
-      ps += p[u];
+      p[u] = fast_exp2(s[u][h] - st.m[h]);
+      st.l[h] += p[u];
     }
-    st.l[h] = fmaf(st.l[h], alpha, ps);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      float a = st.acc[h][e] * alpha;
+      float a = st.acc[h][e];
 #pragma unroll
       for (int u = 0; u < CPL; ++u) a = fmaf(p[u], vf[u][e], a);
       st.acc[h][e] = a;
@@ -191,10 +216,16 @@ __device__ __forceinline__ void fold_tile(const uint4 (&kq)[Tile<T, D>::CPL], ui
 
 // Attend query row `row` of sequence i (KV head g) over logical tokens [t0, t1);
 // t0 is a multiple of 16 and t1 > t0.
+//
+// Blocks stream through two register buffers: while one block is folded the
+// next one's loads are in flight.  The prefetch is issued unconditionally
+// (its index clamped to the last block) so the compiler's wait counts only
+// ever wait for the buffer being folded, never for the one in flight.
 template <typename T, int D, int G>
 __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, int row, int t0, int t1,
                                              RowState<G, Tile<T, D>::E>& st) {
   using TL = Tile<T, D>;
+  constexpr int CPL = TL::CPL;
   const int lane = threadIdx.x;
   const int col = lane % TL::CPR;
   const int rg = lane / TL::CPR;
@@ -206,36 +237,29 @@ __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, in
   for (int h = 0; h < G; ++h) qv[h] = ld16(qrow + h * TL::ROW_BYTES + col * 16);
 
   const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
-  const size_t tile_bytes = (size_t)kBlock * TL::ROW_BYTES;
+  constexpr int tile_bytes = kBlock * TL::ROW_BYTES;
   const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * tile_bytes;
   const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * tile_bytes;
   const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
 
   const int b_first = t0 / kBlock;
-  const int b_last = (t1 - 1) / kBlock;
-  for (int bb = b_first; bb <= b_last; bb += 64) {
-    const int nb = min(64, b_last - bb + 1);
-    const int my_bid = lane < nb ? clamp_block(bt_row[bb + lane], a.num_blocks) : 0;
-    uint4 kq[TL::CPL], vq[TL::CPL];
-    {
-      const int bid = __builtin_amdgcn_readfirstlane(my_bid);
-      load_tile<T, D, G>(kc + bid * block_stride, vc + bid * block_stride, lane_off, kq, vq);
-    }
-    for (int j = 0; j < nb; ++j) {
-      uint4 kn[TL::CPL], vn[TL::CPL];
-      const bool more = j + 1 < nb;
-      if (more) {
-        const int bid = __builtin_amdgcn_readlane(my_bid, j + 1);
-        load_tile<T, D, G>(kc + bid * block_stride, vc + bid * block_stride, lane_off, kn, vn);
-      }
-      fold_tile<T, D, G>(kq, vq, qv, (bb + j) * kBlock, t1, rg, a.scale_log2, st);
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < TL::CPL; ++u) {
-          kq[u] = kn[u];
-          vq[u] = vn[u];
-        }
-      }
+  const int nbt = (t1 - 1) / kBlock - b_first + 1;
+  for (int bb = 0; bb < nbt; bb += 64) {
+    const int nb = min(64, nbt - bb);
+    const int my_bid = lane < nb ? clamp_block(bt_row[b_first + bb + lane], a.num_blocks) : 0;
+    const int tok_base = (b_first + bb) * kBlock;
+    uint4 ka[CPL], va[CPL], kb[CPL], vb[CPL];
+    auto issue = [&](int j, uint4 (&kq)[CPL], uint4 (&vq)[CPL]) {
+      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, j) * block_stride;
+      load_tile<T, D>(tile_rsrc(kc + off, tile_bytes), tile_rsrc(vc + off, tile_bytes), lane_off, kq, vq);
+    };
+    issue(0, ka, va);
+    for (int j = 0; j < nb; j += 2) {
+      issue(min(j + 1, nb - 1), kb, vb);
+      fold_tile<T, D, G>(ka, va, qv, tok_base + j * kBlock, t1, rg, a.scale_log2, st);
+      if (j + 1 >= nb) break;
+      issue(min(j + 2, nb - 1), ka, va);
+      fold_tile<T, D, G>(kb, vb, qv, tok_base + (j + 1) * kBlock, t1, rg, a.scale_log2, st);
     }
   }
 }
