@@ -118,6 +118,29 @@ def cpu_baseline(wl, budget_s=15.0):
     }
 
 
+def copy_probe(pa, torch, stream, steps):
+    """pa_copy_blocks over 16384 pairs of 32 KiB blocks (K and V): 1 GiB read and 1 GiB written per launch."""
+    nb, hkv, d = 32768, 8, 128
+    kc = torch.zeros((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    half = nb // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], dim=1).to(torch.int32).cuda()
+    per_launch = 2 * half * hkv * 16 * d * 2
+    for _ in range(2):
+        pa.pa_copy_blocks(kc, vc, pairs, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        pa.pa_copy_blocks(kc, vc, pairs, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    print(json.dumps({"probe": "pa_copy_blocks", "bytes_read_per_launch": per_launch,
+                      "bytes_written_per_launch": per_launch, "ms": round(ms, 5),
+                      "copy_gbs": round(2 * per_launch / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +149,9 @@ def main():
     ap.add_argument("--workload", default="batched_decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
+                         "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -141,6 +167,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     stream = torch.cuda.current_stream()
+
+    if args.copy_probe:
+        copy_probe(pa, torch, stream, args.steps)
+        return
 
     log(f"generating workload {args.workload}")
     wl = workloads.named(args.workload)

@@ -170,8 +170,15 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *                    (may be NULL when that size is 0); contents need no init
  *
  * Supported: dtype f32 or bf16; head_dim 64 or 128; num_q_heads/num_kv_heads
- * in {1, 2, 4, 8}; block_size 16.  Environment PA_SPLIT=auto (default) |
- * off | <tokens> (a multiple of 16, <= 1024) sets the decode partition size.
+ * in {1, 2, 4, 8}; block_size 16.  bf16 with head_dim 128 runs the scores of
+ * the decode rows on the matrix cores; other combinations use the vector path.
+ * Tuning knobs (environment, read on every call; results stay within the
+ * stated tolerance under every setting):
+ *   PA_SPLIT=auto (default) | off | <tokens>   decode partition size (a multiple
+ *            of 16, <= 8192); auto aims at ~4096 (sequence, KV head, partition)
+ *            work-groups with partitions of 128..2048 tokens
+ *   PA_DECODE_WAVES=1|2|4   waves per decode work-group (matrix-core path)
+ *   PA_DECODE=valu          force the vector decode kernel
  * Errors: PA_ERR_ARG (incl. a workspace smaller than required),
  * PA_ERR_UNSUPPORTED, PA_ERR_RANGE (check mode), PA_ERR_HIP.
  */

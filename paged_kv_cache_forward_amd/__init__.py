@@ -182,13 +182,19 @@ def pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, ma
                                              max_query_len, ctypes.byref(desc)))
 
 
+def new_workspace(nbytes, device):
+    """A uint8 device tensor of ``nbytes`` for ``pa_forward``'s split-KV partials."""
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
                max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
     """Attention for the super-batch; ``out`` is written in place.
 
     ``workspace`` is a uint8 device tensor of at least
-    ``pa_forward_workspace_size(...)`` bytes; when omitted, one is allocated
-    here from torch's caching allocator.
+    ``pa_forward_workspace_size(...)`` bytes (contents need no initialisation);
+    when omitted, one is allocated here from torch's caching allocator.
     """
     torch = _torch()
     desc = cache_desc(k_cache)
@@ -200,7 +206,7 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
         raise ValueError("metadata shapes do not match num_seqs")
     need = pa_forward_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_load().pa_forward(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),

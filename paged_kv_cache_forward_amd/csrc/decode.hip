@@ -44,7 +44,7 @@
 
 namespace pa {
 
-constexpr int kMaxParts = 4096;   // merge keeps one weight per partition in LDS
+constexpr int kMaxParts = 4096;   // bound on partitions per sequence
 
 struct DecodeKernelArgs {
   AttnArgs a;
@@ -132,17 +132,6 @@ struct RowState {
 // descriptor built in SGPRs from the block's base pointer, so each lane's
 // offset inside the tile is a constant and no per-block vector address math is
 // needed.  The descriptor's range is exactly the tile.
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
 template <typename T, int D>
 __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int lane_off,
                                           uint4 (&kq)[Tile<T, D>::CPL], uint4 (&vq)[Tile<T, D>::CPL]) {
@@ -152,12 +141,6 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_bu
 #pragma unroll
   for (int u = 0; u < TL::CPL; ++u) vq[u] = buf_ld16(rv, lane_off + u * TL::R * TL::ROW_BYTES);
 }
-
-// The running max only moves when a score exceeds it by more than this (in
-// base-2 units); until then the weights exp2(s - m) stay below 2^8 and the
-// accumulators need no rescaling.  The result is the same softmax: l and acc
-// always share one reference max per row group.
-constexpr float kRescaleSlack = 8.0f;
 
 // Fold one block tile (tokens tok0 .. tok0+15) into the row group's state.
 template <typename T, int D, int G>
@@ -346,18 +329,21 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeKernelArgs k) {
   }
 }
 
-// One block of 256 threads per (sequence, query head): weights exp2(m_p - M)
-// for every partition, then the weighted sum of the partial accumulators in
-// ascending partition order within each thread's share, reduced in LDS.
+// Split-KV merge: one work-group of 256 threads per (sequence, query head).
+// The threads form R = 256 / (D/4) row groups of D/4 lanes (four output
+// columns per lane); row group r folds partitions r, r+R, r+2R, ... in that
+// order with the log-sum-exp rule, U partitions at a time so their loads are
+// in flight together, and the R row groups are then combined in ascending
+// order through LDS.  The order is fixed, so the result is deterministic.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int32_t part_tokens, int32_t max_parts,
                                                     const float* __restrict__ p_acc,
                                                     const float* __restrict__ p_ml) {
-  constexpr int TPP = D / 4;          // threads per partition row (4 floats each)
-  constexpr int NG = 256 / TPP;       // partition groups
-  __shared__ float w_s[kMaxParts];
-  __shared__ float red[NG][D];
-  __shared__ float wred[4];
+  constexpr int TPR = D / 4;      // lanes per partition row
+  constexpr int R = 256 / TPR;    // row groups
+  constexpr int U = 4;            // partitions per row group per batch
+  __shared__ float s_m[R], s_l[R];
+  __shared__ float4 s_acc[R][TPR];
   const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int q0 = a.qsl[i];
   if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
@@ -366,56 +352,76 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int32_t part_tok
   const int P = min((L + part_tokens - 1) / part_tokens, max_parts);
   if (P <= 1) return;
   const size_t item0 = ((size_t)i * a.num_q_heads + h) * max_parts;
-  const float* ml = p_ml + item0 * 2;
-  const float* acc = p_acc + item0 * D;
+  const float2* ml = reinterpret_cast<const float2*>(p_ml) + item0;
+  const float4* acc = reinterpret_cast<const float4*>(p_acc + item0 * D);
+  const int d4 = tid % TPR, r = tid / TPR;
 
-  float M = -INFINITY;
-  for (int p = tid; p < P; p += 256) M = fmaxf(M, ml[2 * p]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) wred[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  __syncthreads();
-
-  float den = 0.0f;
-  for (int p = tid; p < P; p += 256) {
-    const float w = fast_exp2(ml[2 * p] - M);
-    w_s[p] = w;
-    den = fmaf(w, ml[2 * p + 1], den);
-  }
-  den = wave_sum(den);
-  if ((tid & 63) == 0) wred[tid >> 6] = den;
-  __syncthreads();
-  den = (wred[0] + wred[1]) + (wred[2] + wred[3]);
-
-  const int d4 = tid % TPP, pg = tid / TPP;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p = pg; p < P; p += NG) {
-    const float w = w_s[p];
-    const float4 v = *reinterpret_cast<const float4*>(acc + (size_t)p * D + d4 * 4);
-    s.x = fmaf(w, v.x, s.x); s.y = fmaf(w, v.y, s.y); s.z = fmaf(w, v.z, s.z); s.w = fmaf(w, v.w, s.w);
-  }
-  *reinterpret_cast<float4*>(&red[pg][d4 * 4]) = s;
-  __syncthreads();
-  if (tid < D) {
-    float t = 0.0f;
+  float M = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = r; p0 < P; p0 += R * U) {
+    float2 v[U];
+    float4 x[U];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) t += red[q][tid];
-    red[0][tid] = t / den;
+    for (int u = 0; u < U; ++u) {
+      const int pp = p0 + u * R;
+      if (pp < P) {
+        v[u] = ml[pp];
+        x[u] = acc[(size_t)pp * TPR + d4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p0 + u * R >= P) break;
+      const float Mn = fmaxf(M, v[u].x);       // partition maxima are finite
+      const float sa = fast_exp2(M - Mn);      // 0 on the first partition (M = -inf)
+      const float sb = fast_exp2(v[u].x - Mn);
+      den = fmaf(den, sa, v[u].y * sb);
+      num.x = fmaf(num.x, sa, x[u].x * sb);
+      num.y = fmaf(num.y, sa, x[u].y * sb);
+      num.z = fmaf(num.z, sa, x[u].z * sb);
+      num.w = fmaf(num.w, sa, x[u].w * sb);
+      M = Mn;
+    }
+  }
+  s_acc[r][d4] = num;
+  if (d4 == 0) {
+    s_m[r] = M;
+    s_l[r] = den;
   }
   __syncthreads();
-  constexpr int E = Elem<T>::per16;
-  if (tid < D / E) {
-    uint8_t* orow = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + h) * D * Elem<T>::bytes;
-    store_chunk<T>(orow + tid * 16, &red[0][tid * E]);
+  if (r != 0) return;
+  float Mt = s_m[0];
+#pragma unroll
+  for (int q = 1; q < R; ++q) Mt = fmaxf(Mt, s_m[q]);
+  float dt = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const float f = fast_exp2(s_m[q] - Mt);   // row groups without partitions: -inf -> 0
+    const float4 y = s_acc[q][d4];
+    dt = fmaf(f, s_l[q], dt);
+    o.x = fmaf(f, y.x, o.x); o.y = fmaf(f, y.y, o.y); o.z = fmaf(f, y.z, o.z); o.w = fmaf(f, y.w, o.w);
+  }
+  const float inv = 1.0f / dt;
+  float f4[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+  uint8_t* orow = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + h) * D * Elem<T>::bytes;
+  if constexpr (Elem<T>::bytes == 2) {
+    *reinterpret_cast<uint2*>(orow + d4 * 8) = make_uint2(pack_bf16x2(f4[0], f4[1]), pack_bf16x2(f4[2], f4[3]));
+  } else {
+    *reinterpret_cast<float4*>(orow + d4 * 16) = make_float4(f4[0], f4[1], f4[2], f4[3]);
   }
 }
 
 // ---------------------------------------------------------------------------
 
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t max_seq_len) {
+                            int32_t head_dim, int32_t dtype, int32_t max_seq_len) {
   DecodePlan pl{};
+  const int32_t group = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
+  const char* kind = std::getenv("PA_DECODE");
+  pl.mfma = decode_mfma_supported(dtype, head_dim, group) && !(kind != nullptr && std::strcmp(kind, "valu") == 0);
   const int32_t whole = max_seq_len > 0 ? ((max_seq_len + kBlock - 1) / kBlock) * kBlock : kBlock;
   int32_t part = whole;
   const char* env = std::getenv("PA_SPLIT");
@@ -423,21 +429,30 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
     part = whole;
   } else if (env != nullptr && std::strcmp(env, "auto") != 0 && env[0] != '\0') {
     part = std::atoi(env);
-    if (part < kBlock || part % kBlock != 0 || part > 1024) part = 512;
-  } else {
-    // Enough independent (sequence, KV head, partition) waves to keep every
-    // SIMD streaming: split anything longer than 256 tokens.
-    if (max_seq_len > 256) {
-      const int64_t items = (int64_t)num_seqs * num_kv_heads;
-      part = items * ((max_seq_len + 255) / 256) <= 16384 ? 256 : 512;
-    }
+    if (part < kBlock || part % kBlock != 0 || part > 8192) part = 512;
+  } else if (max_seq_len > 256) {
+    // Size partitions so that (sequence, KV head, partition) work-groups number
+    // about 4096 (several per CU, so the dispatcher balances ragged lengths),
+    // at least 128 tokens each: part ~ S * Hkv * max_seq_len / 4096, rounded
+    // to the nearest power of two in [128, 2048].  Measured on MI355X.
+    const double want = (double)num_seqs * num_kv_heads * max_seq_len / 4096.0;
+    part = 128;
+    while (part < 2048 && want > 1.5 * part) part *= 2;
+  }
+  // Long partitions are shared by four waves of one work-group.
+  pl.waves = part >= 2048 ? 4 : 1;
+  if (const char* wv = std::getenv("PA_DECODE_WAVES")) {
+    const int v = std::atoi(wv);
+    if (v == 1 || v == 2 || v == 4) pl.waves = v;
   }
   while ((whole + part - 1) / part > kMaxParts) part *= 2;
   pl.part_tokens = part;
   pl.max_parts = (whole + part - 1) / part;
-  pl.partial_bytes = pl.max_parts > 1
-                         ? (size_t)num_seqs * num_q_heads * pl.max_parts * (head_dim + 2) * sizeof(float)
-                         : 0;
+  if (pl.max_parts > 1) {
+    const size_t items = (size_t)num_seqs * num_q_heads * pl.max_parts;
+    pl.acc_bytes = round256(items * head_dim * sizeof(float));
+    pl.ml_bytes = round256(items * 2 * sizeof(float));
+  }
   return pl;
 }
 

@@ -17,6 +17,11 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kBlock = 16;          // tokens per cache block
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f; // running-max start: finite, so 2^(m_old - m_new) never sees inf - inf
+// Online softmax with a lazy reference: the running max only moves when a score
+// exceeds it by more than this (base-2 units), so weights exp2(s - m) stay below
+// 2^8 and accumulators are rarely rescaled.  l and acc always share one reference
+// max, so the normalised result is the same softmax.
+constexpr float kRescaleSlack = 8.0f;
 
 // bf16 <-> fp32.  Stored bf16 is the upper half of the fp32 bit pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -92,6 +97,32 @@ template <> struct Elem<uint16_t> { static constexpr int bytes = 2; static const
 
 __device__ __forceinline__ int clamp_block(int b, int num_blocks) {
   return (unsigned)b < (unsigned)num_blocks ? b : num_blocks - 1;
+}
+
+// Broadcast lane H of each 16-lane row to the whole row (DPP row_newbcast).
+template <int H>
+__device__ __forceinline__ float row_bcast(float x) {
+  static_assert(H >= 0 && H < 16, "row lane");
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + H, 0xf, 0xf, true));
+}
+
+// A buffer resource for `bytes` bytes at `base`, built in SGPRs; loads through
+// it are bounds-checked against that range by the hardware.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Widen eight bf16 (one 16-byte chunk) to fp32.
+__device__ __forceinline__ void widen_bf16x8(uint4 w, float* f) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
 }  // namespace pa

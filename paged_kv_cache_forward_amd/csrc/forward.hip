@@ -38,7 +38,7 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
   fs->group = num_q_heads / c->num_kv_heads;
   if (fs->group != 1 && fs->group != 2 && fs->group != 4 && fs->group != 8)
     return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (built for 1, 2, 4, 8)", who, fs->group);
-  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, max_seq_len);
+  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
   fs->any_prefill = max_query_len > 1;
   fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
   return PA_OK;
@@ -86,7 +86,7 @@ extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens
   if (shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_workspace_size",
                &fs) != PA_OK)
     return 0;
-  return fs.plan.partial_bytes;
+  return fs.plan.workspace_bytes();
 }
 
 extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -104,8 +104,9 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   if (block_table_stride <= 0) return fail(PA_ERR_ARG, "pa_forward: block_table_stride %d", block_table_stride);
   if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "pa_forward: scale is not finite");
   if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "pa_forward: causal must be 0 or 1");
-  if (fs.plan.partial_bytes > 0 && (workspace == nullptr || workspace_bytes < fs.plan.partial_bytes))
-    return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", fs.plan.partial_bytes,
+  const size_t ws_need = fs.plan.workspace_bytes();
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
+    return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", ws_need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (check_mode()) {
@@ -135,15 +136,18 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
 
   float* p_acc = nullptr;
   float* p_ml = nullptr;
-  if (fs.plan.partial_bytes > 0) {
+  if (ws_need > 0) {
     p_acc = (float*)workspace;
-    p_ml = p_acc + (size_t)num_seqs * num_q_heads * fs.plan.max_parts * c->head_dim;
+    p_ml = (float*)((uint8_t*)workspace + fs.plan.acc_bytes);
   }
   if (fs.use_mfma_prefill) {
     st = launch_prefill(a, max_query_len, s);
     if (st != PA_OK) return st;
   }
-  st = launch_decode(a, c->dtype, fs.plan, p_acc, p_ml, fs.any_prefill && !fs.use_mfma_prefill, s);
+  if (fs.plan.mfma)
+    st = launch_decode_mfma(a, fs.plan, p_acc, p_ml, s);
+  else
+    st = launch_decode(a, c->dtype, fs.plan, p_acc, p_ml, fs.any_prefill && !fs.use_mfma_prefill, s);
   if (st != PA_OK) return st;
   if (fs.plan.max_parts > 1) st = launch_merge(a, c->dtype, fs.plan, p_acc, p_ml, s);
   return st;

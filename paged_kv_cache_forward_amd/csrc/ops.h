@@ -35,15 +35,23 @@ struct AttnArgs {
   int32_t causal;
 };
 
-// Split-KV plan for the decode path.
+// Split-KV plan for the decode path (sequences with one query token).
+//
+// Workspace layout when the plan needs one (offsets 256-byte aligned):
+//   [partial acc: fp32 [num_seqs][Hq][max_parts][head_dim]]
+//   [partial (max, sum): fp32 [num_seqs][Hq][max_parts][2]]
 struct DecodePlan {
+  bool mfma;             // decode_mfma (bf16, head_dim 128) instead of the VALU kernel
+  int32_t waves;         // waves per work-group of decode_mfma
   int32_t part_tokens;   // tokens per partition (multiple of 16)
   int32_t max_parts;     // partitions of the longest sequence; 1 = no split
-  size_t partial_bytes;  // workspace bytes for (m, l, acc) partials
+  size_t acc_bytes;      // partial accumulators
+  size_t ml_bytes;       // partial (max, sum) pairs
+  size_t workspace_bytes() const { return acc_bytes + ml_bytes; }
 };
 
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                            int32_t head_dim, int32_t max_seq_len);
+                            int32_t head_dim, int32_t dtype, int32_t max_seq_len);
 
 // Decode (VALU) kernel: sequences with one query token; with `rows_mode` it
 // also handles multi-token sequences one query row at a time (no split).
@@ -51,6 +59,11 @@ pa_status launch_decode(const AttnArgs& a, int32_t dtype, const DecodePlan& plan
                         float* partial_ml, bool rows_mode, hipStream_t s);
 pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
                        const float* partial_acc, const float* partial_ml, hipStream_t s);
+
+// Decode on the matrix cores (bf16, head_dim 128); partials go to launch_merge.
+bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
+pa_status launch_decode_mfma(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
+                             hipStream_t s);
 
 // Chunked-prefill (MFMA) kernel for bf16 sequences with more than one query token.
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);

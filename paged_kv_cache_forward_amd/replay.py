@@ -75,7 +75,7 @@ class DeviceRun:
         ws = pa.pa_forward_workspace_size(wl.num_seqs, wl.num_tokens, wl.num_q_heads,
                                           wl.max_seq_len, wl.max_query_len, self.k_cache)
         if ws:
-            self.workspace = torch.empty(ws, dtype=torch.uint8, device=self.dev)
+            self.workspace = pa.new_workspace(ws, self.dev)
         self.fill_context()
 
     def _pool(self, shape, fill):
