@@ -1,18 +1,27 @@
 """Benchmark: one engine step of paged attention on one MI355X.
 
-A step is the whole hot path on one synthetic batch whose host-side
-allocation has already produced its slot mapping: copy-on-write block copies
-(pa_copy_blocks, when the step has any), the cache write of the step's new
-tokens (pa_write_kv), then attention (pa_forward: split-KV decode + merge,
-and chunked prefill when the batch has chunks).  Inputs are resident in HBM
-before the timed region.
+A step is the whole device-side hot path on one synthetic batch whose host
+allocation has already produced its block tables and slot mapping: the
+copy-on-write block copies (pa_copy_blocks, when the step has any), the cache
+write of the step's new tokens (pa_write_kv), then attention (pa_forward:
+decode + split-KV merge, and chunked prefill when the batch has chunks).
+Inputs are resident in HBM before the timed region.  Steps rotate over enough
+identical copies of the K/V pools that no step finds its K/V in the 256 MB
+last-level cache, as successive layers of a model would not.
 
 Default workload: 64 decode sequences with contexts U[128, 4096], 32 query /
 8 KV heads, head_dim 128, bf16, 16-token blocks scattered over a 20000-block
-pool.  Prints one JSON line.
+pool.  Prints one JSON line on stdout; progress goes to stderr.
+
+Two timed regions of --steps steps each follow --warmup untimed steps: the
+first (no instrumentation) gives `value` and `ms_per_step`; the second runs
+with the library's per-kernel HIP-event tracing on and gives the kernel
+durations behind `roofline`.  `--copy-probe` instead runs only the known-size
+copy used to calibrate rocprofv3's HBM byte counters.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,24 +33,44 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode KV-read GB/s (% HBM peak) + tokens/s; prefill MFMA util"
-HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, datasheet
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, datasheet
+PROFILES = os.path.join(ROOT, "profiles")
+CONTEXT = {"tiny_decode": "{35,16,1,50}", "batched_decode": "U[128,4096]",
+           "long_context_decode": "U[32768,131072]",
+           "mixed_superbatch": "16 decode U[256,4096] + 4x512 chunks on 0/1024/4096/8192 cached",
+           "shared_prefix_cow": "2048 shared + U[0,512] private"}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kv_bytes(wl):
-    e = 4 if wl.dtype == "f32" else 2
-    return int(wl.seq_lens.astype(np.int64).sum()) * 2 * wl.num_kv_heads * wl.head_dim * e
+def elem_bytes(wl):
+    return 4 if wl.dtype == "f32" else 2
+
+
+def decode_rows(wl):
+    return [i for i in range(wl.num_seqs) if wl.query_lens[i] == 1]
+
+
+def kv_bytes(wl, seqs=None):
+    """K and V bytes of the visible context, read once per KV head (paging leaves bytes per token unchanged)."""
+    seqs = range(wl.num_seqs) if seqs is None else seqs
+    return sum(int(wl.seq_lens[i]) for i in seqs) * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl)
 
 
 def decode_algorithmic_bytes(wl):
-    """KV read once per KV head + q read + out written + block-table entries."""
-    e = 4 if wl.dtype == "f32" else 2
-    tables = int(sum((int(L) + 15) // 16 for L in wl.seq_lens)) * 4
-    return kv_bytes(wl) + 2 * wl.num_tokens * wl.num_q_heads * wl.head_dim * e + tables
+    """Decode rows: K/V + q read + out written + block-table entries."""
+    seqs = decode_rows(wl)
+    e = elem_bytes(wl)
+    table = sum((int(wl.seq_lens[i]) + 15) // 16 for i in seqs) * 4
+    return kv_bytes(wl, seqs) + 2 * len(seqs) * wl.num_q_heads * wl.head_dim * e + table
+
+
+def write_algorithmic_bytes(wl):
+    """pa_write_kv of the step's new tokens: K and V read and written, plus the slots."""
+    return wl.num_tokens * (2 * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl) + 8)
 
 
 def prefill_flops(wl):
@@ -53,35 +82,95 @@ def prefill_flops(wl):
     return int(f)
 
 
-def time_steps(run, steps, warmup, stream, with_writes=True):
-    """Returns (wall ms per step, event ms per forward call, list of per-forward ms)."""
-    import torch
-    for _ in range(warmup):
+def run_steps(run, steps, stream, with_writes=True):
+    """Enqueue `steps` steps, rotating pool copies; returns nothing (the caller brackets and synchronises)."""
+    for k in range(steps):
+        run.use(k)
         if with_writes:
             run.step_writes(stream)
         run.forward(stream)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+
+def timed_region(run, steps, stream, with_writes=True):
+    """Events + wall clock around exactly `steps` steps, synchronised on both sides."""
+    import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for k in range(steps):
-        if with_writes:
-            run.step_writes(stream)
-        ev[k][0].record(stream)
-        run.forward(stream)
-        ev[k][1].record(stream)
+    run_steps(run, steps, stream, with_writes)
     end.record(stream)
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
-    per_fwd = [a.elapsed_time(b) for a, b in ev]
-    return start.elapsed_time(end) / steps, wall, per_fwd
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return start.elapsed_time(end) / steps, wall_ms
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """The fp64 oracle on a bounded sample of the same workload (first sequences, in order)."""
+def traced_region(pa, run, steps, stream, with_writes=True):
+    """The same steps with per-kernel tracing on; returns {kernel: [ms, ...]}."""
+    import torch
+    torch.cuda.synchronize()
+    pa.pa_trace_read()                       # drop stale records
+    pa.pa_trace_enable(True)
+    try:
+        run_steps(run, steps, stream, with_writes)
+        torch.cuda.synchronize()
+    finally:
+        pa.pa_trace_enable(False)
+    per = {}
+    for name, ms in pa.pa_trace_read():
+        per.setdefault(name, []).append(ms)
+    return per
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_forward_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+KERNEL_SOURCES = {
+    "decode_mfma": ("decode_mfma.hip", "device.h"),
+    "decode_valu": ("decode.hip", "device.h"),
+    "prefill": ("prefill.hip", "device.h"),
+    "write_kv": ("cache_ops.hip", "device.h"),
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged since.
+
+    The summary (profiles/<kernel>-<workload>-hbm_counters.txt) holds key=value
+    lines: FETCH_SIZE and WRITE_SIZE in KiB per dispatch, the scale factors that
+    a plain copy of known size gave for each counter, and the sha256 of the
+    kernel's sources when the counters were taken.  Returns None when there is
+    no summary or the sources have changed.
+    """
+    path = os.path.join(PROFILES, f"{kernel}-{workload}-hbm_counters.txt")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest(*KERNEL_SOURCES[kernel]):
+        return None
+    fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
+    write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
+    return int(round(fetch + write))
+
+
+def cpu_baseline(wl, min_s=10.0, max_s=30.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload.
+
+    The sample is the workload's decode sequences in batch order, cycled until
+    at least `min_s` seconds of oracle time have passed (checked after each
+    sequence); its rate is reported in the bench's own unit (KV GB/s).
+    """
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle
     from helpers import OracleRun
@@ -90,21 +179,26 @@ def cpu_baseline(wl, budget_s=15.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = 1
-    log("cpu baseline: building the oracle's pools")
+    log("cpu baseline: building the oracle's pools (not timed)")
     ref = OracleRun(wl, compute_out=False)
     qsl = wl.query_start_loc
-    e = 4 if wl.dtype == "f32" else 2
-    done_bytes, done_seqs, done_tokens = 0, 0, 0
+    e = elem_bytes(wl)
+    seqs = decode_rows(wl) or list(range(wl.num_seqs))
+    done_bytes, done_seqs, done_tokens, passes = 0, 0, 0, 0
     t0 = time.perf_counter()
-    for i in range(wl.num_seqs):
-        r0, r1 = int(qsl[i]), int(qsl[i + 1])
-        oracle.ref_paged_attention(wl.q[r0:r1], ref.k_cache, ref.v_cache, [ref.tables[i]],
-                                   wl.seq_lens[i:i + 1], np.array([0, r1 - r0]), wl.cached_lens[i:i + 1],
-                                   wl.scale, wl.causal, wl.block_size, wl.dtype)
-        done_seqs += 1
-        done_tokens += r1 - r0
-        done_bytes += int(wl.seq_lens[i]) * 2 * wl.num_kv_heads * wl.head_dim * e
-        if time.perf_counter() - t0 > budget_s:
+    while True:
+        for i in seqs:
+            r0, r1 = int(qsl[i]), int(qsl[i + 1])
+            oracle.ref_paged_attention(wl.q[r0:r1], ref.k_cache, ref.v_cache, [ref.tables[i]],
+                                       wl.seq_lens[i:i + 1], np.array([0, r1 - r0]), wl.cached_lens[i:i + 1],
+                                       wl.scale, wl.causal, wl.block_size, wl.dtype)
+            done_seqs += 1
+            done_tokens += r1 - r0
+            done_bytes += int(wl.seq_lens[i]) * 2 * wl.num_kv_heads * wl.head_dim * e
+            if time.perf_counter() - t0 > max_s:
+                break
+        passes += 1
+        if time.perf_counter() - t0 >= min_s:
             break
     dt = time.perf_counter() - t0
     return {
@@ -112,10 +206,26 @@ def cpu_baseline(wl, budget_s=15.0):
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"pa_forward oracle (NumPy float64) on the first {done_seqs} of {wl.num_seqs} sequences "
-                  f"({done_tokens} query tokens, {done_bytes / 1e6:.1f} MB of K/V) in {dt:.1f} s",
+        "sample": f"ref_paged_attention (NumPy float64) over the {len(seqs)} decode sequences of {wl.name}, "
+                  f"{passes} pass(es): {done_seqs} sequence calls, {done_tokens} query tokens, "
+                  f"{done_bytes / 1e9:.2f} GB of K/V in {dt:.1f} s",
         "tokens_per_s": round(done_tokens / dt, 3),
     }
+
+
+def allocator_rate(pa, wl, reps=3):
+    """Host block allocator: replay the workload's allocation trace through the C ABI (ctypes included)."""
+    from paged_kv_cache_forward_amd.replay import _drive
+    best = None
+    for _ in range(reps):
+        alloc = pa.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+        t0 = time.perf_counter()
+        _drive(wl, alloc)
+        dt = time.perf_counter() - t0
+        best = dt if best is None else min(best, dt)
+    tokens = int(wl.seq_lens.sum() - sum(int(op[3]) for op in wl.trace if op[0] == "fork"))
+    return {"calls": len(wl.trace), "tokens_appended": tokens, "s": round(best, 6),
+            "calls_per_s": round(len(wl.trace) / best, 1), "tokens_per_s": round(tokens / best, 1)}
 
 
 def copy_probe(pa, torch, stream, steps):
@@ -141,12 +251,17 @@ def copy_probe(pa, torch, stream, steps):
                       "copy_gbs": round(2 * per_launch / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def mean(xs):
+    return float(np.mean(xs)) if xs else None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_decode")
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for >= 1 GB of K/V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
     ap.add_argument("--copy-probe", action="store_true",
@@ -154,8 +269,8 @@ def main():
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; see DESIGN.md for how it would shard).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: this build is the "
+              "single-GPU hot path (DESIGN.md describes how it would shard).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -174,27 +289,23 @@ def main():
 
     log(f"generating workload {args.workload}")
     wl = workloads.named(args.workload)
-    log("placing it on the GPU")
-    run = DeviceRun(wl, fill="zero")
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms_step, wall_ms, per_fwd = time_steps(run, args.steps, args.warmup, stream)
-    fwd_ms = float(np.mean(per_fwd))
-
     kvb = kv_bytes(wl)
+    copies = args.copies or max(2, -(-(1 << 30) // max(kvb, 1)))
+    log(f"placing it on the GPU ({copies} pool copies)")
+    run = DeviceRun(wl, fill="zero", copies=copies)
+    log(f"warm-up {args.warmup} steps, then two timed regions of {args.steps} steps")
+    run_steps(run, args.warmup, stream)
+    ms_step, wall_ms = timed_region(run, args.steps, stream)
+    per = traced_region(pa, run, args.steps, stream)
+    kern_ms = {k: round(mean(v), 5) for k, v in per.items()}
+    dominant = max(per, key=lambda k: sum(per[k]))
+    dec_kernel = "decode_mfma" if "decode_mfma" in per else "decode_valu"
+
     algo = decode_algorithmic_bytes(wl)
+    dom_ms = mean(per[dec_kernel])
+    achieved = algo / (dom_ms * 1e-3) / 1e9
+    traffic = measured_traffic(dec_kernel, wl.name)
     value = kvb / (ms_step * 1e-3) / 1e9
-    achieved = algo / (fwd_ms * 1e-3) / 1e9
-    wl_cfg = {
-        "workload": wl.name,
-        "seqs": wl.num_seqs,
-        "context": {"tiny_decode": "{35,16,1,50}", "batched_decode": "U[128,4096]",
-                    "long_context_decode": "U[32768,131072]", "mixed_superbatch": "16 decode U[256,4096] + 4x512 chunks",
-                    "shared_prefix_cow": "2048 shared + U[0,512]"}.get(wl.name, "custom"),
-        "sum_context_tokens": int(wl.seq_lens.sum()),
-        "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
-        "block_size": wl.block_size, "pool_blocks": wl.num_blocks,
-        "step": "pa_copy_blocks (if any) + pa_write_kv(new tokens) + pa_forward",
-    }
     plan_ws = pa.pa_forward_workspace_size(wl.num_seqs, wl.num_tokens, wl.num_q_heads, wl.max_seq_len,
                                            wl.max_query_len, run.k_cache)
     res = {
@@ -210,39 +321,58 @@ def main():
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic",
-        "config": wl_cfg,
+        "config": {
+            "workload": wl.name,
+            "seqs": wl.num_seqs,
+            "context": CONTEXT.get(wl.name, "custom"),
+            "sum_context_tokens": int(wl.seq_lens.sum()),
+            "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "pool_copies": copies,
+            "step": "pa_copy_blocks (if any) + pa_write_kv(new tokens) + pa_forward",
+        },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(wall_ms, 5),
-        "forward_ms": round(fwd_ms, 5),
+        "kernel_ms": kern_ms,
+        "dominant_kernel": dominant,
+        "workspace_bytes": int(plan_ws),
         "roofline": {
-            "kernel": "pa_forward (decode_kernel + merge_kernel)" if plan_ws else "pa_forward (decode_kernel)",
+            "kernel": dec_kernel,
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_launch": algo,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(algo),
+            "launch_ms": round(dom_ms, 5),
         },
     }
+    if "write_kv" in per:
+        wb = write_algorithmic_bytes(wl)
+        res["write_kv"] = {"tokens": wl.num_tokens, "ms": kern_ms["write_kv"],
+                           "GBs": round(wb / (kern_ms["write_kv"] * 1e-3) / 1e9, 2)}
+    res["allocator"] = allocator_rate(pa, wl)
     del run
     torch.cuda.empty_cache()
 
     if not args.no_prefill:
-        log("prefill leg: the four 512-token chunks of the mixed super-batch")
+        log("prefill leg: the four 512-token chunks of the mixed super-batch (forward only)")
         mix = workloads.mixed_superbatch()
         sel = [i for i in range(mix.num_seqs) if mix.query_lens[i] > 1]
         pre = workloads.independent("mixed_prefill_chunks", 4, Hq=32, Hkv=8, D=128, dtype="bf16",
                                     cached=mix.cached_lens[sel], new=mix.query_lens[sel], pool_factor=1.25)
-        prun = DeviceRun(pre, fill="zero")
-        _, _, pf = time_steps(prun, max(5, args.steps // 5), 3, stream, with_writes=False)
-        pms = float(np.mean(pf))
+        prun = DeviceRun(pre, fill="zero", copies=2)
+        psteps = max(5, args.steps // 5)
+        run_steps(prun, 3, stream, with_writes=False)
+        pper = traced_region(pa, prun, psteps, stream, with_writes=False)
+        pms = mean(pper["prefill"])
         fl = prefill_flops(pre)
         tf = fl / (pms * 1e-3) / 1e12
         res["prefill"] = {"workload": "4 chunks x 512 tokens on 0/1024/4096/8192 cached, 32/8 heads, D128, bf16",
-                          "ms": round(pms, 5), "tflops": round(tf, 2),
-                          "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl}
+                          "kernel": "prefill", "ms": round(pms, 5), "tflops": round(tf, 2),
+                          "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl,
+                          "kernel_ms": {k: round(mean(v), 5) for k, v in pper.items()}}
         del prun
         torch.cuda.empty_cache()
 

@@ -191,6 +191,29 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Tracing (instrumentation; not part of the method)                         */
+/* ------------------------------------------------------------------------ */
+
+/* One timed kernel launch: `kernel` names it (static storage); `ms` is the
+ * time between HIP events recorded just before and just after the launch on
+ * the caller's stream, or -1 if the events could not be read. */
+typedef struct {
+  const char* kernel;
+  float ms;
+} pa_trace_record;
+
+/* Turn per-kernel timing on (on != 0) or off for every later device call of
+ * this process.  While on, each kernel launch records two HIP events on the
+ * caller's stream (no synchronisation); at most 4096 records are kept, the
+ * oldest dropped first.  Always PA_OK. */
+pa_status pa_trace_enable(int32_t on);
+
+/* Waits for the recorded events, copies up to `cap` records (launch order)
+ * into host array `out`, sets *n to the number copied, and clears the list.
+ * Errors: PA_ERR_ARG (n NULL, cap < 0, out NULL with cap > 0), PA_ERR_HIP. */
+pa_status pa_trace_read(pa_trace_record* out, int32_t cap, int32_t* n);
+
+/* ------------------------------------------------------------------------ */
 /* Host block allocator (no GPU calls; one thread at a time per allocator)   */
 /* ------------------------------------------------------------------------ */
 

@@ -41,6 +41,10 @@ class CacheDesc(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class TraceRecord(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("ms", ctypes.c_float)]
+
+
 class AllocStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("blocks_total", "blocks_free", "blocks_used", "blocks_shared",
@@ -59,6 +63,8 @@ _SIGS = {
     "pa_forward_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_trace_enable": (_i32, [_i32]),
+    "pa_trace_read": (_i32, [ctypes.POINTER(TraceRecord), _i32, _pi32]),
     "pa_alloc_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_seq_create": (_i32, [_vp, _pi32]),
@@ -216,6 +222,21 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
                           _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
                           int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
                           ws_ptr, ws_bytes, _stream(stream)))
+
+
+# -- tracing ---------------------------------------------------------------------
+
+def pa_trace_enable(on=True):
+    """Per-kernel HIP-event timing of every later device call (see pa_trace_read)."""
+    _check(_load().pa_trace_enable(1 if on else 0))
+
+
+def pa_trace_read(cap=4096):
+    """Waits for the recorded events; returns [(kernel name, ms), ...] in launch order and clears them."""
+    buf = (TraceRecord * cap)()
+    n = ctypes.c_int32()
+    _check(_load().pa_trace_read(buf, cap, ctypes.byref(n)))
+    return [(buf[k].kernel.decode(), float(buf[k].ms)) for k in range(n.value)]
 
 
 # -- host allocator -------------------------------------------------------------

@@ -112,9 +112,11 @@ extern "C" pa_status pa_write_kv(const void* k, const void* v, void* k_cache, vo
   const int64_t total = (int64_t)num_tokens * chunks_per_token;
   const int64_t nblk = (total + 255) / 256;
   if (nblk > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: too many tokens in one call");
+  const int mark = trace_begin(s);
   hipLaunchKernelGGL(write_kv_kernel, dim3((unsigned)nblk, 2), dim3(256), 0, s,
                      (const uint8_t*)k, (const uint8_t*)v, (uint8_t*)k_cache, (uint8_t*)v_cache,
                      slot_mapping, total, chunks_per_token, chunks_per_row, num_slots);
+  trace_end(s, mark, "write_kv");
   return launch_status("pa_write_kv");
 }
 
@@ -145,7 +147,9 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
     }
   }
   const int chunks_per_block = c->num_kv_heads * kBlock * c->head_dim * elem_bytes(c->dtype) / 16;
+  const int mark = trace_begin(s);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, s, (uint8_t*)k_cache,
                      (uint8_t*)v_cache, pairs, chunks_per_block, c->num_blocks);
+  trace_end(s, mark, "copy_blocks");
   return launch_status("pa_copy_blocks");
 }

@@ -458,6 +458,9 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
 
 template <typename T, int D>
 static pa_status launch_decode_d(const DecodeKernelArgs& k, int G, dim3 grid, hipStream_t s) {
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: query heads per KV head %d", G);
+  const int mark = trace_begin(s);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_kernel<T, D, 1>), grid, dim3(64), 0, s, k); break;
     case 2: hipLaunchKernelGGL((decode_kernel<T, D, 2>), grid, dim3(64), 0, s, k); break;
@@ -465,6 +468,7 @@ static pa_status launch_decode_d(const DecodeKernelArgs& k, int G, dim3 grid, hi
     case 8: hipLaunchKernelGGL((decode_kernel<T, D, 8>), grid, dim3(64), 0, s, k); break;
     default: return fail(PA_ERR_UNSUPPORTED, "pa_forward: query heads per KV head %d", G);
   }
+  trace_end(s, mark, "decode_valu");
   return launch_status("pa_forward (decode)");
 }
 
@@ -482,7 +486,9 @@ pa_status launch_decode(const AttnArgs& a, int32_t dtype, const DecodePlan& plan
 
 pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
                        const float* partial_acc, const float* partial_ml, hipStream_t s) {
+  if (a.head_dim != 64 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: head_dim %d", a.head_dim);
   dim3 grid(a.num_seqs, a.num_q_heads);
+  const int mark = trace_begin(s);
   if (dtype == PA_BF16 && a.head_dim == 128)
     hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), grid, dim3(256), 0, s, a, plan.part_tokens,
                        plan.max_parts, partial_acc, partial_ml);
@@ -497,6 +503,7 @@ pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
                        plan.max_parts, partial_acc, partial_ml);
   else
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: head_dim %d", a.head_dim);
+  trace_end(s, mark, "merge");
   return launch_status("pa_forward (merge)");
 }
 

@@ -302,6 +302,9 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(MfmaDecodeArgs k) 
 
 template <int NW>
 pa_status launch_nw(const MfmaDecodeArgs& k, int G, dim3 grid, hipStream_t s) {
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: %d query heads per KV head", G);
+  const int mark = trace_begin(s);
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_mfma_kernel<1, NW>), grid, dim3(64 * NW), 0, s, k); break;
     case 2: hipLaunchKernelGGL((decode_mfma_kernel<2, NW>), grid, dim3(64 * NW), 0, s, k); break;
@@ -309,6 +312,7 @@ pa_status launch_nw(const MfmaDecodeArgs& k, int G, dim3 grid, hipStream_t s) {
     case 8: hipLaunchKernelGGL((decode_mfma_kernel<8, NW>), grid, dim3(64 * NW), 0, s, k); break;
     default: return fail(PA_ERR_UNSUPPORTED, "pa_forward: %d query heads per KV head", G);
   }
+  trace_end(s, mark, "decode_mfma");
   return launch_status("pa_forward (decode, matrix cores)");
 }
 

@@ -282,12 +282,16 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, hipStream_t s
   const int G = a.num_q_heads / a.num_kv_heads;
   const int TOK = kRowsPerWG / G;
   dim3 grid((max_query_len + TOK - 1) / TOK, a.num_kv_heads, a.num_seqs);
+  if (a.head_dim != 64 && a.head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill head_dim %d", a.head_dim);
+  const int mark = trace_begin(s);
   if (a.head_dim == 128)
     hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, a);
   else if (a.head_dim == 64)
     hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, a);
   else
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill head_dim %d", a.head_dim);
+  trace_end(s, mark, "prefill");
   return launch_status("pa_forward (prefill)");
 }
 

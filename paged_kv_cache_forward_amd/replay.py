@@ -40,7 +40,14 @@ def _drive(wl, alloc):
 
 
 class DeviceRun:
-    def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None):
+    """One workload's device state; ``copies`` > 1 keeps that many identical K/V pools.
+
+    Steps can rotate through the copies (``use``) so that consecutive steps
+    read different HBM and nothing is served from the 256 MB last-level cache
+    (the way successive layers of a model read different caches).
+    """
+
+    def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None, copies=1):
         import torch
         self.torch = torch
         self.wl = wl
@@ -77,6 +84,13 @@ class DeviceRun:
         if ws:
             self.workspace = pa.new_workspace(ws, self.dev)
         self.fill_context()
+        self.pools = [(self.k_cache, self.v_cache)]
+        for _ in range(1, copies):
+            self.pools.append((self.k_cache.clone(), self.v_cache.clone()))
+
+    def use(self, copy):
+        """Make pool copy ``copy`` the one later calls read and write."""
+        self.k_cache, self.v_cache = self.pools[copy % len(self.pools)]
 
     def _pool(self, shape, fill):
         torch = self.torch
