@@ -19,6 +19,7 @@ namespace pa {
 struct ForwardShape {
   int32_t group;
   DecodePlan plan;
+  PrefillPlan pplan;
   bool use_mfma_prefill;
   bool any_prefill;
 };
@@ -41,6 +42,8 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
   fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
   fs->any_prefill = max_query_len > 1;
   fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
+  fs->pplan = make_prefill_plan(num_tokens, num_q_heads, c->head_dim, max_seq_len, max_query_len,
+                                fs->use_mfma_prefill);
   return PA_OK;
 }
 
@@ -86,7 +89,7 @@ extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens
   if (shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_workspace_size",
                &fs) != PA_OK)
     return 0;
-  return fs.plan.workspace_bytes();
+  return fs.plan.workspace_bytes() + fs.pplan.workspace_bytes();
 }
 
 extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -104,7 +107,7 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   if (block_table_stride <= 0) return fail(PA_ERR_ARG, "pa_forward: block_table_stride %d", block_table_stride);
   if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "pa_forward: scale is not finite");
   if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "pa_forward: causal must be 0 or 1");
-  const size_t ws_need = fs.plan.workspace_bytes();
+  const size_t ws_need = fs.plan.workspace_bytes() + fs.pplan.workspace_bytes();
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
     return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", ws_need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -136,12 +139,17 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
 
   float* p_acc = nullptr;
   float* p_ml = nullptr;
+  float* pre_o = nullptr;
+  float* pre_ml = nullptr;
   if (ws_need > 0) {
-    p_acc = (float*)workspace;
-    p_ml = (float*)((uint8_t*)workspace + fs.plan.acc_bytes);
+    uint8_t* base = (uint8_t*)workspace;
+    p_acc = (float*)base;
+    p_ml = (float*)(base + fs.plan.acc_bytes);
+    pre_o = (float*)(base + fs.plan.workspace_bytes());
+    pre_ml = (float*)(base + fs.plan.workspace_bytes() + fs.pplan.o_bytes);
   }
   if (fs.use_mfma_prefill) {
-    st = launch_prefill(a, max_query_len, s);
+    st = launch_prefill(a, max_query_len, fs.pplan, pre_o, pre_ml, s);
     if (st != PA_OK) return st;
   }
   if (fs.plan.mfma)

@@ -70,8 +70,28 @@ bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 pa_status launch_decode_mfma(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
                              hipStream_t s);
 
-// Chunked-prefill (MFMA) kernel for bf16 sequences with more than one query token.
+// Split-KV plan for the chunked-prefill kernel: the key range of every
+// (sequence, query tile, KV head) work-group is cut into pieces of piece_keys
+// keys (a multiple of 64); work-groups whose range spans more than one piece
+// write fp32 partials per piece and the prefill merge kernel combines them.
+// Workspace (after the decode partials, 256-byte aligned):
+//   [partial O: fp32 [num_tokens][Hq][pieces][head_dim]]
+//   [partial (max, sum): fp32 [num_tokens][Hq][pieces][2]]
+struct PrefillPlan {
+  int32_t piece_keys;
+  int32_t pieces;      // pieces of the longest key range; 1 = no split
+  size_t o_bytes;
+  size_t ml_bytes;
+  size_t workspace_bytes() const { return o_bytes + ml_bytes; }
+};
+
+PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                              int32_t max_query_len, bool mfma);
+
+// Chunked-prefill (MFMA) kernel for bf16 sequences with more than one query
+// token, followed by its merge when the plan splits key ranges.
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
-pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, hipStream_t s);
+pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
+                         hipStream_t s);
 
 }  // namespace pa

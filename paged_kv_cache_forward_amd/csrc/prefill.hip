@@ -11,67 +11,120 @@
 // table like any other cached token.  Prefill is compute-bound (same page as
 // above, bullet on disaggregation), so both contractions run on MFMA.
 //
-// Tiling: a workgroup (4 waves) owns 128 query rows of one KV head g, a row
-// being a (token, query head) pair: row r -> token r / G, head g*G + r % G,
-// so the G heads sharing g share every K/V tile.  Each wave owns 32 rows
-// (two 16-row MFMA tiles).  Keys stream in tiles of 64 (four 16-token cache
-// blocks) through double-buffered LDS.
+// Work-group: 4 waves owning 128 query rows of one KV head g, a row being a
+// (token, query head) pair: row r -> token r / G, head g*G + r % G, so the G
+// heads sharing g share every K/V tile; each wave owns 32 rows (two 16-row
+// MFMA tiles).  Launch order: KV head fastest (every work-group of one KV head
+// runs on one XCD and shares that XCD's L2 for the K/V it re-reads), then the
+// query tile, latest tiles (most keys) first, then the sequence.
 //
-// Contractions use v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16 fp32):
-//   S^T = K Q^T   A = K tile rows (keys) from LDS, B = Q^T from registers;
-//                 the C fragment leaves lane l with four consecutive keys of
-//                 one query row (row = l % 16);
-//   O^T += V^T P^T  B = P^T taken straight from two S^T fragments (keys
-//                 4q..4q+3 and 16+4q..16+4q+3 of a 32-key step, q = l / 16),
-//                 A = V^T read from a transposed LDS copy of the V tile with
-//                 the same key order, so no shuffles are needed; the C
-//                 fragment leaves lane l with four head-dim columns of its own
-//                 query row, so the softmax rescale is per lane.
-// Softmax statistics are per query row, reduced across the four lanes sharing
-// it; scores are in base-2 units.  P is rounded to bf16 for the second MFMA;
-// accumulation stays fp32.  Keys past the visible end are masked by select
-// and V rows past it are zeroed in LDS, so stale or NaN slots never reach an
-// accumulator.
+// K/V tiles of 64 keys (four 16-token cache blocks) are loaded one tile
+// ahead into registers and stored to a double-buffered LDS stage.  Each load
+// goes through a buffer descriptor built in SGPRs for one cache block whose
+// range ends at the sequence's last token, so slots past it (stale, possibly
+// NaN) read as zero and never reach an MFMA.  The block table of the
+// work-group's key range is staged in LDS, a window at a time.
+//
+// Contractions, v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16 fp32):
+//   S^T = K Q^T     A = K rows from LDS (lane: key row l % 16, dims 8 (l / 16)
+//                   of each 32-dim step), B = Q^T held in registers; the C
+//                   fragment gives lane l keys 4q .. 4q+3 (q = l / 16) of
+//                   query row l % 16.
+//   O^T += V^T P^T  B = P^T straight from two S^T fragments (keys 4q..4q+3 and
+//                   16+4q..16+4q+3 of a 32-key step); A = V^T read from the
+//                   row-major V tile with ds_read_b64_tr_b16, which hands lane
+//                   l four consecutive keys of head-dim column l % 16 when the
+//                   16 lanes of its group point at the four key rows (four
+//                   lanes per row, four dims each).  No transposing copy.
+// Softmax state is per query row, spread over the four lanes holding its
+// keys; scores are in base-2 units; the running max only moves when a score
+// beats it by 2^8 (kRescaleSlack), so accumulators are rarely rescaled.  P is
+// rounded to bf16 (nearest even) for the second MFMA; accumulation is fp32.
+// Keys past a row's visible end are masked by select on the tiles that need
+// it; tiles past every row of a wave are skipped.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
 #include "device.h"
 #include "ops.h"
 #include "status.h"
 
 namespace pa {
+namespace {
 
-constexpr int kRowsPerWG = 128;
-constexpr int kKeysPerTile = 64;
+constexpr int kRowsPerWG = 128;   // (token, query head) rows per work-group: 4 waves x 32
+constexpr int kKeys = 64;         // keys per tile: four 16-token cache blocks
+constexpr int kBtCache = 1024;    // block-table entries staged in LDS (16384 tokens)
 
 template <int D>
 struct PCfg {
+  static constexpr int ROW = D * 2;                       // bytes of one key row (one KV head)
+  static constexpr int TILE = kBlock * ROW;               // bytes of one (block, KV head) tile
   static constexpr int KS = D / 32;                       // MFMA k-steps over the head dim
   static constexpr int DT = D / 16;                       // 16-column output tiles
-  static constexpr int CPK = D / 8;                       // 16-byte chunks per key row
-  static constexpr int KC = kKeysPerTile * CPK / 256;     // K chunks per thread per tile
-  static constexpr int VK = D / 32;                       // V keys per thread per tile
-  static constexpr int K_STRIDE = D * 2 + 16;             // LDS bytes per key row (padded)
-  static constexpr int V_STRIDE = kKeysPerTile * 2 + 8;   // LDS bytes per head-dim row of V^T
-  static constexpr int K_BYTES = kKeysPerTile * K_STRIDE;
-  static constexpr int V_BYTES = D * V_STRIDE;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
-  static_assert(KC * 256 == kKeysPerTile * CPK, "K tile split");
-  static_assert((256 / CPK) * VK == kKeysPerTile && kBlock % VK == 0, "V tile split");
+  static constexpr int KSTR = ROW + 16;                   // LDS row stride of K (bank spread)
+  static constexpr int VSTR = ROW + 32;                   // LDS row stride of V (bank spread)
+  static constexpr int KBUF = kKeys * KSTR;
+  static constexpr int BUF = KBUF + kKeys * VSTR;         // one stage: K tile, then V tile
+  static constexpr int LPT = kKeys * ROW / (16 * 256);    // 16-byte loads per thread per tensor per tile
+  static_assert(LPT * 16 * 256 == kKeys * ROW, "tile split");
+  static_assert(TILE % 1024 == 0, "a wave's 1 KiB of a load stays inside one block tile");
 };
 
-// Element x (0..7) of a chunk of eight bf16, as the low 16 bits of a dword.
-__device__ __forceinline__ uint32_t bf16_at(const uint4& w, int x) {
-  const uint32_t word = (x >> 1) == 0 ? w.x : (x >> 1) == 1 ? w.y : (x >> 1) == 2 ? w.z : w.w;
-  return (x & 1) ? (word >> 16) : (word & 0xffffu);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;   // LDS byte pointer (no generic-pointer checks)
+
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+
+__device__ __forceinline__ u32x4_t buf_ld16v(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
+__device__ __forceinline__ s16x4_t lds_read_tr(const lds_u8* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+}
+
+struct PrefillArgs {
+  AttnArgs a;
+  int32_t qtiles;       // query tiles of the longest chunk
+  int32_t piece_keys;   // keys per split piece (multiple of kKeys)
+  int32_t pieces;       // pieces of the longest key range
+  float* p_o;           // [num_tokens][Hq][pieces][D] partial outputs (unnormalised)
+  float* p_ml;          // [num_tokens][Hq][pieces][2] partial (max in base-2 units, sum)
+};
+
+// Which (KV head, query tile, sequence, piece) a work-group handles.  KV head
+// fastest (every work-group of one KV head on one XCD); pieces slowest and in
+// descending order, because only long key ranges have high pieces: the
+// longest work is dispatched first and the short pieces fill the tail.
+struct PrefillItem {
+  int g, p, qt, i;
+};
+__device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces, int qtiles, int num_seqs) {
+  PrefillItem it;
+  it.g = wg % Hkv;
+  int r = wg / Hkv;
+  it.qt = qtiles - 1 - r % qtiles;
+  r /= qtiles;
+  it.i = r % num_seqs;
+  it.p = pieces - 1 - r / num_seqs;
+  return it;
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * C::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_stage[2 * C::BUF];
+  __shared__ int s_bt[kBtCache];
+  lds_u8* const lds = (lds_u8*)lds_stage;
 
-  const int G = a.num_q_heads / a.num_kv_heads;
+  const AttnArgs& a = pk.a;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
   const int TOK = kRowsPerWG / G;
-  const int i = blockIdx.z, g = blockIdx.y;
-  const int qt = gridDim.x - 1 - blockIdx.x;   // later query tiles see more keys: start them first
+  const PrefillItem it = prefill_item(blockIdx.x, Hkv, pk.pieces, pk.qtiles, a.num_seqs);
+  const int g = it.g, qt = it.qt, i = it.i;
   const int q0 = a.qsl[i];
   const int n = a.qsl[i + 1] - q0;
   if (n <= 1 || q0 < 0 || q0 + n > a.num_tokens) return;
@@ -82,11 +135,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
   const int tok_last = min(tok0 + TOK, n) - 1;
   const int kv_end = a.causal ? min(L, c + tok_last + 1) : L;
   if (kv_end <= 0) return;
-  const int ntiles = (kv_end + kKeysPerTile - 1) / kKeysPerTile;
+  // This work-group's piece of the key range; the last piece takes whatever
+  // remains, so every key is covered whatever the lengths.
+  const int k_lo = it.p * pk.piece_keys;
+  if (k_lo >= kv_end) return;
+  const int k_hi = it.p == pk.pieces - 1 ? kv_end : min(k_lo + pk.piece_keys, kv_end);
+  const bool split = kv_end > pk.piece_keys && pk.pieces > 1;   // partials instead of the output
+  const int kt0 = k_lo / kKeys;
+  const int kt_end = (k_hi + kKeys - 1) / kKeys;
+  const int ntiles = kt_end - kt0;
+  const int nblk = (k_hi + kBlock - 1) / kBlock;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
-  const size_t row_bytes = (size_t)D * 2;
+
+  // The block table of the work-group's key range passes through LDS in
+  // windows of kBtCache entries; a window is refilled (behind a barrier) when
+  // the loads reach it, so no global load sits inside the tile loop.
+  const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
+  auto fill_window = [&](int win) {
+    const int b0 = win * kBtCache;
+    for (int b = tid; b < min(nblk - b0, kBtCache); b += 256) s_bt[b] = clamp_block(bt_row[b0 + b], a.num_blocks);
+  };
+  int cur_win = kt0 * (kKeys / kBlock) / kBtCache;
+  fill_window(cur_win);
 
   // Query fragments (B operand of S^T = K Q^T): lane holds 8 head-dim values of its row.
   bf16x8_t qf[2][C::KS];
@@ -97,10 +170,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     row_tok[rt] = tok0 + r / G;
     row_head[rt] = g * G + r % G;
     const bool ok = row_tok[rt] < n;
-    const uint8_t* qp = (const uint8_t*)a.q + ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * row_bytes;
+    const uint8_t* qp =
+        (const uint8_t*)a.q + ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * C::ROW;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      uint4 v = ok ? ld16(qp + ks * 64 + lq * 16) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v = ok ? ld16(qp + ks * 64 + lq * 16) : make_uint4(0u, 0u, 0u, 0u);
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -115,145 +189,146 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
 
   const int wave_tok_first = tok0 + (w * 32) / G;
   const int wave_tok_last = min(tok0 + (w * 32 + 31) / G, n - 1);
-  const int vis_min = a.causal ? min(L, c + wave_tok_first + 1) : L;  // keys every row of the wave sees
+  const int vis_min = a.causal ? min(L, c + wave_tok_first + 1) : L;   // keys every row of the wave sees
+  const int lim0 = a.causal ? min(L, c + row_tok[0] + 1) : L;
+  const int lim1 = a.causal ? min(L, c + row_tok[1] + 1) : L;
 
-  const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
-  const size_t tile_bytes = (size_t)kBlock * row_bytes;            // one (block, head) tile
-  const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
-  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * tile_bytes;
-  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * tile_bytes;
+  const size_t block_stride = (size_t)Hkv * C::TILE;
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * C::TILE;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * C::TILE;
 
-  // Staging registers: K chunk (key kc_key, 16B column kc_col) and V keys vk0..vk0+VK-1 at column v_col.
-  uint4 kst[C::KC];
-  uint4 vst[C::VK];
-  const int v_col = tid % C::CPK;
-  const int v_kg = tid / C::CPK;
+  __syncthreads();   // first block-table window ready
 
-  auto load_tile = [&](int kt) {
-    const int key0 = kt * kKeysPerTile;
-#pragma unroll
-    for (int u = 0; u < C::KC; ++u) {
-      const int ch = tid + 256 * u;
-      const int key = ch / C::CPK, col = ch % C::CPK;
-      const int kabs = key0 + key;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (kabs < kv_end) {
-        const int bid = clamp_block(bt_row[kabs / kBlock], a.num_blocks);
-        v = ld16(kc + bid * block_stride + (kabs % kBlock) * row_bytes + col * 16);
-      }
-      kst[u] = v;
+  auto block_id = [&](int b) -> int {   // b < nblk, inside the current window, wave-uniform
+    return __builtin_amdgcn_readfirstlane(s_bt[b - cur_win * kBtCache]);
+  };
+
+  // This thread's u-th 16-byte load of a 64-key tile laid out row-major: a
+  // wave's 1 KiB never straddles two cache blocks.
+  // Loads are issued unconditionally (a tile index past the end reloads the
+  // last tile) so the wait before each LDS store counts only older loads.
+  auto load_regs = [&](int kt_req, u32x4_t (&ks)[C::LPT], u32x4_t (&vs)[C::LPT]) {
+    const int kt = min(kt_req, kt_end - 1);
+    const int win = kt * (kKeys / kBlock) / kBtCache;   // a tile never straddles two windows
+    if (win != cur_win) {
+      cur_win = win;
+      fill_window(win);
+      __syncthreads();
     }
-    const int vkey0 = key0 + v_kg * C::VK;   // VK consecutive keys, all inside one cache block
-    const int bid = vkey0 < kv_end ? clamp_block(bt_row[vkey0 / kBlock], a.num_blocks) : 0;
 #pragma unroll
-    for (int e = 0; e < C::VK; ++e) {
-      const int kabs = vkey0 + e;
-      vst[e] = kabs < kv_end ? ld16(vc + bid * block_stride + (kabs % kBlock) * row_bytes + v_col * 16)
-                             : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < C::LPT; ++u) {
+      const int wave_off = u * 4096 + w * 1024;          // uniform
+      const int blk = kt * (kKeys / kBlock) + wave_off / C::TILE;
+      const int rows = __builtin_amdgcn_readfirstlane(blk < nblk ? min(max(L - blk * kBlock, 0), kBlock) : 0);
+      const int bid = rows > 0 ? block_id(blk) : 0;
+      const size_t off = (size_t)bid * block_stride;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, rows * C::ROW);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, rows * C::ROW);
+      const int in_tile = wave_off % C::TILE + lane * 16;
+      ks[u] = buf_ld16v(rk, in_tile);
+      vs[u] = buf_ld16v(rv, in_tile);
+    }
+  };
+  auto store_lds = [&](int buf, const u32x4_t (&ks)[C::LPT], const u32x4_t (&vs)[C::LPT]) {
+    lds_u8* kl = lds + buf * C::BUF;
+    lds_u8* vl = kl + C::KBUF;
+#pragma unroll
+    for (int u = 0; u < C::LPT; ++u) {
+      const int off = u * 4096 + w * 1024 + lane * 16;
+      const int key = off / C::ROW, colb = off % C::ROW;
+      *reinterpret_cast<lds_u32x4*>(kl + key * C::KSTR + colb) = ks[u];
+      *reinterpret_cast<lds_u32x4*>(vl + key * C::VSTR + colb) = vs[u];
     }
   };
 
-  auto store_tile = [&](int buf) {
-    uint8_t* kl = lds + buf * C::BUF_BYTES;
-    uint8_t* vl = kl + C::K_BYTES;
+  auto compute = [&](int kt, int buf) {
+    const int key0 = kt * kKeys;
+    if (a.causal && key0 > c + wave_tok_last) return;   // past every row of this wave
+    const lds_u8* kl = lds + buf * C::BUF;
+    const lds_u8* vl = kl + C::KBUF;
+    f32x4_t s[2][4];
 #pragma unroll
-    for (int u = 0; u < C::KC; ++u) {
-      const int ch = tid + 256 * u;
-      const int key = ch / C::CPK, col = ch % C::CPK;
-      *reinterpret_cast<uint4*>(kl + key * C::K_STRIDE + col * 16) = kst[u];
-    }
-    // V^T: head-dim row d = v_col*8 + x gets this thread's VK keys, consecutive.
+    for (int kt16 = 0; kt16 < 4; ++kt16) {
+      s[0][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      s[1][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      uint8_t* dst = vl + (v_col * 8 + x) * C::V_STRIDE + v_kg * C::VK * 2;
-      if constexpr (C::VK == 4) {
-        const uint32_t lo = bf16_at(vst[0], x) | (bf16_at(vst[1], x) << 16);
-        const uint32_t hi = bf16_at(vst[2], x) | (bf16_at(vst[3], x) << 16);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = bf16_at(vst[0], x) | (bf16_at(vst[1], x) << 16);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8_t kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
+            kl + (kt16 * 16 + lr) * C::KSTR + ks * 64 + lq * 16);
+        s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
+        s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
       }
     }
-  };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
-    if (more) load_tile(kt + 1);
-    const int key0 = kt * kKeysPerTile;
-    const bool skip = a.causal && key0 > c + wave_tok_last;   // every row of this wave is past it
-    if (!skip) {
-      const uint8_t* kl = lds + buf * C::BUF_BYTES;
-      const uint8_t* vl = kl + C::K_BYTES;
-      f32x4_t s[2][4];
+    const bool full = key0 + kKeys <= vis_min;
+    bf16x8_t pb[2][2];
 #pragma unroll
-      for (int kt16 = 0; kt16 < 4; ++kt16) {
-        s[0][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        s[1][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt) {
+      const int lim = rt == 0 ? lim0 : lim1;
+      float mx = -INFINITY;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kl + (kt16 * 16 + lr) * C::K_STRIDE + ks * 64 + lq * 16);
-          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
-          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
+      for (int kt16 = 0; kt16 < 4; ++kt16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = s[rt][kt16][e] * a.scale_log2;
+          if (!full) v = (key0 + kt16 * 16 + lq * 4 + e) < lim ? v : -INFINITY;
+          s[rt][kt16][e] = v;
+          mx = fmaxf(mx, v);
         }
-      }
-      const bool full = key0 + kKeysPerTile <= vis_min;
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int lim = a.causal ? min(L, c + row_tok[rt] + 1) : L;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt16 = 0; kt16 < 4; ++kt16)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float v = s[rt][kt16][e] * a.scale_log2;
-            if (!full) v = (key0 + kt16 * 16 + lq * 4 + e) < lim ? v : -INFINITY;
-            s[rt][kt16][e] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(m[rt], mx);
+      if (__any(mx > m[rt] + kRescaleSlack)) {   // rare after a row's first tile
+        float rm = fmaxf(mx, __shfl_xor(mx, 16));
+        rm = fmaxf(rm, __shfl_xor(rm, 32));
+        const float mn = fmaxf(m[rt], rm);
         const float alpha = fast_exp2(m[rt] - mn);
         m[rt] = mn;
-        float ls = 0.0f;
-#pragma unroll
-        for (int kt16 = 0; kt16 < 4; ++kt16)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = fast_exp2(s[rt][kt16][e] - mn);
-            s[rt][kt16][e] = p;
-            ls += p;
-          }
-        l[rt] = fmaf(l[rt], alpha, ls);
+        l[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) o[rt][dt] *= alpha;
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pb[rt][ks2][e] = static_cast<__bf16>(s[rt][2 * ks2][e]);
-            pb[rt][ks2][4 + e] = static_cast<__bf16>(s[rt][2 * ks2 + 1][e]);
-          }
       }
+      float part[4];
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+      for (int kt16 = 0; kt16 < 4; ++kt16) {
 #pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const uint8_t* vp = vl + (dt * 16 + lr) * C::V_STRIDE + (ks2 * 32 + lq * 4) * 2;
-          const uint2 v0 = *reinterpret_cast<const uint2*>(vp);
-          const uint2 v1 = *reinterpret_cast<const uint2*>(vp + 32);
-          const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
-          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
-          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) s[rt][kt16][e] = fast_exp2(s[rt][kt16][e] - m[rt]);
+        part[kt16] = (s[rt][kt16][0] + s[rt][kt16][1]) + (s[rt][kt16][2] + s[rt][kt16][3]);
+      }
+      l[rt] += (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[rt][ks2][e] = static_cast<__bf16>(s[rt][2 * ks2][e]);
+          pb[rt][ks2][4 + e] = static_cast<__bf16>(s[rt][2 * ks2 + 1][e]);
         }
     }
-    if (more) store_tile(buf ^ 1);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const lds_u8* vp = vl + (ks2 * 32 + 4 * lq + (lr >> 2)) * C::VSTR + (dt * 16 + 4 * (lr & 3)) * 2;
+        const s16x4_t v0 = lds_read_tr(vp);
+        const s16x4_t v1 = lds_read_tr(vp + 16 * C::VSTR);
+        const bf16x8_t vf = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
+        o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
+      }
+  };
+
+  // Pipeline: tile kt+1 is loaded into registers while tile kt is computed
+  // from LDS, then stored to the other LDS stage.
+  u32x4_t kr[C::LPT], vr[C::LPT];
+  load_regs(kt0, kr, vr);
+  store_lds(0, kr, vr);
+  __syncthreads();
+  for (int kt = kt0; kt < kt_end; kt += 2) {
+    load_regs(kt + 1, kr, vr);
+    compute(kt, 0);
+    store_lds(1, kr, vr);
+    __syncthreads();
+    if (kt + 1 >= kt_end) break;
+    load_regs(kt + 2, kr, vr);
+    compute(kt + 1, 1);
+    store_lds(0, kr, vr);
     __syncthreads();
   }
 
@@ -263,36 +338,147 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnArgs a) {
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     if (row_tok[rt] >= n) continue;
+    if (split) {
+      // Piece it.p of this row: unnormalised O^T columns, max (base 2) and sum.
+      // A piece past a row's causal limit leaves (kNegBig, 0, 0), weight 0 in the merge.
+      const size_t item = ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * pk.pieces + it.p;
+      float* po = pk.p_o + item * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+        *reinterpret_cast<float4*>(po + dt * 16 + lq * 4) =
+            make_float4(o[rt][dt][0], o[rt][dt][1], o[rt][dt][2], o[rt][dt][3]);
+      if (lq == 0) *reinterpret_cast<float2*>(pk.p_ml + item * 2) = make_float2(m[rt], lt);
+      continue;
+    }
     const float inv = 1.0f / lt;
-    uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * row_bytes;
+    uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * C::ROW;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const f32x4_t v = o[rt][dt] * inv;
-      *reinterpret_cast<uint2*>(op + (dt * 16 + lq * 4) * 2) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      *reinterpret_cast<uint2*>(op + (dt * 16 + lq * 4) * 2) =
+          make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     }
   }
 }
 
-bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 &&
-         kRowsPerWG % group == 0;
+// Prefill split-KV merge: one work-group of 256 threads per (KV head, query
+// tile, sequence) whose key range was split; two threads per (token, head)
+// row, each owning half of the head dim.  Pieces are combined in ascending
+// order with the log-sum-exp rule, so the result is deterministic.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs pk) {
+  constexpr int HALF = D / 2;
+  const AttnArgs& a = pk.a;
+  const int Hkv = a.num_kv_heads;
+  const int G = a.num_q_heads / Hkv;
+  const int TOK = kRowsPerWG / G;
+  const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.qtiles, a.num_seqs);
+  const int q0 = a.qsl[it.i];
+  const int n = a.qsl[it.i + 1] - q0;
+  if (n <= 1 || q0 < 0 || q0 + n > a.num_tokens) return;
+  const int tok0 = it.qt * TOK;
+  if (tok0 >= n) return;
+  const int L = min(a.seq_lens[it.i], a.bt_stride * kBlock);
+  const int c = a.cached_lens[it.i];
+  const int tok_last = min(tok0 + TOK, n) - 1;
+  const int kv_end = a.causal ? min(L, c + tok_last + 1) : L;
+  if (kv_end <= pk.piece_keys || pk.pieces <= 1) return;   // written by the prefill kernel itself
+  const int np = min((kv_end + pk.piece_keys - 1) / pk.piece_keys, pk.pieces);
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int tok = tok0 + r / G, head = it.g * G + r % G;
+  if (tok >= n) return;
+  const size_t item0 = ((size_t)(q0 + tok) * a.num_q_heads + head) * pk.pieces;
+  const float2* ml = reinterpret_cast<const float2*>(pk.p_ml) + item0;
+  float M = ml[0].x;
+  for (int pp = 1; pp < np; ++pp) M = fmaxf(M, ml[pp].x);
+  float den = 0.0f;
+  float acc[HALF];
+#pragma unroll
+  for (int e = 0; e < HALF; ++e) acc[e] = 0.0f;
+  for (int pp = 0; pp < np; ++pp) {
+    const float2 v = ml[pp];
+    const float w = fast_exp2(v.x - M);
+    den = fmaf(w, v.y, den);
+    const float4* src = reinterpret_cast<const float4*>(pk.p_o + (item0 + pp) * D + half * HALF);
+#pragma unroll
+    for (int q = 0; q < HALF / 4; ++q) {
+      const float4 x = src[q];
+      acc[4 * q] = fmaf(w, x.x, acc[4 * q]);
+      acc[4 * q + 1] = fmaf(w, x.y, acc[4 * q + 1]);
+      acc[4 * q + 2] = fmaf(w, x.z, acc[4 * q + 2]);
+      acc[4 * q + 3] = fmaf(w, x.w, acc[4 * q + 3]);
+    }
+  }
+  const float inv = 1.0f / den;
+  uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + tok) * a.num_q_heads + head) * (D * 2) + half * HALF * 2;
+#pragma unroll
+  for (int q = 0; q < HALF / 8; ++q)
+    *reinterpret_cast<uint4*>(op + q * 16) = make_uint4(
+        pack_bf16x2(acc[8 * q] * inv, acc[8 * q + 1] * inv), pack_bf16x2(acc[8 * q + 2] * inv, acc[8 * q + 3] * inv),
+        pack_bf16x2(acc[8 * q + 4] * inv, acc[8 * q + 5] * inv), pack_bf16x2(acc[8 * q + 6] * inv, acc[8 * q + 7] * inv));
 }
 
-pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, hipStream_t s) {
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 && kRowsPerWG % group == 0;
+}
+
+PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
+                              int32_t max_query_len, bool mfma) {
+  PrefillPlan pp{};
+  pp.piece_keys = 1 << 30;
+  pp.pieces = 1;
+  if (!mfma || max_query_len <= 1 || max_seq_len <= 0) return pp;
+  // A work-group's key range is cut into at most four pieces of at least
+  // 1024 keys, so the longest chunk is spread over more CUs and every CU keeps
+  // two work-groups busy; PA_PREFILL_SPLIT=off|<keys> overrides.
+  int64_t keys = std::max<int64_t>(1024, ((int64_t)(max_seq_len + 3) / 4 + kKeys - 1) / kKeys * kKeys);
+  if (const char* env = std::getenv("PA_PREFILL_SPLIT")) {
+    if (std::strcmp(env, "off") == 0) keys = (int64_t)1 << 30;
+    else if (std::atoi(env) >= kKeys) keys = (std::atoi(env) + kKeys - 1) / kKeys * kKeys;
+  }
+  pp.piece_keys = (int32_t)std::min<int64_t>(keys, (int64_t)1 << 30);
+  pp.pieces = (int32_t)std::max<int64_t>(1, ((int64_t)max_seq_len + pp.piece_keys - 1) / pp.piece_keys);
+  if (pp.pieces > 1) {
+    const size_t items = (size_t)num_tokens * num_q_heads * pp.pieces;
+    pp.o_bytes = round256(items * head_dim * sizeof(float));
+    pp.ml_bytes = round256(items * 2 * sizeof(float));
+  }
+  return pp;
+}
+
+pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
+                         hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int TOK = kRowsPerWG / G;
-  dim3 grid((max_query_len + TOK - 1) / TOK, a.num_kv_heads, a.num_seqs);
+  const int qtiles = (max_query_len + TOK - 1) / TOK;
+  const int64_t tiles = (int64_t)qtiles * a.num_kv_heads * a.num_seqs;
+  const int64_t wgs = tiles * pp.pieces;
   if (a.head_dim != 64 && a.head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill head_dim %d", a.head_dim);
-  const int mark = trace_begin(s);
+  if (wgs > 0x7fffffff / 256)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill grid of %lld work-groups", (long long)wgs);
+  if (pp.pieces > 1 && (p_o == nullptr || p_ml == nullptr))
+    return fail(PA_ERR_ARG, "pa_forward: prefill split needs workspace");
+  PrefillArgs k{a, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
+  int mark = trace_begin(s);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, grid, dim3(256), 0, s, a);
-  else if (a.head_dim == 64)
-    hipLaunchKernelGGL(prefill_kernel<64>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)wgs), dim3(256), 0, s, k);
   else
-    return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill head_dim %d", a.head_dim);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)wgs), dim3(256), 0, s, k);
   trace_end(s, mark, "prefill");
-  return launch_status("pa_forward (prefill)");
+  pa_status st = launch_status("pa_forward (prefill)");
+  if (st != PA_OK || pp.pieces <= 1) return st;
+  mark = trace_begin(s);
+  if (a.head_dim == 128)
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, s, k);
+  else
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, s, k);
+  trace_end(s, mark, "prefill_merge");
+  return launch_status("pa_forward (prefill merge)");
 }
 
 }  // namespace pa

@@ -126,6 +126,14 @@ def test_split_sizes(split, monkeypatch):
     check_parity(workloads.mini("decode_bf16"), pools=False)
 
 
+@pytest.mark.parametrize("split", ["off", "64", "192", "1024"])
+def test_prefill_split_sizes(split, monkeypatch):
+    """Every prefill key-range split meets the tolerance (pieces merged by the prefill merge kernel)."""
+    monkeypatch.setenv("PA_PREFILL_SPLIT", split)
+    for name in ("mixed_bf16", "mixed_gqa8", "noncausal_bf16", "mixed_mha_d64"):
+        check_parity(workloads.mini(name), pools=False)
+
+
 def test_degenerate_batches():
     ensure_library()
     # sequences with no query rows between others, a length-1 context, and a 1-token chunk
