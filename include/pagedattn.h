@@ -129,7 +129,8 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
 /*
  * pa_forward_workspace_size — bytes of device scratch pa_forward needs for the
  * same host arguments (0 when the call needs none).  Depends only on its
- * arguments and the PA_SPLIT environment variable (see pa_forward).
+ * arguments and the tuning variables PA_DECODE, PA_DECODE_TOTAL_WAVES,
+ * PA_SPLIT and PA_PREFILL_SPLIT (see pa_forward).
  */
 size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                  int32_t max_seq_len, int32_t max_query_len,
@@ -152,9 +153,10 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   out = sum_t softmax_t(scale * <q, K_t>) V_t
  * where K_t / V_t is token t of sequence i, in block block_tables[i][t / 16]
  * at row t % 16.  Accumulation is fp32; out is rounded once (nearest-even for
- * bf16).  Sequences with n_i = 1 run the split-KV decode path (partitions of
- * a few hundred tokens merged by log-sum-exp); sequences with n_i > 1 run
- * the chunked-prefill path (bf16: matrix cores).
+ * bf16).  Sequences with n_i = 1 run the split-KV decode path (their keys cut
+ * into parts whose partial results are merged by log-sum-exp); sequences with
+ * n_i > 1 run the chunked-prefill path (bf16: matrix cores; long key ranges
+ * likewise cut into pieces and merged).
  *
  *   out, q           device, [num_tokens][num_q_heads][head_dim], c->dtype
  *   k_cache, v_cache device pools (read only)
@@ -172,13 +174,26 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  * Supported: dtype f32 or bf16; head_dim 64 or 128; num_q_heads/num_kv_heads
  * in {1, 2, 4, 8}; block_size 16.  bf16 with head_dim 128 runs the scores of
  * the decode rows on the matrix cores; other combinations use the vector path.
+ * Decode on the matrix cores, up to 1024 sequences: a fixed grid of waves
+ * cuts each KV head's concatenated decode tiles into equal ranges (balanced);
+ * otherwise per-sequence partitions.  Results are deterministic: the same
+ * inputs give the same bits.  With the balanced decode, where a sequence is
+ * cut depends on the other sequences of the batch, so a reordered batch may
+ * differ in the last bits (within the stated tolerance).
  * Tuning knobs (environment, read on every call; results stay within the
  * stated tolerance under every setting):
- *   PA_SPLIT=auto (default) | off | <tokens>   decode partition size (a multiple
- *            of 16, <= 8192); auto aims at ~4096 (sequence, KV head, partition)
- *            work-groups with partitions of 128..2048 tokens
- *   PA_DECODE_WAVES=1|2|4   waves per decode work-group (matrix-core path)
- *   PA_DECODE=valu          force the vector decode kernel
+ *   PA_DECODE=partition     per-sequence partitions instead of the balanced decode
+ *   PA_DECODE=valu          force the vector decode kernel (partitioned)
+ *   PA_DECODE_TOTAL_WAVES=<1..65536>  balanced decode: waves in all (default
+ *            1024, one per SIMD), divided evenly among the KV heads
+ *   PA_DECODE_DEPTH=2|3|4   balanced decode: K/V tiles in flight per wave (default 3)
+ *   PA_SPLIT=auto (default) | off | <tokens>   partitioned decode: partition
+ *            size (a multiple of 16, <= 8192); auto aims at ~4096 (sequence,
+ *            KV head, partition) work-groups with partitions of 128..2048 tokens
+ *   PA_DECODE_WAVES=1|2|4   partitioned decode: waves per work-group
+ *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
+ *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
+ *            max(1024, a quarter of the longest sequence)
  * Errors: PA_ERR_ARG (incl. a workspace smaller than required),
  * PA_ERR_UNSUPPORTED, PA_ERR_RANGE (check mode), PA_ERR_HIP.
  */

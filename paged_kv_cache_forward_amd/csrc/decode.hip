@@ -35,6 +35,7 @@
 // Output: a sequence with one partition writes its normalised result directly;
 // otherwise each partition writes (m, l, acc) to the workspace and the merge
 // kernel below combines them in ascending partition order.
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 
@@ -448,7 +449,34 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
   while ((whole + part - 1) / part > kMaxParts) part *= 2;
   pl.part_tokens = part;
   pl.max_parts = (whole + part - 1) / part;
-  if (pl.max_parts > 1) {
+  pl.balanced = pl.mfma && decode_balanced_supported(num_seqs) &&
+                !(kind != nullptr && std::strcmp(kind, "partition") == 0);
+  if (pl.balanced) {
+    // 1024 single-wave work-groups in all: one per SIMD, every one resident
+    // at once (LDS and registers allow four per CU at depth 3), never more
+    // than the tiles there can be.  Measured on MI355X: HBM-bound batches
+    // gain nothing from more waves or deeper rings.  PA_DECODE_TOTAL_WAVES
+    // and PA_DECODE_DEPTH override.
+    int64_t target = 1024;
+    if (const char* tw = std::getenv("PA_DECODE_TOTAL_WAVES")) {
+      const int v = std::atoi(tw);
+      if (v >= 1 && v <= 65536) target = v;
+    }
+    const int64_t max_tiles = (int64_t)num_seqs * (whole / kBlock);
+    const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(target / num_kv_heads, max_tiles));
+    pl.waves_per_head = (int32_t)wg;
+    pl.depth = 3;
+    if (const char* dp = std::getenv("PA_DECODE_DEPTH")) {
+      const int v = std::atoi(dp);
+      if (v >= 2 && v <= 4) pl.depth = v;
+    }
+    pl.part_tokens = whole;
+    pl.max_parts = 1;
+    const size_t slots = (size_t)num_seqs + (size_t)wg;
+    pl.info_bytes = round256((size_t)num_seqs * 2 * sizeof(int32_t));
+    pl.acc_bytes = round256(slots * num_q_heads * head_dim * sizeof(float));
+    pl.ml_bytes = round256(slots * num_q_heads * 2 * sizeof(float));
+  } else if (pl.max_parts > 1) {
     const size_t items = (size_t)num_seqs * num_q_heads * pl.max_parts;
     pl.acc_bytes = round256(items * head_dim * sizeof(float));
     pl.ml_bytes = round256(items * 2 * sizeof(float));

@@ -300,6 +300,437 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(MfmaDecodeArgs k) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Balanced one-round decode.
+//
+// A fixed grid of W = Hkv * Wg single-wave work-groups, every one of which
+// has work: for KV head g, the decode tiles of all sequences are concatenated
+// in batch order into one stream of `total` tiles, and wave rank r of that
+// head takes tiles [r*total/Wg, (r+1)*total/Wg).  Every wave therefore moves
+// the same bytes, all waves are resident at once and each CU holds the same
+// number of them (no early-exiting work-groups to skew the dispatcher), and
+// each wave pays the start-up latency chain once.  A wave whose range crosses
+// sequence boundaries folds each sequence's part separately: a sequence it
+// covers whole is written out directly; otherwise its part goes to partial
+// slot i + r (unique: ranges are disjoint and ordered) and the merge kernel
+// combines a sequence's parts in rank order.  The wave holding a sequence's
+// first tile records (first rank, parts) for the merge.
+constexpr int kMaxBalancedSeqs = 1024;   // prefix sums kept in LDS per wave
+
+struct BalancedArgs {
+  AttnArgs a;
+  int32_t waves_per_head;   // Wg
+  int32_t slots;            // partial slots per KV head: num_seqs + Wg
+  float* p_acc;             // [Hkv][slots][G][D]
+  float* p_ml;              // [Hkv][slots][G][2]  (max in base-2 units, sum)
+  int2* seqinfo;            // [num_seqs]: (first rank, parts) of each decode sequence
+};
+
+inline size_t balanced_lds_bytes(int num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
+
+__device__ __forceinline__ int64_t stream_start(int r, int64_t total, int Wg) { return (int64_t)r * total / Wg; }
+// Rank whose range holds tile t: the largest r with stream_start(r) <= t.
+__device__ __forceinline__ int stream_owner(int64_t t, int64_t total, int Wg) {
+  return (int)(((t + 1) * Wg - 1) / total);
+}
+
+// Combine the four row groups (lanes j, j+16, j+32, j+48): afterwards every
+// lane (r, j) holds the wave's max M and sum lt of head j % G and, for every
+// head h, the accumulator of dims 8j .. 8j+7.
+template <int G>
+__device__ __forceinline__ void combine_row_groups(WaveState<G>& st, float& M, float& lt) {
+  M = fmaxf(st.m, __shfl_xor(st.m, 16));
+  M = fmaxf(M, __shfl_xor(M, 32));
+  const float f = fast_exp2(st.m - M);
+  lt = st.l * f;
+  lt += __shfl_xor(lt, 16);
+  lt += __shfl_xor(lt, 32);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float fh = bcast(f, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = st.acc[h][e] * fh;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      st.acc[h][e] = x;
+    }
+  }
+}
+
+// Write one finished segment of sequence i: the output when the segment is
+// the whole sequence, else a partial in slot i + rank of this KV head.
+template <int G>
+__device__ __forceinline__ void finish_segment(const BalancedArgs& k, int i, int g, int rank, bool whole, int q0,
+                                              WaveState<G>& st) {
+  const AttnArgs& a = k.a;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & 15, r = lane >> 4;
+  float M, lt;
+  combine_row_groups<G>(st, M, lt);
+  const size_t slot = (size_t)g * k.slots + (size_t)(i + rank);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if ((h & 3) != r) continue;   // row group r writes heads r, r+4, ...
+    if (whole) {
+      const float inv = 1.0f / bcast(lt, h);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = st.acc[h][e] * inv;
+      uint8_t* op = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + g * G + h) * kRowBytes + j * 16;
+      st16(op, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                          pack_bf16x2(f[6], f[7])));
+    } else {
+      float* dst = k.p_acc + (slot * G + h) * kD + 8 * j;
+      *reinterpret_cast<float4*>(dst) = make_float4(st.acc[h][0], st.acc[h][1], st.acc[h][2], st.acc[h][3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(st.acc[h][4], st.acc[h][5], st.acc[h][6], st.acc[h][7]);
+    }
+  }
+  if (!whole && r == 0 && j < G) *reinterpret_cast<float2*>(k.p_ml + (slot * G + j) * 2) = make_float2(M, lt);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The copies into LDS below are waited for explicitly.  Vector memory
+// operations complete in issue order, so "at most n outstanding" guarantees
+// completion of every operation that has n or more younger ones.  The waits
+// are assembly with a memory clobber so that no read of the copied data can
+// be moved above them.
+#define PA_VM_WAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// Buffer resource words for `bytes` bytes at a wave-uniform `base`.
+__device__ __forceinline__ u32x4_t rsrc_words(const uint8_t* base, int bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4_t w;
+  w.x = __builtin_amdgcn_readfirstlane((unsigned)p);
+  w.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+  w.z = (unsigned)bytes;
+  w.w = 0x00020000u;
+  return w;
+}
+
+// Copy 16 bytes per lane from the buffer (lane offset `voff`, bounds-checked:
+// out-of-range reads give zeros) to LDS at `lds` + 16 * lane.  Written as
+// assembly so that the compiler does not track these copies: every read of
+// the data they write is preceded by an explicit wait (PA_VM_WAIT), and extra
+// operations it does not count only make its own waits stricter.  M0 holds
+// the LDS address; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, const void* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
+__device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most 8 * t vector memory operations (t tiles' copies) are outstanding, t = 1..3.
+__device__ __forceinline__ void wait_tiles(int t) {
+  if (t <= 1) PA_VM_WAIT(8);
+  else if (t == 2) PA_VM_WAIT(16);
+  else PA_VM_WAIT(24);
+}
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+// One wave streams its range of the KV head's concatenated tiles, NS tiles
+// deep, through LDS: each tile is copied global -> LDS by the buffer unit
+// (no registers hold data in flight), into one of NS stage buffers that are
+// separate LDS arrays so that the wait before reading a stage covers only the
+// copies into that stage.  Each lane copies, and later reads back, exactly
+// the 16-byte pieces of the K and V tiles it uses, in the lane layout above.
+// Block-table entries are looked up 64 tiles at a time, one tile per lane
+// (sequence by binary search over the prefix sums), well ahead of use.  The
+// query rows of the next segment's sequence are copied to LDS one segment
+// ahead, so a sequence boundary only flushes the fold state: nothing issued
+// there is waited on by the next fold.
+template <int G, int NS>
+__global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
+  static_assert(16 % G == 0, "query heads per KV head must divide 16");
+  static_assert(NS >= 2 && NS <= 4, "tiles in flight");
+  // Per-sequence tables in dynamic LDS, sized by the batch (balanced_lds_bytes):
+  // prefix sums of decode tiles [num_seqs + 1], then query row << 5 | (valid
+  // keys of the last tile - 1) [num_seqs].
+  extern __shared__ int s_dyn[];
+  int* s_cum = s_dyn;
+  int* s_meta = s_dyn + k.a.num_seqs + 1;
+  __shared__ int s_raw[2][64];                   // lookup windows: block-table entry (copied), sequence, logical block
+  __shared__ int s_sj[2][2][64];
+  __shared__ __attribute__((aligned(16))) uint4 s_q[4 * 4 * G];    // next segment's query rows: [ks][r][h]
+  __shared__ __attribute__((aligned(16))) uint4 s_t0[512];         // tile stages: K [ks][lane], V [e][lane]
+  __shared__ __attribute__((aligned(16))) uint4 s_t1[512];
+  __shared__ __attribute__((aligned(16))) uint4 s_t2[512];
+  __shared__ __attribute__((aligned(16))) uint4 s_t3[512];
+  const AttnArgs& a = k.a;
+  const int Hkv = a.num_kv_heads;
+  const int g = blockIdx.x % Hkv, rank = blockIdx.x / Hkv;
+  const int lane = threadIdx.x;
+  const int S = a.num_seqs;
+
+  // Decode tiles of every sequence (0 for sequences with other than one query
+  // token), four chunks of 64 per batch so their loads overlap, then exclusive
+  // prefix sums in place.
+  for (int c0 = 0; c0 < S; c0 += 256) {
+    int T[4], M[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      T[u] = 0;
+      M[u] = 0;
+      if (i < S) {
+        const int q0 = a.qsl[i], n = a.qsl[i + 1] - q0;
+        const int len = min(a.seq_lens[i], a.bt_stride * kBlock);
+        if (n == 1 && q0 >= 0 && q0 < a.num_tokens && len > 0) {
+          T[u] = (len + kBlock - 1) / kBlock;
+          M[u] = (q0 << 5) | (len - 1 - (T[u] - 1) * kBlock);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      if (i < S) {
+        s_cum[i] = T[u];
+        s_meta[i] = M[u];
+      }
+    }
+  }
+  int carry = 0;
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    const int i = c0 + lane;
+    const int T = i < S ? s_cum[i] : 0;
+    int x = T;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (i < S) s_cum[i] = carry + x - T;
+    carry += __shfl(x, 63);
+  }
+  if (lane == 0) s_cum[S] = carry;
+  __syncthreads();
+  const int64_t total = carry;
+  // With fewer tiles than waves, the first `total` ranks take one tile each,
+  // so every rank that runs has a non-empty range and a sequence's parts sit
+  // in consecutive ranks.
+  const int Wg = (int)min((int64_t)k.waves_per_head, total);
+  if (rank >= Wg) return;
+  const int tb = (int)stream_start(rank, total, Wg);
+  const int n = (int)(stream_start(rank + 1, total, Wg) - tb);
+
+  // Lookup window w: tile 64 w + lane -> sequence and logical block (binary
+  // search over the prefix sums) and its block-table entry, copied to LDS.
+  const u32x4_t rbt = rsrc_words((const uint8_t*)a.block_tables,
+                                 (int)min((int64_t)S * a.bt_stride * 4, (int64_t)0x7fffffff));
+  auto lookup = [&](int window) {
+    const int u = window * 64 + lane;
+    int seq = 0, jt = 0;
+    if (u < n) {
+      const int t = tb + u;
+      int lo = 0, hi = S - 1;   // largest i with s_cum[i] <= t (that sequence has tiles)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      seq = lo;
+      jt = t - s_cum[lo];
+      lds_copy4(rbt, &s_raw[window & 1][0], (seq * a.bt_stride + jt) * 4);
+    }
+    s_sj[window & 1][0][lane] = seq;
+    s_sj[window & 1][1][lane] = jt;
+  };
+  lookup(0);
+  lookup(1);
+  PA_VM_WAIT(0);
+  int window = 0;
+
+  const int j = lane & 15, r = lane >> 4;
+  const int hq0 = g * G;
+  // Query rows of sequence `seq` -> s_q, lane r * G + h copying dims 32 ks + 8 r .. +8 of head h.
+  auto copy_q = [&](int seq) {
+    const int q0 = __builtin_amdgcn_readfirstlane(s_meta[seq] >> 5);
+    const u32x4_t rq = rsrc_words((const uint8_t*)a.q + ((size_t)q0 * a.num_q_heads + hq0) * kRowBytes, G * kRowBytes);
+    if (lane < 4 * G) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lds_copy16(rq, s_q + ks * 4 * G, (lane % G) * kRowBytes + (lane / G) * 16 + ks * 64);
+    }
+  };
+  copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]));
+  int q_tile = -(NS - 1);   // tile whose issue followed the last query copy
+
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * kTileBytes;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * kTileBytes;
+  const size_t block_stride = (size_t)Hkv * kTileBytes;
+  const int koff = j * kRowBytes + r * 16;
+  const int voff = 4 * r * kRowBytes + j * 16;
+  auto stage = [&](int sI) -> uint4* { return sI == 0 ? s_t0 : sI == 1 ? s_t1 : sI == 2 ? s_t2 : s_t3; };
+  auto issue = [&](int u, int sI) {
+    const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[(u >> 6) & 1][u & 63]), a.num_blocks);
+    const size_t off = (size_t)bid * block_stride;
+    const u32x4_t rk = rsrc_words(kc + off, kTileBytes);
+    const u32x4_t rv = rsrc_words(vc + off, kTileBytes);
+    uint4* dst = stage(sI);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds_copy16(rv, dst + 256 + e * 64, voff + e * kRowBytes);
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, n - 1), s0);
+
+  WaveState<G> st;
+  bf16x8_t qf[4];
+  int cur = -1, cur_end = 0, cur_j0 = 0, cur_jl = 0;
+  for (int u0 = 0; u0 < n; u0 += NS) {
+#pragma unroll
+    for (int sI = 0; sI < NS; ++sI) {
+      const int u = u0 + sI;
+      if (u >= n) break;
+      if ((u >> 6) != window) {
+        // Window w begins: look up window w + 1 into the slot window w - 1
+        // used.  Its first tile is issued NS - 1 tiles before window w + 1
+        // begins; by then the per-tile waits below have covered the copies.
+        ++window;
+        lookup(window + 1);
+      }
+      const int seq = __builtin_amdgcn_readfirstlane(s_sj[window & 1][0][u & 63]);
+      const int jt = __builtin_amdgcn_readfirstlane(s_sj[window & 1][1][u & 63]);
+      if (seq != cur) {
+        if (cur >= 0) {
+          const int T = s_cum[cur + 1] - s_cum[cur];
+          finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
+        }
+        cur = seq;
+        const int meta = s_meta[seq];
+        cur_end = (s_cum[seq + 1] - s_cum[seq] - 1) * kBlock + (meta & 31) + 1;   // sequence length
+        cur_j0 = jt;
+        if (jt == 0 && g == 0 && lane == 0) {
+          const int last = stream_owner((int64_t)s_cum[seq + 1] - 1, total, Wg);
+          k.seqinfo[seq] = make_int2(rank, last - rank + 1);
+        }
+        // This sequence's query copy was followed by the issues of tiles
+        // q_tile .. u - 1 (eight copies each; at least one tile).
+        __builtin_amdgcn_sched_barrier(0);
+        wait_tiles(min(u - q_tile, NS - 1));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          qf[ks] = __builtin_bit_cast(bf16x8_t, s_q[ks * 4 * G + r * G + j % G]);
+        // The copy of the next sequence's rows overwrites s_q: the reads above come first.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        int nx = seq + 1;                      // next sequence with tiles, if this range reaches it
+        while (nx < S && s_cum[nx + 1] == s_cum[nx]) ++nx;
+        if (nx < S && s_cum[nx] < tb + n) {
+          copy_q(nx);
+          q_tile = u;
+        }
+        st.m = kNegBig;
+        st.l = 0.0f;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.0f;
+      }
+      // The stage refilled here was read by the previous fold; the copies
+      // stay after those reads and ahead of the reads of this tile's stage,
+      // which wait for this tile's copies: NS - 1 tiles were issued after them.
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(u + NS - 1, n - 1), (sI + NS - 1) % NS);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_tiles(NS - 1);
+      cur_jl = jt;
+      const lds_u32x4_t* src = (const lds_u32x4_t*)stage(sI);
+      uint4 kq[4], vq[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vq[e] = __builtin_bit_cast(uint4, src[256 + e * 64 + lane]);
+      fold<G>(kq, vq, qf, jt * kBlock, cur_end, r, a.scale_log2, st);
+    }
+  }
+  const int T = s_cum[cur + 1] - s_cum[cur];
+  finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
+}
+
+// Merge of the balanced decode's parts: one work-group of 256 threads per
+// (sequence, query head), row group q folding parts q, q+8, ... in rank order
+// with the log-sum-exp rule, then combining row groups through LDS in order.
+template <int G>
+__global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
+  constexpr int TPR = kD / 4, R = 256 / TPR, U = 4;
+  __shared__ float s_m[R], s_l[R];
+  __shared__ float4 s_acc[R][TPR];
+  const AttnArgs& a = k.a;
+  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int q0 = a.qsl[i];
+  if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
+  if (min(a.seq_lens[i], a.bt_stride * kBlock) <= 0) return;
+  const int2 si = k.seqinfo[i];          // written by this call's decode kernel
+  const int P = si.y;
+  if (P <= 1) return;                    // written out by the decode kernel
+  const int g = h / G, hh = h % G;
+  const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);
+  const int d4 = tid % TPR, rq = tid / TPR;
+  float Mx = -INFINITY, den = 0.0f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = rq; p0 < P; p0 += R * U) {
+    float2 v[U];
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pp = p0 + u * R;
+      if (pp < P) {
+        const size_t e = (slot0 + pp) * G + hh;
+        v[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
+        x[u] = reinterpret_cast<const float4*>(k.p_acc + e * kD)[d4];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (p0 + u * R >= P) break;
+      const float Mn = fmaxf(Mx, v[u].x);
+      const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(v[u].x - Mn);
+      den = fmaf(den, sa, v[u].y * sb);
+      num.x = fmaf(num.x, sa, x[u].x * sb);
+      num.y = fmaf(num.y, sa, x[u].y * sb);
+      num.z = fmaf(num.z, sa, x[u].z * sb);
+      num.w = fmaf(num.w, sa, x[u].w * sb);
+      Mx = Mn;
+    }
+  }
+  s_acc[rq][d4] = num;
+  if (d4 == 0) {
+    s_m[rq] = Mx;
+    s_l[rq] = den;
+  }
+  __syncthreads();
+  if (rq != 0) return;
+  float Mt = s_m[0];
+#pragma unroll
+  for (int q = 1; q < R; ++q) Mt = fmaxf(Mt, s_m[q]);
+  float dt = 0.0f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const float f = fast_exp2(s_m[q] - Mt);
+    const float4 y = s_acc[q][d4];
+    dt = fmaf(f, s_l[q], dt);
+    o.x = fmaf(f, y.x, o.x); o.y = fmaf(f, y.y, o.y); o.z = fmaf(f, y.z, o.z); o.w = fmaf(f, y.w, o.w);
+  }
+  const float inv = 1.0f / dt;
+  uint8_t* op = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + h) * kRowBytes + d4 * 8;
+  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
+}
+
 template <int NW>
 pa_status launch_nw(const MfmaDecodeArgs& k, int G, dim3 grid, hipStream_t s) {
   if (G != 1 && G != 2 && G != 4 && G != 8)
@@ -316,7 +747,38 @@ pa_status launch_nw(const MfmaDecodeArgs& k, int G, dim3 grid, hipStream_t s) {
   return launch_status("pa_forward (decode, matrix cores)");
 }
 
+template <int G>
+pa_status launch_balanced_g(const BalancedArgs& k, int depth, hipStream_t s) {
+  const int W = k.waves_per_head * k.a.num_kv_heads;
+  const size_t lds = balanced_lds_bytes(k.a.num_seqs);
+  int mark = trace_begin(s);
+  if (depth == 4) hipLaunchKernelGGL((decode_balanced_kernel<G, 4>), dim3(W), dim3(64), lds, s, k);
+  else if (depth == 3) hipLaunchKernelGGL((decode_balanced_kernel<G, 3>), dim3(W), dim3(64), lds, s, k);
+  else hipLaunchKernelGGL((decode_balanced_kernel<G, 2>), dim3(W), dim3(64), lds, s, k);
+  trace_end(s, mark, "decode_mfma");
+  pa_status st = launch_status("pa_forward (decode, balanced)");
+  if (st != PA_OK) return st;
+  mark = trace_begin(s);
+  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs, k.a.num_q_heads), dim3(256), 0, s, k);
+  trace_end(s, mark, "merge");
+  return launch_status("pa_forward (decode merge, balanced)");
+}
+
 }  // namespace
+
+bool decode_balanced_supported(int32_t num_seqs) { return num_seqs >= 1 && num_seqs <= kMaxBalancedSeqs; }
+
+pa_status launch_decode_balanced(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
+                                 int32_t* part_table, hipStream_t s) {
+  BalancedArgs k{a, plan.waves_per_head, a.num_seqs + plan.waves_per_head, p_acc, p_ml, (int2*)part_table};
+  switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_balanced_g<1>(k, plan.depth, s);
+    case 2: return launch_balanced_g<2>(k, plan.depth, s);
+    case 4: return launch_balanced_g<4>(k, plan.depth, s);
+    case 8: return launch_balanced_g<8>(k, plan.depth, s);
+    default: return fail(PA_ERR_UNSUPPORTED, "pa_forward: %d query heads per KV head", a.num_q_heads / a.num_kv_heads);
+  }
+}
 
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
   return dtype == PA_BF16 && head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);

@@ -137,14 +137,16 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   a.scale_log2 = scale * kLog2e;
   a.causal = causal;
 
+  int32_t* p_info = nullptr;
   float* p_acc = nullptr;
   float* p_ml = nullptr;
   float* pre_o = nullptr;
   float* pre_ml = nullptr;
   if (ws_need > 0) {
     uint8_t* base = (uint8_t*)workspace;
-    p_acc = (float*)base;
-    p_ml = (float*)(base + fs.plan.acc_bytes);
+    p_info = (int32_t*)base;
+    p_acc = (float*)(base + fs.plan.info_bytes);
+    p_ml = (float*)(base + fs.plan.info_bytes + fs.plan.acc_bytes);
     pre_o = (float*)(base + fs.plan.workspace_bytes());
     pre_ml = (float*)(base + fs.plan.workspace_bytes() + fs.pplan.o_bytes);
   }
@@ -152,6 +154,7 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
     st = launch_prefill(a, max_query_len, fs.pplan, pre_o, pre_ml, s);
     if (st != PA_OK) return st;
   }
+  if (fs.plan.balanced) return launch_decode_balanced(a, fs.plan, p_acc, p_ml, p_info, s);
   if (fs.plan.mfma)
     st = launch_decode_mfma(a, fs.plan, p_acc, p_ml, s);
   else

@@ -40,19 +40,30 @@ struct AttnArgs {
   int32_t causal;
 };
 
-// Split-KV plan for the decode path (sequences with one query token).
+// Plan for the decode path (sequences with one query token).
 //
-// Workspace layout when the plan needs one (offsets 256-byte aligned):
+// Balanced (decode_mfma, at most 1024 sequences): `waves_per_head` waves per KV
+// head split that head's concatenated decode tiles into equal ranges.
+// Workspace (offsets 256-byte aligned):
+//   [part table: int32 [num_seqs][2]]
+//   [partial acc: fp32 [Hkv][num_seqs + waves_per_head][G][head_dim]]
+//   [partial (max, sum): fp32 [Hkv][num_seqs + waves_per_head][G][2]]
+// Partitioned (otherwise): sequences are cut into partitions of part_tokens.
+// Workspace when max_parts > 1:
 //   [partial acc: fp32 [num_seqs][Hq][max_parts][head_dim]]
 //   [partial (max, sum): fp32 [num_seqs][Hq][max_parts][2]]
 struct DecodePlan {
-  bool mfma;             // decode_mfma (bf16, head_dim 128) instead of the VALU kernel
-  int32_t waves;         // waves per work-group of decode_mfma
-  int32_t part_tokens;   // tokens per partition (multiple of 16)
-  int32_t max_parts;     // partitions of the longest sequence; 1 = no split
-  size_t acc_bytes;      // partial accumulators
-  size_t ml_bytes;       // partial (max, sum) pairs
-  size_t workspace_bytes() const { return acc_bytes + ml_bytes; }
+  bool mfma;               // decode on the matrix cores (bf16, head_dim 128), else the VALU kernel
+  bool balanced;           // balanced one-round decode_mfma launch
+  int32_t waves_per_head;  // balanced: waves per KV head
+  int32_t depth;           // balanced: K/V tiles in flight per wave (2..4)
+  int32_t waves;           // partitioned decode_mfma: waves per work-group
+  int32_t part_tokens;     // partitioned: tokens per partition (multiple of 16)
+  int32_t max_parts;       // partitioned: partitions of the longest sequence; 1 = no split
+  size_t info_bytes;       // balanced: part table
+  size_t acc_bytes;        // partial accumulators
+  size_t ml_bytes;         // partial (max, sum) pairs
+  size_t workspace_bytes() const { return info_bytes + acc_bytes + ml_bytes; }
 };
 
 DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -69,6 +80,10 @@ pa_status launch_merge(const AttnArgs& a, int32_t dtype, const DecodePlan& plan,
 bool decode_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 pa_status launch_decode_mfma(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
                              hipStream_t s);
+// Balanced decode_mfma and its merge (both launched here).
+bool decode_balanced_supported(int32_t num_seqs);
+pa_status launch_decode_balanced(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
+                                 int32_t* part_table, hipStream_t s);
 
 // Split-KV plan for the chunked-prefill kernel: the key range of every
 // (sequence, query tile, KV head) work-group is cut into pieces of piece_keys

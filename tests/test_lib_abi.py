@@ -63,17 +63,42 @@ def test_host_argument_errors_without_a_gpu():
     assert st == pa.PA_OK
 
 
-def test_workspace_size_follows_the_split():
+def _r256(n):
+    return (n + 255) // 256 * 256
+
+
+def test_workspace_size_follows_the_split(monkeypatch):
+    """Partitioned decode: partial accumulators [S][Hq][P][D] fp32, then (max, sum) [S][Hq][P][2]."""
     import ctypes
+    monkeypatch.setenv("PA_DECODE", "partition")
     pa = ensure_library()
     desc = pa.CacheDesc(20000, 8, 128, 16, pa.PA_BF16)
     small = pa.lib.pa_forward_workspace_size(64, 64, 32, 200, 1, ctypes.byref(desc))
     big = pa.lib.pa_forward_workspace_size(64, 64, 32, 4096, 1, ctypes.byref(desc))
     assert small == 0 and big > 0
-
-    def r256(n):
-        return (n + 255) // 256 * 256
-
-    # layout: partial accumulators [S][Hq][P][D] fp32, then partial (max, sum) [S][Hq][P][2] fp32
-    parts = [p for p in range(1, 4097) if big == r256(64 * 32 * p * 128 * 4) + r256(64 * 32 * p * 8)]
+    parts = [p for p in range(1, 4097) if big == _r256(64 * 32 * p * 128 * 4) + _r256(64 * 32 * p * 8)]
     assert len(parts) == 1 and parts[0] > 1
+
+
+def test_workspace_size_of_the_balanced_decode(monkeypatch):
+    """Balanced decode: part table [S][2] int32, then partials for S + Wg slots per KV head
+    ([Hkv][S+Wg][G][D] fp32 and [Hkv][S+Wg][G][2] fp32), Wg = min(total waves / Hkv, S * tiles)."""
+    import ctypes
+    monkeypatch.delenv("PA_DECODE", raising=False)
+    pa = ensure_library()
+    desc = pa.CacheDesc(20000, 8, 128, 16, pa.PA_BF16)
+
+    def expect(S, Hq, wg):
+        return _r256(S * 8) + _r256((S + wg) * Hq * 128 * 4) + _r256((S + wg) * Hq * 8)
+
+    for total, S, L, wg in [(None, 64, 4096, 128), (None, 3, 20, 6), ("64", 64, 4096, 8), ("1", 5, 100, 1)]:
+        if total is None:
+            monkeypatch.delenv("PA_DECODE_TOTAL_WAVES", raising=False)
+        else:
+            monkeypatch.setenv("PA_DECODE_TOTAL_WAVES", total)
+        got = pa.lib.pa_forward_workspace_size(S, S, 32, L, 1, ctypes.byref(desc))
+        assert got == expect(S, 32, wg), (total, S, L, got)
+    # over 1024 sequences the partitioned kernel takes over
+    monkeypatch.delenv("PA_DECODE_TOTAL_WAVES", raising=False)
+    got = pa.lib.pa_forward_workspace_size(2000, 2000, 32, 200, 1, ctypes.byref(desc))
+    assert got == 0
