@@ -661,74 +661,105 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
 }
 
-// Merge of the balanced decode's parts: one work-group of 256 threads per
-// (sequence, query head), row group q folding parts q, q+8, ... in rank order
-// with the log-sum-exp rule, then combining row groups through LDS in order.
+// Merge of the balanced decode's parts: one work-group of four waves per
+// (sequence, KV head), for all G query heads of that head.  A part's G x D
+// partial block is contiguous, so reading a part is one coalesced load of 2G
+// floats per lane (lane = head * 64/G + chunk).  Wave w folds parts w, w+4,
+// ... in order with the log-sum-exp rule (four parts' loads in flight), then
+// wave 0 combines the four waves in order through LDS.
 template <int G>
 __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
-  constexpr int TPR = kD / 4, R = 256 / TPR, U = 4;
-  __shared__ float s_m[R], s_l[R];
-  __shared__ float4 s_acc[R][TPR];
+  constexpr int LPH = 64 / G;          // lanes per head
+  constexpr int DPL = kD / LPH;        // dims per lane: 2 G
+  constexpr int NWV = 4, U = 4;
+  __shared__ float s_m[NWV][G], s_l[NWV][G];
+  __shared__ float4 s_num[NWV][DPL / 4][64];
   const AttnArgs& a = k.a;
-  const int i = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int i = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane / LPH, c = lane % LPH;
   const int q0 = a.qsl[i];
   if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
   if (min(a.seq_lens[i], a.bt_stride * kBlock) <= 0) return;
   const int2 si = k.seqinfo[i];          // written by this call's decode kernel
   const int P = si.y;
   if (P <= 1) return;                    // written out by the decode kernel
-  const int g = h / G, hh = h % G;
   const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);
-  const int d4 = tid % TPR, rq = tid / TPR;
   float Mx = -INFINITY, den = 0.0f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int p0 = rq; p0 < P; p0 += R * U) {
-    float2 v[U];
-    float4 x[U];
+  float num[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) num[e] = 0.0f;
+  for (int p0 = w; p0 < P; p0 += NWV * U) {
+    float2 ml[U];
+    float4 x[U][DPL / 4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int pp = p0 + u * R;
-      if (pp < P) {
-        const size_t e = (slot0 + pp) * G + hh;
-        v[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
-        x[u] = reinterpret_cast<const float4*>(k.p_acc + e * kD)[d4];
+      if (p0 + u * NWV < P) {
+        const size_t e = (slot0 + p0 + u * NWV) * G + h;
+        ml[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
+        const float4* src = reinterpret_cast<const float4*>(k.p_acc + e * kD + c * DPL);
+#pragma unroll
+        for (int v = 0; v < DPL / 4; ++v) x[u][v] = src[v];
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (p0 + u * R >= P) break;
-      const float Mn = fmaxf(Mx, v[u].x);
-      const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(v[u].x - Mn);
-      den = fmaf(den, sa, v[u].y * sb);
-      num.x = fmaf(num.x, sa, x[u].x * sb);
-      num.y = fmaf(num.y, sa, x[u].y * sb);
-      num.z = fmaf(num.z, sa, x[u].z * sb);
-      num.w = fmaf(num.w, sa, x[u].w * sb);
+      if (p0 + u * NWV >= P) break;
+      const float Mn = fmaxf(Mx, ml[u].x);
+      const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(ml[u].x - Mn);
+      den = fmaf(den, sa, ml[u].y * sb);
+#pragma unroll
+      for (int v = 0; v < DPL / 4; ++v) {
+        num[4 * v + 0] = fmaf(num[4 * v + 0], sa, x[u][v].x * sb);
+        num[4 * v + 1] = fmaf(num[4 * v + 1], sa, x[u][v].y * sb);
+        num[4 * v + 2] = fmaf(num[4 * v + 2], sa, x[u][v].z * sb);
+        num[4 * v + 3] = fmaf(num[4 * v + 3], sa, x[u][v].w * sb);
+      }
       Mx = Mn;
     }
   }
-  s_acc[rq][d4] = num;
-  if (d4 == 0) {
-    s_m[rq] = Mx;
-    s_l[rq] = den;
+  if (c == 0) {
+    s_m[w][h] = Mx;    // -inf for a wave without parts: weight 0 below
+    s_l[w][h] = den;
   }
+#pragma unroll
+  for (int v = 0; v < DPL / 4; ++v)
+    s_num[w][v][lane] = make_float4(num[4 * v], num[4 * v + 1], num[4 * v + 2], num[4 * v + 3]);
   __syncthreads();
-  if (rq != 0) return;
-  float Mt = s_m[0];
+  if (w != 0) return;
+  float Mt = s_m[0][h];
 #pragma unroll
-  for (int q = 1; q < R; ++q) Mt = fmaxf(Mt, s_m[q]);
+  for (int ww = 1; ww < NWV; ++ww) Mt = fmaxf(Mt, s_m[ww][h]);
   float dt = 0.0f;
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float o[DPL];
 #pragma unroll
-  for (int q = 0; q < R; ++q) {
-    const float f = fast_exp2(s_m[q] - Mt);
-    const float4 y = s_acc[q][d4];
-    dt = fmaf(f, s_l[q], dt);
-    o.x = fmaf(f, y.x, o.x); o.y = fmaf(f, y.y, o.y); o.z = fmaf(f, y.z, o.z); o.w = fmaf(f, y.w, o.w);
+  for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+#pragma unroll
+  for (int ww = 0; ww < NWV; ++ww) {
+    const float f = fast_exp2(s_m[ww][h] - Mt);
+    dt = fmaf(f, s_l[ww][h], dt);
+#pragma unroll
+    for (int v = 0; v < DPL / 4; ++v) {
+      const float4 y = s_num[ww][v][lane];
+      o[4 * v + 0] = fmaf(f, y.x, o[4 * v + 0]);
+      o[4 * v + 1] = fmaf(f, y.y, o[4 * v + 1]);
+      o[4 * v + 2] = fmaf(f, y.z, o[4 * v + 2]);
+      o[4 * v + 3] = fmaf(f, y.w, o[4 * v + 3]);
+    }
   }
   const float inv = 1.0f / dt;
-  uint8_t* op = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + h) * kRowBytes + d4 * 8;
-  *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
+  uint32_t wd[DPL / 2];
+#pragma unroll
+  for (int e = 0; e < DPL / 2; ++e) wd[e] = pack_bf16x2(o[2 * e] * inv, o[2 * e + 1] * inv);
+  uint8_t* op = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + g * G + h) * kRowBytes + c * DPL * 2;
+  if constexpr (DPL == 2) {
+    *reinterpret_cast<uint32_t*>(op) = wd[0];
+  } else if constexpr (DPL == 4) {
+    *reinterpret_cast<uint2*>(op) = make_uint2(wd[0], wd[1]);
+  } else {
+#pragma unroll
+    for (int v = 0; v < DPL / 8; ++v)
+      *reinterpret_cast<uint4*>(op + 16 * v) = make_uint4(wd[4 * v], wd[4 * v + 1], wd[4 * v + 2], wd[4 * v + 3]);
+  }
 }
 
 template <int NW>
@@ -759,7 +790,7 @@ pa_status launch_balanced_g(const BalancedArgs& k, int depth, hipStream_t s) {
   pa_status st = launch_status("pa_forward (decode, balanced)");
   if (st != PA_OK) return st;
   mark = trace_begin(s);
-  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs, k.a.num_q_heads), dim3(256), 0, s, k);
+  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(256), 0, s, k);
   trace_end(s, mark, "merge");
   return launch_status("pa_forward (decode merge, balanced)");
 }
