@@ -123,11 +123,43 @@ def traced_region(pa, run, steps, stream, with_writes=True):
     return per
 
 
+def strip_comments(text):
+    """C/C++ source without // and /* */ comments, trailing blanks or blank lines (string literals kept)."""
+    out, i, n, quote = [], 0, len(text), None
+    while i < n:
+        c = text[i]
+        if quote:
+            out.append(c)
+            if c == "\\" and i + 1 < n:
+                out.append(text[i + 1])
+                i += 2
+                continue
+            if c == quote:
+                quote = None
+            i += 1
+        elif c in "\"'":
+            quote = c
+            out.append(c)
+            i += 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [l.rstrip() for l in "".join(out).split("\n")]
+    return "\n".join(l for l in lines if l)
+
+
 def source_digest(*names):
+    """sha256 of the kernels' code (comments and blank lines stripped): a comment edit keeps it."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_forward_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_forward_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()
 
 

@@ -1,5 +1,12 @@
 // Decode attention for bf16 K/V with head_dim 128: scores on the matrix cores,
-// P.V on the vector ALUs, split-KV partitions written for the merge kernel.
+// P.V on the vector ALUs.  Two launches share the per-tile fold below:
+//   * the balanced kernel (decode_balanced_kernel, further down; the default
+//     up to 1024 sequences): a fixed grid of waves cuts each KV head's
+//     concatenated tiles into equal ranges, stages them through LDS, and
+//     writes partial results for its own merge kernel;
+//   * the partitioned kernel (decode_mfma_kernel): one work-group per
+//     (sequence, KV head, partition), partials merged by the merge kernel of
+//     decode.hip.
 //
 // What is computed: "PagedAttention et vLLM" (aiunderstanding.org), section
 // "Plongée profonde": the new token of each sequence attends to all of its
@@ -19,8 +26,8 @@
 // v_mfma_f32_16x16x32_bf16 per 32 dims does it in 4 instructions, reading the
 // K tile in its stored layout as the A operand.
 //
-// Work item: one work-group of NW waves per (sequence i, KV head g, partition
-// p of `part_tokens` tokens).  Wave w folds tiles w, w+NW, ... of the partition.
+// Partitioned kernel's work item: one work-group of NW waves per (sequence i,
+// KV head g, partition p of `part_tokens` tokens).  Wave w folds tiles w, w+NW, ... of the partition.
 // Launch order is g fastest, so consecutive work-groups (which the dispatcher
 // spreads over the 8 XCDs) of one sequence and partition run on different XCDs
 // while every work-group of one KV head lands on the same XCD.
@@ -45,8 +52,8 @@
 // -inf and their V rows are zeroed, so stale or NaN slots never reach an
 // accumulator.
 //
-// Finish: the row groups are combined with the log-sum-exp rule, then the NW
-// waves through LDS.  A sequence with one partition writes its output;
+// Partitioned finish: the row groups are combined with the log-sum-exp rule,
+// then the NW waves through LDS.  A sequence with one partition writes its output;
 // otherwise each partition writes (max, sum, acc) to the workspace and the
 // merge kernel, launched next on the same stream, combines the partitions in
 // ascending order.  (Merging inside this kernel -- the last partition to finish
@@ -54,7 +61,7 @@
 // write-back per work-group; measured on MI355X that serialises at roughly
 // 0.5 us per partition per XCD and cost more than the separate launch.)
 //
-// Start-up: the block-table entries of a wave's first tiles are requested
+// Partitioned start-up: the block-table entries of a wave's first tiles are requested
 // together with the sequence length (the index is clamped to the table, so
 // the speculative read is always in bounds), which removes one dependent
 // memory round trip from every work-group.
