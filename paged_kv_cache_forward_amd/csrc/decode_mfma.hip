@@ -396,57 +396,6 @@ __device__ __forceinline__ void finish_segment(const BalancedArgs& k, int i, int
   if (!whole && r == 0 && j < G) *reinterpret_cast<float2*>(k.p_ml + (slot * G + j) * 2) = make_float2(M, lt);
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// The copies into LDS below are waited for explicitly.  Vector memory
-// operations complete in issue order, so "at most n outstanding" guarantees
-// completion of every operation that has n or more younger ones.  The waits
-// are assembly with a memory clobber so that no read of the copied data can
-// be moved above them.
-#define PA_VM_WAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
-
-// Buffer resource words for `bytes` bytes at a wave-uniform `base`.
-__device__ __forceinline__ u32x4_t rsrc_words(const uint8_t* base, int bytes) {
-  const unsigned long long p = (unsigned long long)base;
-  u32x4_t w;
-  w.x = __builtin_amdgcn_readfirstlane((unsigned)p);
-  w.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
-  w.z = (unsigned)bytes;
-  w.w = 0x00020000u;
-  return w;
-}
-
-// Copy 16 bytes per lane from the buffer (lane offset `voff`, bounds-checked:
-// out-of-range reads give zeros) to LDS at `lds` + 16 * lane.  Written as
-// assembly so that the compiler does not track these copies: every read of
-// the data they write is preceded by an explicit wait (PA_VM_WAIT), and extra
-// operations it does not count only make its own waits stricter.  M0 holds
-// the LDS address; nothing else in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, const void* lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-// As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
-__device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most 8 * t vector memory operations (t tiles' copies) are outstanding, t = 1..3.
-__device__ __forceinline__ void wait_tiles(int t) {
-  if (t <= 1) PA_VM_WAIT(8);
-  else if (t == 2) PA_VM_WAIT(16);
-  else PA_VM_WAIT(24);
-}
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-
 // One wave streams its range of the KV head's concatenated tiles, NS tiles
 // deep, through LDS: each tile is copied global -> LDS by the buffer unit
 // (no registers hold data in flight), into one of NS stage buffers that are

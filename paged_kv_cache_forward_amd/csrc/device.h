@@ -119,6 +119,59 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int voff) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---- Copies global -> LDS through the buffer unit ---------------------------
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The copies into LDS below are waited for explicitly.  Vector memory
+// operations complete in issue order, so "at most n outstanding" guarantees
+// completion of every operation that has n or more younger ones.  The waits
+// are assembly with a memory clobber so that no read of the copied data can
+// be moved above them.
+#define PA_VM_WAIT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// Buffer resource words for `bytes` bytes at a wave-uniform `base`.
+__device__ __forceinline__ u32x4_t rsrc_words(const uint8_t* base, int bytes) {
+  const unsigned long long p = (unsigned long long)base;
+  u32x4_t w;
+  w.x = __builtin_amdgcn_readfirstlane((unsigned)p);
+  w.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
+  w.z = (unsigned)bytes;
+  w.w = 0x00020000u;
+  return w;
+}
+
+// Copy 16 bytes per lane from the buffer (lane offset `voff`, bounds-checked:
+// out-of-range reads give zeros) to LDS at `lds` + 16 * lane.  Written as
+// assembly so that the compiler does not track these copies: every read of
+// the data they write is preceded by an explicit wait (PA_VM_WAIT), and extra
+// operations it does not count only make its own waits stricter.  M0 holds
+// the LDS address; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(u32x4_t rsrc, const void* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
+__device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most 8 * t vector memory operations (t tiles' copies) are outstanding, t = 1..3.
+__device__ __forceinline__ void wait_tiles(int t) {
+  if (t <= 1) PA_VM_WAIT(8);
+  else if (t == 2) PA_VM_WAIT(16);
+  else PA_VM_WAIT(24);
+}
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
 // Widen eight bf16 (one 16-byte chunk) to fp32.
 __device__ __forceinline__ void widen_bf16x8(uint4 w, float* f) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);

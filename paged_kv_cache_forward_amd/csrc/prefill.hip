@@ -18,12 +18,13 @@
 // runs on one XCD and shares that XCD's L2 for the K/V it re-reads), then the
 // query tile, latest tiles (most keys) first, then the sequence.
 //
-// K/V tiles of 64 keys (four 16-token cache blocks) are loaded one tile
-// ahead into registers and stored to a double-buffered LDS stage.  Each load
-// goes through a buffer descriptor built in SGPRs for one cache block whose
-// range ends at the sequence's last token, so slots past it (stale, possibly
-// NaN) read as zero and never reach an MFMA.  The block table of the
-// work-group's key range is staged in LDS, a window at a time.
+// K/V tiles of 64 keys (four 16-token cache blocks) are copied global -> LDS
+// by the buffer unit, one tile ahead, into a double-buffered LDS stage (no
+// registers hold data in flight).  Each copy goes through a buffer resource
+// for one cache block whose range ends at the sequence's last token, so slots
+// past it (stale, possibly NaN) read as zero and never reach an MFMA.  The
+// block table of the work-group's key range is staged in LDS, a window at a
+// time.
 //
 // Contractions, v_mfma_f32_16x16x32_bf16 (A 16x32, B 32x16, C 16x16 fp32):
 //   S^T = K Q^T     A = K rows from LDS (lane: key row l % 16, dims 8 (l / 16)
@@ -53,29 +54,40 @@
 namespace pa {
 namespace {
 
-constexpr int kRowsPerWG = 128;   // (token, query head) rows per work-group: 4 waves x 32
+constexpr int kWaves = 4;                    // waves per work-group (4 or 8)
+constexpr int kWavesPerBlock = kWaves / 4;   // waves copying each of a tile's four cache blocks
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWG = 32 * kWaves;      // (token, query head) rows per work-group: 32 per wave
 constexpr int kKeys = 64;         // keys per tile: four 16-token cache blocks
 constexpr int kBtCache = 1024;    // block-table entries staged in LDS (16384 tokens)
 
+// LDS stage of one 64-key tile, filled by buffer-unit copies (16 bytes per
+// lane, lane l of a copy landing at its piece base + 16 l), one 1 KiB piece
+// per copy, laid out so that every fragment read is conflict-free:
+//   K piece (block b, k-step ks): lane (lr, lq) = lq * 16 + lr holds key row
+//     16 b + lr, dims 32 ks + 8 lq .. +8 -- exactly the A fragment that lane
+//     reads for S^T = K Q^T, so it reads its own 16 bytes back.
+//   V piece (block b, dim pair dp): lane dsel * 32 + 2 r + h holds key row
+//     16 b + r, dims 16 (2 dp + dsel) + 8 h .. +8; a transpose read for
+//     output columns dt = 2 dp + dsel then has each 16-lane group reading
+//     128 contiguous bytes.
+// Each of the tile's four cache blocks is copied by kWaves / 4 waves: with
+// four waves, wave b copies block b's KS K pieces and DT/2 V pieces; with
+// eight, waves 2b and 2b + 1 split them.
 template <int D>
 struct PCfg {
   static constexpr int ROW = D * 2;                       // bytes of one key row (one KV head)
   static constexpr int TILE = kBlock * ROW;               // bytes of one (block, KV head) tile
-  static constexpr int KS = D / 32;                       // MFMA k-steps over the head dim
-  static constexpr int DT = D / 16;                       // 16-column output tiles
-  static constexpr int KSTR = ROW + 16;                   // LDS row stride of K (bank spread)
-  static constexpr int VSTR = ROW + 32;                   // LDS row stride of V (bank spread)
-  static constexpr int KBUF = kKeys * KSTR;
-  static constexpr int BUF = KBUF + kKeys * VSTR;         // one stage: K tile, then V tile
-  static constexpr int LPT = kKeys * ROW / (16 * 256);    // 16-byte loads per thread per tensor per tile
-  static_assert(LPT * 16 * 256 == kKeys * ROW, "tile split");
-  static_assert(TILE % 1024 == 0, "a wave's 1 KiB of a load stays inside one block tile");
+  static constexpr int KS = D / 32;                       // MFMA k-steps over the head dim; K pieces per block
+  static constexpr int DT = D / 16;                       // 16-column output tiles; DT / 2 V pieces per block
+  static constexpr int KBUF = kKeys * ROW;                // K part of a stage
+  static constexpr int BUF = 2 * KBUF;                    // one stage: K pieces, then V pieces
+  static_assert(KBUF == 4 * KS * 1024 && KBUF == 4 * (DT / 2) * 1024, "1 KiB pieces");
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;   // LDS byte pointer (no generic-pointer checks)
 
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
 
 __device__ __forceinline__ u32x4_t buf_ld16v(__amdgpu_buffer_rsrc_t r, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
@@ -113,9 +125,9 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillArgs pk) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_stage[2 * C::BUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_stage[2 * C::BUF];
   __shared__ int s_bt[kBtCache];
   lds_u8* const lds = (lds_u8*)lds_stage;
 
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
   const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
   auto fill_window = [&](int win) {
     const int b0 = win * kBtCache;
-    for (int b = tid; b < min(nblk - b0, kBtCache); b += 256) s_bt[b] = clamp_block(bt_row[b0 + b], a.num_blocks);
+    for (int b = tid; b < min(nblk - b0, kBtCache); b += kThreads) s_bt[b] = clamp_block(bt_row[b0 + b], a.num_blocks);
   };
   int cur_win = kt0 * (kKeys / kBlock) / kBtCache;
   fill_window(cur_win);
@@ -179,17 +191,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
     }
   }
 
+  // Exponent arguments are cs * s - m in base-2 units (cs = |scale| log2 e),
+  // one fma per score; a negative scale is folded into Q by exact sign flips,
+  // so the running max can be taken over raw scores.
+  // cs >= 1e-30 so that a masked score (-inf) always gives a -inf argument;
+  // at scale 0 the arguments stay 0 to fp32 precision (uniform weights).
+  const float cs = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  if (a.scale_log2 < 0.0f) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        uint4 u = __builtin_bit_cast(uint4, qf[rt][ks]);
+        u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+        qf[rt][ks] = __builtin_bit_cast(bf16x8_t, u);
+      }
+  }
+  // A operand of all ones: the extra output tile o[rt][DT] accumulates each
+  // row's sum of the (bf16) weights on the matrix cores, in every element.
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
   float m[2] = {kNegBig, kNegBig};
-  float l[2] = {0.0f, 0.0f};
-  f32x4_t o[2][C::DT];
+  f32x4_t o[2][C::DT + 1];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt <= C::DT; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int wave_tok_first = tok0 + (w * 32) / G;
   const int wave_tok_last = min(tok0 + (w * 32 + 31) / G, n - 1);
-  const int vis_min = a.causal ? min(L, c + wave_tok_first + 1) : L;   // keys every row of the wave sees
   const int lim0 = a.causal ? min(L, c + row_tok[0] + 1) : L;
   const int lim1 = a.causal ? min(L, c + row_tok[1] + 1) : L;
 
@@ -203,49 +232,92 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
     return __builtin_amdgcn_readfirstlane(s_bt[b - cur_win * kBtCache]);
   };
 
-  // This thread's u-th 16-byte load of a 64-key tile laid out row-major: a
-  // wave's 1 KiB never straddles two cache blocks.
-  // Loads are issued unconditionally (a tile index past the end reloads the
-  // last tile) so the wait before each LDS store counts only older loads.
-  auto load_regs = [&](int kt_req, u32x4_t (&ks)[C::LPT], u32x4_t (&vs)[C::LPT]) {
-    const int kt = min(kt_req, kt_end - 1);
+  // Copy tile kt of the key range into LDS stage `buf` (this wave: block w of
+  // the tile).  Each copy goes through a buffer resource for one cache block
+  // whose range ends at the sequence's last token, so rows past it read as
+  // zero.  A tile past the end is not copied (it is never computed).
+  const int dsel = lane >> 5, vr2 = (lane & 31) >> 1, vh = lane & 1;
+  auto dma_tile = [&](int kt, int buf) {
+    if (kt >= kt_end) return;
     const int win = kt * (kKeys / kBlock) / kBtCache;   // a tile never straddles two windows
     if (win != cur_win) {
       cur_win = win;
       fill_window(win);
       __syncthreads();
     }
+    const int blk = kt * (kKeys / kBlock) + w / kWavesPerBlock;
+    const int part = w % kWavesPerBlock;   // with two waves per block: 0 copies K, 1 copies V
+    const int rows = __builtin_amdgcn_readfirstlane(blk < nblk ? min(max(L - blk * kBlock, 0), kBlock) : 0);
+    const int bid = rows > 0 ? block_id(blk) : 0;
+    const size_t off = (size_t)bid * block_stride;
+    const u32x4_t rk = rsrc_words(kc + off, rows * C::ROW);
+    const u32x4_t rv = rsrc_words(vc + off, rows * C::ROW);
+    const int b = w / kWavesPerBlock;
+    if (kWavesPerBlock == 1 || part == 0) {   // the block's K pieces
+      uint8_t* kdst = lds_stage + buf * C::BUF + b * C::KS * 1024;
 #pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      const int wave_off = u * 4096 + w * 1024;          // uniform
-      const int blk = kt * (kKeys / kBlock) + wave_off / C::TILE;
-      const int rows = __builtin_amdgcn_readfirstlane(blk < nblk ? min(max(L - blk * kBlock, 0), kBlock) : 0);
-      const int bid = rows > 0 ? block_id(blk) : 0;
-      const size_t off = (size_t)bid * block_stride;
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, rows * C::ROW);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, rows * C::ROW);
-      const int in_tile = wave_off % C::TILE + lane * 16;
-      ks[u] = buf_ld16v(rk, in_tile);
-      vs[u] = buf_ld16v(rv, in_tile);
+      for (int ks = 0; ks < C::KS; ++ks) lds_copy16(rk, kdst + ks * 1024, lr * C::ROW + ks * 64 + lq * 16);
+    }
+    if (kWavesPerBlock == 1 || part == 1) {   // its V pieces
+      uint8_t* vdst = lds_stage + buf * C::BUF + C::KBUF + b * (C::DT / 2) * 1024;
+#pragma unroll
+      for (int dp = 0; dp < C::DT / 2; ++dp)
+        lds_copy16(rv, vdst + dp * 1024, vr2 * C::ROW + (2 * dp + dsel) * 32 + vh * 16);
     }
   };
-  auto store_lds = [&](int buf, const u32x4_t (&ks)[C::LPT], const u32x4_t (&vs)[C::LPT]) {
-    lds_u8* kl = lds + buf * C::BUF;
-    lds_u8* vl = kl + C::KBUF;
+
+  // Per-lane LDS addresses of the K and V fragments; every fragment read is
+  // one of these plus an immediate offset.
+  // (Both stages' offsets fit the 16-bit immediate: at most 65024 bytes at D = 128.)
+  const lds_u8* k_lane = lds + lane * 16;
+  const lds_u8* v_lane = lds + C::KBUF + (4 * lq + (lr >> 2)) * 32 + (lr & 3) * 8;
+
+  // Online softmax of one tile's scores s (raw), weights to bf16 P^T
+  // fragments.  Keys at or past a row's visible limit get score -inf, by one
+  // compare against a per-row threshold and one select per score, only in
+  // lanes that hold such keys (one code path: the register allocation stays
+  // tight).
+  auto softmax_tile = [&](f32x4_t (&s)[2][4], int key0, bf16x8_t (&pb)[2][2]) {
 #pragma unroll
-    for (int u = 0; u < C::LPT; ++u) {
-      const int off = u * 4096 + w * 1024 + lane * 16;
-      const int key = off / C::ROW, colb = off % C::ROW;
-      *reinterpret_cast<lds_u32x4*>(kl + key * C::KSTR + colb) = ks[u];
-      *reinterpret_cast<lds_u32x4*>(vl + key * C::VSTR + colb) = vs[u];
+    for (int rt = 0; rt < 2; ++rt) {
+      const int t = (rt == 0 ? lim0 : lim1) - key0 - lq * 4;   // key kt16 * 16 + e of this lane is visible iff < t
+      if (t < 3 * 16 + 4) {   // some key of this lane is not visible (diagonal and last tiles)
+#pragma unroll
+        for (int kt16 = 0; kt16 < 4; ++kt16)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[rt][kt16][e] = kt16 * 16 + e < t ? s[rt][kt16][e] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt16 = 0; kt16 < 4; ++kt16)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, s[rt][kt16][e]);
+      const float mxs = mx * cs;   // -inf when this lane sees no key of the tile
+      if (__any(mxs > m[rt] + kRescaleSlack)) {   // rare after a row's first tile
+        float rm = fmaxf(mxs, __shfl_xor(mxs, 16));
+        rm = fmaxf(rm, __shfl_xor(rm, 32));
+        const float mn = fmaxf(m[rt], rm);
+        const float alpha = fast_exp2(m[rt] - mn);
+        m[rt] = mn;
+#pragma unroll
+        for (int dt = 0; dt <= C::DT; ++dt) o[rt][dt] *= alpha;
+      }
+      auto weight = [&](int kt16, int e) { return fast_exp2(fmaf(s[rt][kt16][e], cs, -m[rt])); };
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pb[rt][ks2][e] = static_cast<__bf16>(weight(2 * ks2, e));
+          pb[rt][ks2][4 + e] = static_cast<__bf16>(weight(2 * ks2 + 1, e));
+        }
     }
   };
 
   auto compute = [&](int kt, int buf) {
     const int key0 = kt * kKeys;
     if (a.causal && key0 > c + wave_tok_last) return;   // past every row of this wave
-    const lds_u8* kl = lds + buf * C::BUF;
-    const lds_u8* vl = kl + C::KBUF;
+    const lds_u8* kl = k_lane + buf * C::BUF;
+    const lds_u8* vl = v_lane + buf * C::BUF;
     f32x4_t s[2][4];
 #pragma unroll
     for (int kt16 = 0; kt16 < 4; ++kt16) {
@@ -253,90 +325,56 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
       s[1][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t kf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(
-            kl + (kt16 * 16 + lr) * C::KSTR + ks * 64 + lq * 16);
+        const bf16x8_t kf =
+            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(kl + (kt16 * C::KS + ks) * 1024);
         s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
         s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
       }
+      if (kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
     }
-    const bool full = key0 + kKeys <= vis_min;
     bf16x8_t pb[2][2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int lim = rt == 0 ? lim0 : lim1;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt16 = 0; kt16 < 4; ++kt16)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = s[rt][kt16][e] * a.scale_log2;
-          if (!full) v = (key0 + kt16 * 16 + lq * 4 + e) < lim ? v : -INFINITY;
-          s[rt][kt16][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      if (__any(mx > m[rt] + kRescaleSlack)) {   // rare after a row's first tile
-        float rm = fmaxf(mx, __shfl_xor(mx, 16));
-        rm = fmaxf(rm, __shfl_xor(rm, 32));
-        const float mn = fmaxf(m[rt], rm);
-        const float alpha = fast_exp2(m[rt] - mn);
-        m[rt] = mn;
-        l[rt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) o[rt][dt] *= alpha;
-      }
-      float part[4];
-#pragma unroll
-      for (int kt16 = 0; kt16 < 4; ++kt16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[rt][kt16][e] = fast_exp2(s[rt][kt16][e] - m[rt]);
-        part[kt16] = (s[rt][kt16][0] + s[rt][kt16][1]) + (s[rt][kt16][2] + s[rt][kt16][3]);
-      }
-      l[rt] += (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pb[rt][ks2][e] = static_cast<__bf16>(s[rt][2 * ks2][e]);
-          pb[rt][ks2][4 + e] = static_cast<__bf16>(s[rt][2 * ks2 + 1][e]);
-        }
-    }
+    softmax_tile(s, key0, pb);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const lds_u8* vp = vl + (ks2 * 32 + 4 * lq + (lr >> 2)) * C::VSTR + (dt * 16 + 4 * (lr & 3)) * 2;
+        // keys 32 ks2 + 4 lq + lr / 4 (block 2 ks2) and 16 further (block 2 ks2 + 1)
+        const lds_u8* vp = vl + (2 * ks2 * (C::DT / 2) + dt / 2) * 1024 + (dt & 1) * 512;
         const s16x4_t v0 = lds_read_tr(vp);
-        const s16x4_t v1 = lds_read_tr(vp + 16 * C::VSTR);
+        const s16x4_t v1 = lds_read_tr(vp + (C::DT / 2) * 1024);
         const bf16x8_t vf = __builtin_bit_cast(
             bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
         o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
         o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
       }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      o[0][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ks2], o[0][C::DT], 0, 0, 0);
+      o[1][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][ks2], o[1][C::DT], 0, 0, 0);
+    }
   };
 
-  // Pipeline: tile kt+1 is loaded into registers while tile kt is computed
-  // from LDS, then stored to the other LDS stage.
-  u32x4_t kr[C::LPT], vr[C::LPT];
-  load_regs(kt0, kr, vr);
-  store_lds(0, kr, vr);
+  // Pipeline: tile kt+1 is copied into the other LDS stage while tile kt is
+  // computed; each wave then waits for its own copies, and the barrier makes
+  // every wave's copies visible (and frees the stage just read for refill).
+  dma_tile(kt0, 0);
+  PA_VM_WAIT(0);
   __syncthreads();
   for (int kt = kt0; kt < kt_end; kt += 2) {
-    load_regs(kt + 1, kr, vr);
+    dma_tile(kt + 1, 1);
     compute(kt, 0);
-    store_lds(1, kr, vr);
+    PA_VM_WAIT(0);
     __syncthreads();
     if (kt + 1 >= kt_end) break;
-    load_regs(kt + 2, kr, vr);
+    dma_tile(kt + 2, 0);
     compute(kt + 1, 1);
-    store_lds(0, kr, vr);
+    PA_VM_WAIT(0);
     __syncthreads();
   }
 
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    float lt = l[rt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = o[rt][C::DT][0];   // the row's weight sum (ones tile)
     if (row_tok[rt] >= n) continue;
     if (split) {
       // Piece it.p of this row: unnormalised O^T columns, max (base 2) and sum.
@@ -366,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs pk) {
 // row, each owning half of the head dim.  Pieces are combined in ascending
 // order with the log-sum-exp rule, so the result is deterministic.
 template <int D>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs pk) {
+__global__ __launch_bounds__(2 * kRowsPerWG) void prefill_merge_kernel(PrefillArgs pk) {
   constexpr int HALF = D / 2;
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
@@ -466,17 +504,17 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   PrefillArgs k{a, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
   int mark = trace_begin(s);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)wgs), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
   else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)wgs), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
   trace_end(s, mark, "prefill");
   pa_status st = launch_status("pa_forward (prefill)");
   if (st != PA_OK || pp.pieces <= 1) return st;
   mark = trace_begin(s);
   if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3((unsigned)tiles), dim3(2 * kRowsPerWG), 0, s, k);
   else
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, s, k);
+    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3((unsigned)tiles), dim3(2 * kRowsPerWG), 0, s, k);
   trace_end(s, mark, "prefill_merge");
   return launch_status("pa_forward (prefill merge)");
 }
