@@ -16,8 +16,11 @@ pool.  Prints one JSON line on stdout; progress goes to stderr.
 Two timed regions of --steps steps each follow --warmup untimed steps: the
 first (no instrumentation) gives `value` and `ms_per_step`; the second runs
 with the library's per-kernel HIP-event tracing on and gives the kernel
-durations behind `roofline`.  `--copy-probe` instead runs only the known-size
-copy used to calibrate rocprofv3's HBM byte counters.
+durations behind `roofline`.  Side legs: the prefill chunks of the mixed
+super-batch (MFMA utilisation), a step launched call by call vs replayed from
+a HIP graph (`graph`, tiny and batched decode), the host allocator's replay
+rate, and the CPU oracle (`cpu_baseline`).  `--copy-probe` instead runs only
+the known-size copy used to calibrate rocprofv3's HBM byte counters.
 """
 
 import argparse
@@ -287,6 +290,50 @@ def mean(xs):
     return float(np.mean(xs)) if xs else None
 
 
+def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
+    """One serving step (pa_copy_blocks + pa_write_kv + pa_forward) per launch vs replayed from a HIP graph.
+
+    Both are timed back to back over `steps` steps on a side stream with HIP
+    events; the replay's output bits must equal the eager step's.
+    """
+    wl = workloads.named(name)
+    run = DeviceRun(wl, fill="zero")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            run.step()
+    torch.cuda.synchronize()
+    want = run.host(run.out).copy()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run.step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not np.array_equal(run.host(run.out), want):
+        raise RuntimeError(f"graph replay of {name} differs from the eager step")
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):
+            for _ in range(5):
+                fn()
+            a.record(side)
+            for _ in range(steps):
+                fn()
+            b.record(side)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    eager_us = timed(run.step)
+    graph_us = timed(graph.replay)
+    del graph, run
+    torch.cuda.empty_cache()
+    return {"workload": name, "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
+            "speedup": round(eager_us / graph_us, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -296,6 +343,7 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for >= 1 GB of K/V)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph step-replay leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -407,6 +455,11 @@ def main():
                           "kernel_ms": {k: round(mean(v), 5) for k, v in pper.items()}}
         del prun
         torch.cuda.empty_cache()
+
+    if not args.no_graph:
+        log("graph leg: one step per launch vs replayed from a HIP graph (tiny and batched decode)")
+        res["graph"] = [graph_leg(pa, torch, workloads, DeviceRun, n, max(20, args.steps))
+                        for n in ("tiny_decode", "batched_decode")]
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl)

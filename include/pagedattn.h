@@ -205,6 +205,22 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      const pa_cache_desc* c, float scale, int32_t causal,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * HIP graphs.  pa_write_kv, pa_copy_blocks and pa_forward may be recorded into
+ * a HIP graph (stream capture on `stream`), so that a whole serving step
+ * replays as one launch ([ART] forward-pass paragraph: the step's kernels are
+ * replayed from a captured graph to save launch overhead).  On the fast path
+ * none of them allocates, synchronises, writes memory with a memset or reads
+ * device memory on the host.  A captured call keeps its host arguments
+ * (pointers, sizes, max_seq_len, max_query_len, scale, causal, and the
+ * environment knobs as read at capture); device data -- q, the caches, block
+ * tables, slot mappings, seq_lens, query_start_loc, cached_lens -- are read
+ * at each replay, so a step may be replayed after its inputs are updated in
+ * place within the captured sizes (e.g. lengths that grew, up to the captured
+ * max_seq_len).  While the stream is being captured, tracing records nothing
+ * and check mode (PA_CHECK=1) returns PA_ERR_ARG.
+ */
+
 /* ------------------------------------------------------------------------ */
 /* Tracing (instrumentation; not part of the method)                         */
 /* ------------------------------------------------------------------------ */

@@ -93,6 +93,7 @@ extern "C" pa_status pa_write_kv(const void* k, const void* v, void* k_cache, vo
   hipStream_t s = (hipStream_t)stream;
   const int64_t num_slots = (int64_t)c->num_blocks * kBlock;
   if (check_mode()) {
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_write_kv: PA_CHECK=1 cannot run on a stream being captured");
     std::vector<int64_t> h(num_tokens);
     if (hipMemcpyAsync(h.data(), slot_mapping, sizeof(int64_t) * num_tokens, hipMemcpyDeviceToHost, s) !=
             hipSuccess ||
@@ -129,6 +130,7 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
   if (!k_cache || !v_cache || !pairs) return fail(PA_ERR_ARG, "pa_copy_blocks: NULL device pointer");
   hipStream_t s = (hipStream_t)stream;
   if (check_mode()) {
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_copy_blocks: PA_CHECK=1 cannot run on a stream being captured");
     std::vector<int32_t> h(2 * (size_t)num_pairs);
     if (hipMemcpyAsync(h.data(), pairs, sizeof(int32_t) * h.size(), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)

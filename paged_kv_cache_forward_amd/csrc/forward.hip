@@ -113,6 +113,7 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (check_mode()) {
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_forward: PA_CHECK=1 cannot run on a stream being captured");
     st = validate_metadata(block_tables, block_table_stride, seq_lens, query_start_loc, cached_lens, num_seqs,
                            num_tokens, max_seq_len, max_query_len, c->num_blocks, s);
     if (st != PA_OK) return st;

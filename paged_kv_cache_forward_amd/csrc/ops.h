@@ -14,8 +14,13 @@ inline int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
 pa_status check_desc(const pa_cache_desc* c, const char* who);
 pa_status launch_status(const char* who);
 
+// True while `s` is being captured into a HIP graph (calls that would
+// synchronise or read device memory on the host refuse to run then).
+bool stream_capturing(hipStream_t s);
+
 // Tracing: bracket a kernel launch with trace_begin / trace_end on its stream
-// (no-ops unless pa_trace_enable(1)); `kernel` must have static storage.
+// (no-ops unless pa_trace_enable(1), and while the stream is being captured);
+// `kernel` must have static storage.
 int trace_begin(hipStream_t s);
 void trace_end(hipStream_t s, int mark, const char* kernel);
 

@@ -43,8 +43,14 @@ hipEvent_t take_event() {
 
 }  // namespace
 
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st != hipStreamCaptureStatusNone;
+}
+
 int trace_begin(hipStream_t s) {
   if (!g_on.load(std::memory_order_relaxed)) return -1;
+  if (stream_capturing(s)) return -1;   // an event recorded in a graph fires only at replay
   std::lock_guard<std::mutex> lk(g_mu);
   hipEvent_t e = take_event();
   if (e == nullptr || hipEventRecord(e, s) != hipSuccess) return -1;
