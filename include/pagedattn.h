@@ -313,6 +313,57 @@ int32_t pa_block_refcount(const pa_alloc* a, int32_t block);
 /* Free list, head first: copies up to cap ids into out; *n receives its length. */
 pa_status pa_alloc_free_list(const pa_alloc* a, int32_t* out, int32_t cap, int32_t* n);
 
+/*
+ * Prefix caching.  [ART] prefix-caching paragraph: the engine hashes blocks
+ * of tokens and keeps them; a request that starts with the same tokens finds
+ * the matching blocks and reuses their K/V instead of recomputing them.
+ * [HADA] bullet "Prefix Caching".  Host-side only: a hit gives the new
+ * sequence the existing physical blocks, and the caller's prefill then runs
+ * with cached_lens = *n_cached.
+ *
+ * Rules (exact; both the library and its reference follow them):
+ *   - Chained block hash: for full block b of a token sequence (tokens
+ *     B*b .. B*b+B-1), h(b) = FNV-1a 64 of the 8 little-endian bytes of
+ *     h(b-1) followed by the 4 little-endian bytes of each token id, with
+ *     h(-1) = 0xcbf29ce484222325 (the FNV-1a 64 offset basis; FNV prime
+ *     0x100000001b3).  A block's hash thus names the whole prefix it ends.
+ *   - A registered block carries its hash, its parent's hash and its B
+ *     tokens; the cache maps a hash to at most one registered block.  A
+ *     lookup hits only when the hash, the parent hash and every token match.
+ *   - pa_prefix_register(seq, tokens, n): for each full block b of the first
+ *     n tokens of seq (n <= the sequence's length), in order, that is not
+ *     registered yet: if no block is registered under h(b), register it;
+ *     otherwise leave it unregistered (the sequence keeps its own copy).
+ *   - pa_prefix_lookup(tokens, n): creates a sequence (the next id) holding
+ *     the longest run of full blocks b = 0, 1, ... that hit, leaving at least
+ *     one token uncached (b < (n - 1) / B).  Each hit block's refcount rises
+ *     by one; a hit block with refcount 0 is taken out of the free list.
+ *     *n_cached = B * hits is the sequence's length; the caller appends the
+ *     other n - *n_cached tokens (pa_seq_append) and runs their prefill.
+ *   - A registered block whose refcount falls to 0 stays registered at the
+ *     free-list tail; when the free list hands it out again it is first
+ *     unregistered (evicted).  Blocks registered after it stay: a lookup
+ *     reaches them only through a block registered under the same hash,
+ *     i.e. after the same tokens, so their K/V stay valid.
+ *   - A registered block is never written while registered: an append that
+ *     would write into one without copying it (a fork shared it part-way and
+ *     the other holders have let go) unregisters it first (an eviction).
+ * tokens: host int32 [n_tokens].  Errors: PA_ERR_ARG (NULL arguments,
+ * unknown sequence, n_tokens outside [0, length] for register, < 0 for lookup).
+ */
+pa_status pa_prefix_register(pa_alloc* a, int32_t seq, const int32_t* tokens, int32_t n_tokens);
+pa_status pa_prefix_lookup(pa_alloc* a, const int32_t* tokens, int32_t n_tokens, int32_t* seq_id,
+                           int32_t* n_cached);
+
+typedef struct {
+  int64_t blocks_registered;  /* blocks currently in the cache */
+  int64_t registered_free;    /* of those, refcount 0 (on the free list) */
+  int64_t lookups;            /* pa_prefix_lookup calls */
+  int64_t hit_blocks;         /* blocks reused by them */
+  int64_t evictions;          /* registered blocks dropped from the cache */
+} pa_prefix_stats_t;
+pa_status pa_prefix_stats(const pa_alloc* a, pa_prefix_stats_t* s);
+
 #ifdef __cplusplus
 }
 #endif

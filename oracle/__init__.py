@@ -28,7 +28,9 @@ Pages followed (cited by title and section throughout the package):
 Modules:
   numerics   -- widening of stored element formats (fp32, bf16 bits) to float64
   blocks     -- block counts and unused-slot accounting (closed forms)
-  alloc      -- RefAllocator: block allocator with refcounts and copy-on-write
+  alloc      -- RefAllocator: block allocator with refcounts, copy-on-write
+                and the prefix cache
+  prefix     -- chained FNV-1a 64 block hashes for prefix caching
   cache      -- cache write through a slot mapping; whole-block copies
   attention  -- paged attention over a varlen super-batch; split/merge pieces
 
@@ -40,6 +42,7 @@ float64 library attention routine); none is "parity unpinned".
 from .numerics import to_f64
 from .blocks import blocks_needed, unused_slots, unused_fraction
 from .alloc import RefAllocator, OutOfBlocks
+from .prefix import fnv1a64, block_hash, chain
 from .cache import ref_write_kv, ref_copy_blocks
 from .attention import (
     gather_logical,
@@ -56,6 +59,9 @@ __all__ = [
     "unused_fraction",
     "RefAllocator",
     "OutOfBlocks",
+    "fnv1a64",
+    "block_hash",
+    "chain",
     "ref_write_kv",
     "ref_copy_blocks",
     "gather_logical",

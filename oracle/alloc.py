@@ -30,11 +30,29 @@ Readings taken where the pages are silent (each is listed in the design doc):
     needs, it raises OutOfBlocks and changes nothing.
   * ``free(seq)`` drops the refcount of each of the sequence's blocks in table
     order, returning those that reach zero to the tail of the free list.
+
+Prefix caching ([ART] paragraph on prefix caching: blocks of tokens are hashed
+and kept; a request starting with the same tokens reuses them), readings:
+  * Block hashes chain as in ``oracle.prefix``.  A registered block carries its
+    hash, its parent's hash and its tokens; the cache maps a hash to at most
+    one block; a lookup hits only if hash, parent hash and tokens all match.
+  * ``prefix_register(seq, tokens, n)`` registers, in order, each full block
+    of the first n tokens that is not registered yet, unless another block is
+    already registered under its hash.
+  * ``prefix_lookup(tokens, n)`` creates a sequence holding the longest run of
+    hitting full blocks from the start, leaving at least one token uncached
+    (b < (n - 1) // B); each hit block's refcount rises by one, and a hit
+    block with refcount 0 leaves the free list.  Returns (seq, B * hits).
+  * A registered block freed to refcount 0 stays registered at the free-list
+    tail; handing it out again (append) unregisters it first (eviction).
+  * An append that writes into a registered block in place (no copy due)
+    unregisters it first (eviction): cached blocks are never overwritten.
 """
 
 from collections import deque
 
 from .blocks import blocks_needed
+from .prefix import FNV_OFFSET, block_hash
 
 
 class OutOfBlocks(Exception):
@@ -55,6 +73,21 @@ class RefAllocator:
         self.tables = {}   # seq id -> list of physical block ids (logical order)
         self.lengths = {}  # seq id -> tokens stored
         self.next_id = 0
+        self.reg = {}      # registered block -> (hash, parent hash, tokens)
+        self.cache = {}    # hash -> registered block
+        self.lookups = 0
+        self.hit_blocks = 0
+        self.evictions = 0
+
+    def _unregister(self, b):
+        if b in self.reg:   # eviction: the block is about to be written
+            del self.cache[self.reg.pop(b)[0]]
+            self.evictions += 1
+
+    def _pop_free(self):
+        b = self.free.popleft()
+        self._unregister(b)
+        return b
 
     # -- sequence lifetime -------------------------------------------------
     def create(self):
@@ -105,13 +138,15 @@ class RefAllocator:
         copied = set()
         for p in range(start, start + n_tokens):
             j = p // B
+            if p % B != 0 and j not in copied and self.refcount[table[j]] == 1:
+                self._unregister(table[j])   # written in place: leaves the cache
             if p % B == 0:
-                fresh = self.free.popleft()
+                fresh = self._pop_free()
                 self.refcount[fresh] = 1
                 table.append(fresh)
             elif j not in copied and self.refcount[table[j]] > 1:
                 old = table[j]
-                fresh = self.free.popleft()
+                fresh = self._pop_free()
                 self.refcount[fresh] = 1
                 self.refcount[old] -= 1
                 table[j] = fresh
@@ -129,6 +164,58 @@ class RefAllocator:
             if self.refcount[b] == 0:
                 self.free.append(b)
         del self.lengths[seq]
+
+    # -- prefix caching ----------------------------------------------------
+    def prefix_register(self, seq, tokens, n_tokens=None):
+        n = len(tokens) if n_tokens is None else n_tokens
+        if seq not in self.tables:
+            raise KeyError(f"unknown sequence {seq}")
+        if not 0 <= n <= self.lengths[seq]:
+            raise ValueError("n_tokens must lie in [0, len(seq)]")
+        B = self.block_size
+        parent = FNV_OFFSET
+        for b in range(n // B):
+            blk_tokens = tuple(int(t) for t in tokens[b * B:(b + 1) * B])
+            h = block_hash(parent, blk_tokens)
+            blk = self.tables[seq][b]
+            if blk not in self.reg and h not in self.cache:
+                self.reg[blk] = (h, parent, blk_tokens)
+                self.cache[h] = blk
+            parent = h
+
+    def prefix_lookup(self, tokens, n_tokens=None):
+        n = len(tokens) if n_tokens is None else n_tokens
+        if n < 0:
+            raise ValueError("n_tokens must be >= 0")
+        B = self.block_size
+        hits, parent = [], FNV_OFFSET
+        for b in range(max(n - 1, 0) // B):
+            blk_tokens = tuple(int(t) for t in tokens[b * B:(b + 1) * B])
+            h = block_hash(parent, blk_tokens)
+            blk = self.cache.get(h)
+            if blk is None or self.reg[blk][1] != parent or self.reg[blk][2] != blk_tokens:
+                break
+            hits.append(blk)
+            parent = h
+        for blk in hits:
+            if self.refcount[blk] == 0:
+                self.free.remove(blk)
+            self.refcount[blk] += 1
+        sid = self.create()
+        self.tables[sid] = hits
+        self.lengths[sid] = len(hits) * B
+        self.lookups += 1
+        self.hit_blocks += len(hits)
+        return sid, len(hits) * B
+
+    def prefix_stats(self):
+        return {
+            "blocks_registered": len(self.reg),
+            "registered_free": sum(1 for b in self.reg if self.refcount[b] == 0),
+            "lookups": self.lookups,
+            "hit_blocks": self.hit_blocks,
+            "evictions": self.evictions,
+        }
 
     # -- inspection --------------------------------------------------------
     def block_table(self, seq):

@@ -51,6 +51,11 @@ class AllocStats(ctypes.Structure):
                  "tokens_logical", "slots_logical", "slots_physical")]
 
 
+class PrefixStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("blocks_registered", "registered_free", "lookups", "hit_blocks", "evictions")]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
 _pdesc = ctypes.POINTER(CacheDesc)
@@ -75,6 +80,9 @@ _SIGS = {
     "pa_alloc_stats": (_i32, [_vp, ctypes.POINTER(AllocStats)]),
     "pa_block_refcount": (_i32, [_vp, _i32]),
     "pa_alloc_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
+    "pa_prefix_register": (_i32, [_vp, _i32, _pi32, _i32]),
+    "pa_prefix_lookup": (_i32, [_vp, _pi32, _i32, _pi32, _pi32]),
+    "pa_prefix_stats": (_i32, [_vp, ctypes.POINTER(PrefixStats)]),
 }
 
 _LIB = None
@@ -309,3 +317,23 @@ class BlockAllocator:
         out = np.empty(max(n.value, 1), dtype=np.int32)
         _check(_load().pa_alloc_free_list(self._h, out.ctypes.data_as(_pi32), n.value, ctypes.byref(n)))
         return out[:n.value].tolist()
+
+    # prefix caching
+    def prefix_register(self, seq, tokens, n_tokens=None):
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(tok) if n_tokens is None else n_tokens
+        _check(_load().pa_prefix_register(self._h, seq, tok.ctypes.data_as(_pi32), n))
+
+    def prefix_lookup(self, tokens, n_tokens=None):
+        """Returns (new sequence id, tokens already cached)."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = len(tok) if n_tokens is None else n_tokens
+        sid, cached = ctypes.c_int32(), ctypes.c_int32()
+        _check(_load().pa_prefix_lookup(self._h, tok.ctypes.data_as(_pi32), n, ctypes.byref(sid),
+                                        ctypes.byref(cached)))
+        return sid.value, cached.value
+
+    def prefix_stats(self):
+        st = PrefixStats()
+        _check(_load().pa_prefix_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in PrefixStats._fields_}

@@ -11,13 +11,18 @@
 // of blocks is the point where a scheduler preempts, so an append that cannot
 // be satisfied fails without changing anything.
 //
-// The exact rules (free-list order, id assignment, copy trigger) are stated in
-// include/pagedattn.h.  Everything here is single-threaded per allocator and
-// touches no GPU state.
+// Prefix caching: "Внутреннее устройство vLLM" (artificials.ru), paragraph on
+// prefix caching: blocks of tokens are hashed and kept, and a request that
+// begins with the same tokens reuses the matching blocks.
+//
+// The exact rules (free-list order, id assignment, copy trigger, block hash,
+// registration and eviction) are stated in include/pagedattn.h.  Everything
+// here is single-threaded per allocator and touches no GPU state.
 #include <algorithm>
 #include <cstdint>
-#include <deque>
+#include <list>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedattn.h"
@@ -26,8 +31,21 @@
 struct pa_alloc {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::deque<int32_t> free_list;
+  // Free list (head = next block handed out); a prefix-cache hit can take a
+  // block from the middle, hence a list with each member's position.
+  std::list<int32_t> free_list;
+  std::vector<std::list<int32_t>::iterator> free_pos;
+  std::vector<char> is_free;
   std::vector<int32_t> refcount;
+  // Prefix cache: hash -> registered block; per block its hash, parent hash, tokens.
+  struct Reg {
+    bool on = false;
+    uint64_t hash = 0, parent = 0;
+    std::vector<int32_t> tokens;
+  };
+  std::vector<Reg> reg;
+  std::unordered_map<uint64_t, int32_t> cache;
+  int64_t lookups = 0, hit_blocks = 0, evictions = 0;
   struct Seq {
     bool live = false;
     int32_t length = 0;
@@ -47,6 +65,47 @@ struct pa_alloc {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+static void push_free(pa_alloc* a, int32_t b) {
+  a->free_pos[b] = a->free_list.insert(a->free_list.end(), b);
+  a->is_free[b] = 1;
+}
+
+static void unregister(pa_alloc* a, int32_t b) {
+  pa_alloc::Reg& r = a->reg[b];
+  if (!r.on) return;
+  auto it = a->cache.find(r.hash);
+  if (it != a->cache.end() && it->second == b) a->cache.erase(it);
+  r.on = false;
+  r.tokens.clear();
+  a->evictions += 1;
+}
+
+// Head of the free list, for a write: a registered block is evicted first.
+static int32_t pop_free(pa_alloc* a) {
+  const int32_t b = a->free_list.front();
+  a->free_list.pop_front();
+  a->is_free[b] = 0;
+  unregister(a, b);
+  return b;
+}
+
+// FNV-1a 64 (offset basis 0xcbf29ce484222325, prime 0x100000001b3) of the
+// parent hash's 8 little-endian bytes, then each token id's 4 little-endian bytes.
+static uint64_t block_hash(uint64_t parent, const int32_t* tok, int32_t n) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&](uint8_t byte) {
+    h ^= byte;
+    h *= 0x100000001b3ull;
+  };
+  for (int k = 0; k < 8; ++k) mix((uint8_t)(parent >> (8 * k)));
+  for (int32_t t = 0; t < n; ++t) {
+    const uint32_t u = (uint32_t)tok[t];
+    for (int k = 0; k < 4; ++k) mix((uint8_t)(u >> (8 * k)));
+  }
+  return h;
+}
+static constexpr uint64_t kHashRoot = 0xcbf29ce484222325ull;
+
 extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                                      const int32_t* free_order, pa_alloc** out) {
   if (out == nullptr) return pa::fail(PA_ERR_ARG, "pa_alloc_create: out is NULL");
@@ -59,6 +118,9 @@ extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
   a->num_blocks = num_blocks;
   a->block_size = block_size;
   a->refcount.assign(num_blocks, 0);
+  a->free_pos.resize(num_blocks);
+  a->is_free.assign(num_blocks, 0);
+  a->reg.resize(num_blocks);
   if (free_order != nullptr) {
     std::vector<char> seen(num_blocks, 0);
     for (int32_t k = 0; k < num_blocks; ++k) {
@@ -69,10 +131,10 @@ extern "C" pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size,
                         k, b);
       }
       seen[b] = 1;
-      a->free_list.push_back(b);
+      push_free(a, b);
     }
   } else {
-    for (int32_t b = 0; b < num_blocks; ++b) a->free_list.push_back(b);
+    for (int32_t b = 0; b < num_blocks; ++b) push_free(a, b);
   }
   *out = a;
   return PA_OK;
@@ -136,19 +198,19 @@ extern "C" pa_status pa_seq_append(pa_alloc* a, int32_t seq, int32_t n_tokens, i
   if (copies > 0 && (cow_pairs_out == nullptr || cow_cap < copies || n_cow == nullptr))
     return pa::fail(PA_ERR_ARG, "pa_seq_append: a copy-on-write pair is due but cow_cap=%d", cow_cap);
 
-  // Pass 2: apply, position by position.
+  // Pass 2: apply, position by position.  A registered block written in place
+  // (no copy due) leaves the prefix cache first.
+  if (start % B != 0 && copies == 0) unregister(a, s->table[start / B]);
   int32_t ncow = 0;
   for (int64_t p = start; p < end; ++p) {
     const int64_t j = p / B;
     if (p % B == 0) {
-      int32_t fresh = a->free_list.front();
-      a->free_list.pop_front();
+      int32_t fresh = pop_free(a);
       a->refcount[fresh] = 1;
       s->table.push_back(fresh);
     } else if (p == start && copies > 0) {
       int32_t old = s->table[j];
-      int32_t fresh = a->free_list.front();
-      a->free_list.pop_front();
+      int32_t fresh = pop_free(a);
       a->refcount[fresh] = 1;
       a->refcount[old] -= 1;
       s->table[j] = fresh;
@@ -168,7 +230,7 @@ extern "C" pa_status pa_seq_free(pa_alloc* a, int32_t seq) {
   pa_alloc::Seq* s = a->find(seq);
   if (s == nullptr) return pa::fail(PA_ERR_ARG, "pa_seq_free: unknown sequence %d", seq);
   for (int32_t b : s->table) {
-    if (--a->refcount[b] == 0) a->free_list.push_back(b);
+    if (--a->refcount[b] == 0) push_free(a, b);   // a registered block stays registered
   }
   s->table.clear();
   s->table.shrink_to_fit();
@@ -225,5 +287,85 @@ extern "C" pa_status pa_alloc_free_list(const pa_alloc* a, int32_t* out, int32_t
   if (out == nullptr) return PA_OK;
   int32_t k = 0;
   for (auto it = a->free_list.begin(); it != a->free_list.end() && k < cap; ++it) out[k++] = *it;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_prefix_register(pa_alloc* a, int32_t seq, const int32_t* tokens, int32_t n_tokens) {
+  if (a == nullptr) return pa::fail(PA_ERR_ARG, "pa_prefix_register: NULL allocator");
+  pa_alloc::Seq* s = a->find(seq);
+  if (s == nullptr) return pa::fail(PA_ERR_ARG, "pa_prefix_register: unknown sequence %d", seq);
+  if (n_tokens < 0 || n_tokens > s->length)
+    return pa::fail(PA_ERR_ARG, "pa_prefix_register: n_tokens %d outside [0, %d]", n_tokens, s->length);
+  if (n_tokens > 0 && tokens == nullptr) return pa::fail(PA_ERR_ARG, "pa_prefix_register: tokens is NULL");
+  const int32_t B = a->block_size;
+  uint64_t parent = kHashRoot;
+  for (int32_t b = 0; b < n_tokens / B; ++b) {
+    const uint64_t h = block_hash(parent, tokens + (int64_t)b * B, B);
+    const int32_t blk = s->table[b];
+    pa_alloc::Reg& r = a->reg[blk];
+    if (!r.on && a->cache.find(h) == a->cache.end()) {
+      r.on = true;
+      r.hash = h;
+      r.parent = parent;
+      r.tokens.assign(tokens + (int64_t)b * B, tokens + (int64_t)(b + 1) * B);
+      a->cache.emplace(h, blk);
+    }
+    parent = h;
+  }
+  return PA_OK;
+}
+
+extern "C" pa_status pa_prefix_lookup(pa_alloc* a, const int32_t* tokens, int32_t n_tokens, int32_t* seq_id,
+                                      int32_t* n_cached) {
+  if (a == nullptr || seq_id == nullptr || n_cached == nullptr)
+    return pa::fail(PA_ERR_ARG, "pa_prefix_lookup: NULL argument");
+  if (n_tokens < 0) return pa::fail(PA_ERR_ARG, "pa_prefix_lookup: n_tokens %d < 0", n_tokens);
+  if (n_tokens > 0 && tokens == nullptr) return pa::fail(PA_ERR_ARG, "pa_prefix_lookup: tokens is NULL");
+  const int32_t B = a->block_size;
+  const int32_t max_blocks = n_tokens > 0 ? (n_tokens - 1) / B : 0;   // leave at least one token
+  std::vector<int32_t> hits;
+  uint64_t parent = kHashRoot;
+  for (int32_t b = 0; b < max_blocks; ++b) {
+    const int32_t* tk = tokens + (int64_t)b * B;
+    const uint64_t h = block_hash(parent, tk, B);
+    auto it = a->cache.find(h);
+    if (it == a->cache.end()) break;
+    const pa_alloc::Reg& r = a->reg[it->second];
+    if (r.parent != parent || !std::equal(r.tokens.begin(), r.tokens.end(), tk)) break;
+    hits.push_back(it->second);
+    parent = h;
+  }
+  for (int32_t blk : hits) {
+    if (a->refcount[blk] == 0 && a->is_free[blk]) {
+      a->free_list.erase(a->free_pos[blk]);
+      a->is_free[blk] = 0;
+    }
+    a->refcount[blk] += 1;
+  }
+  a->seqs.emplace_back();
+  pa_alloc::Seq& c = a->seqs.back();
+  c.live = true;
+  c.length = (int32_t)hits.size() * B;
+  c.table = std::move(hits);
+  a->lookups += 1;
+  a->hit_blocks += (int64_t)c.table.size();
+  *seq_id = (int32_t)a->seqs.size() - 1;
+  *n_cached = c.length;
+  return PA_OK;
+}
+
+extern "C" pa_status pa_prefix_stats(const pa_alloc* a, pa_prefix_stats_t* st) {
+  if (a == nullptr || st == nullptr) return pa::fail(PA_ERR_ARG, "pa_prefix_stats: NULL argument");
+  int64_t reg = 0, reg_free = 0;
+  for (int32_t b = 0; b < a->num_blocks; ++b) {
+    if (!a->reg[b].on) continue;
+    reg += 1;
+    reg_free += a->refcount[b] == 0;
+  }
+  st->blocks_registered = reg;
+  st->registered_free = reg_free;
+  st->lookups = a->lookups;
+  st->hit_blocks = a->hit_blocks;
+  st->evictions = a->evictions;
   return PA_OK;
 }

@@ -112,3 +112,77 @@ def test_out_of_blocks_atomic_and_errors():
     assert (a2.free_list(), a2.block_table(ch), a2.refcount(1)) == before
     slots, pairs = a2.append(ch, 1)
     assert pairs == [(1, 2)]
+
+
+def same_prefix_state(lib_a, ref):
+    assert lib_a.prefix_stats() == ref.prefix_stats()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_prefix_traces_bit_exact(seed):
+    """Lookups, registrations, appends, forks and frees over a few shared prompts
+    drawn from a small vocabulary, so that hits, misses, evictions and in-place
+    writes into registered blocks all occur."""
+    pa = ensure_library()
+    rng = np.random.default_rng(100 + seed)
+    nb = int(rng.integers(12, 40))
+    B = 16
+    order = rng.permutation(nb)
+    a = pa.BlockAllocator(nb, B, order)
+    r = oracle.RefAllocator(nb, B, order)
+    prompts = [rng.integers(0, 20, size=int(rng.integers(1, 90))).tolist() for _ in range(4)]
+    live = []          # (lib id, ref id, planned tokens; the first r.length(ref id) are stored)
+    for step in range(400):
+        op = int(rng.integers(0, 8))
+        if op == 0 or not live:
+            toks = prompts[int(rng.integers(0, 4))] + rng.integers(0, 20, size=int(rng.integers(0, 30))).tolist()
+            sl, cl = a.prefix_lookup(toks)
+            sr, cr = r.prefix_lookup(toks)
+            assert cl == cr
+            live.append((sl, sr, toks))
+        elif op == 1:
+            sl, sr, toks = live[int(rng.integers(0, len(live)))]
+            k = int(rng.integers(0, r.length(sr) + 1))
+            live.append((a.fork(sl, k), r.fork(sr, k), list(toks[:k])))
+        elif op in (2, 3):
+            i = int(rng.integers(0, len(live)))
+            sl, sr, toks = live[i]
+            n = int(rng.integers(0, 40))
+            try:
+                want = r.append(sr, n)
+            except oracle.OutOfBlocks:
+                with pytest.raises(pa.OutOfBlocks):
+                    a.append(sl, n)
+            else:
+                slots, pairs = a.append(sl, n)
+                assert slots.tolist() == want[0] and pairs == want[1]
+                short = r.length(sr) - len(toks)
+                if short > 0:
+                    toks.extend(rng.integers(0, 20, size=short).tolist())
+        elif op in (4, 5):
+            sl, sr, toks = live[int(rng.integers(0, len(live)))]
+            k = int(rng.integers(0, r.length(sr) + 1))
+            a.prefix_register(sl, toks, k)
+            r.prefix_register(sr, toks, k)
+        else:
+            sl, sr, _ = live.pop(int(rng.integers(0, len(live))))
+            a.free_seq(sl)
+            r.free_seq(sr)
+        same_state(a, r, [(x[0], x[1]) for x in live])
+        same_prefix_state(a, r)
+    st = r.prefix_stats()
+    assert st["lookups"] > 0 and st["hit_blocks"] > 0 and st["evictions"] > 0
+
+
+def test_prefix_errors():
+    pa = ensure_library()
+    a = pa.BlockAllocator(4, 16)
+    s = a.create()
+    a.append(s, 20)
+    with pytest.raises(pa.PagedAttnError):
+        a.prefix_register(s, list(range(21)))         # more tokens than the sequence holds
+    with pytest.raises(pa.PagedAttnError):
+        a.prefix_register(7, list(range(4)))          # unknown sequence
+    with pytest.raises(pa.PagedAttnError):
+        a.prefix_lookup([1, 2, 3], -1)
+    assert a.prefix_lookup([]) == (1, 0)

@@ -31,6 +31,15 @@ MUTATIONS = [
     ("cow-keeps-ref", "alloc.py", "self.refcount[old] -= 1", "pass", ["test_oracle_alloc.py"]),
     ("fork-drops-partial-block", "alloc.py", "[: blocks_needed(share_tokens, self.block_size)]", "[: share_tokens // self.block_size]", ["test_oracle_alloc.py"]),
     ("lifo-reuse", "alloc.py", "self.free.append(b)", "self.free.appendleft(b)", ["test_oracle_alloc.py"]),
+    ("fnv-prime", "prefix.py", "FNV_PRIME = 0x100000001B3", "FNV_PRIME = 0x100000001B5", ["test_oracle_prefix.py"]),
+    ("fnv-mul-before-xor", "prefix.py", "h ^= byte\n        h = (h * FNV_PRIME) & _MASK", "h = (h * FNV_PRIME) & _MASK\n        h ^= byte", ["test_oracle_prefix.py"]),
+    ("hash-drops-parent", "prefix.py", "data = int(parent).to_bytes(8, \"little\") + b\"\".join(", "data = b\"\".join(", ["test_oracle_prefix.py"]),
+    ("token-low-byte", "prefix.py", "(int(t) & 0xFFFFFFFF).to_bytes(4, \"little\")", "(int(t) & 0xFF).to_bytes(4, \"little\")", ["test_oracle_prefix.py"]),
+    ("lookup-caches-all", "alloc.py", "for b in range(max(n - 1, 0) // B):", "for b in range(n // B):", ["test_oracle_prefix.py"]),
+    ("lookup-keeps-free", "alloc.py", "                self.free.remove(blk)\n", "                pass\n", ["test_oracle_prefix.py"]),
+    ("no-eviction", "alloc.py", "        b = self.free.popleft()\n        self._unregister(b)", "        b = self.free.popleft()", ["test_oracle_prefix.py"]),
+    ("register-overwrites", "alloc.py", "if blk not in self.reg and h not in self.cache:", "if blk not in self.reg:", ["test_oracle_prefix.py"]),
+    ("in-place-write-kept", "alloc.py", "self._unregister(table[j])   # written in place", "pass   # written in place", ["test_oracle_prefix.py"]),
     ("v-from-k", "cache.py", "v_cache[blocks, :, rows, :] = np.asarray(v)[keep]", "v_cache[blocks, :, rows, :] = np.asarray(k)[keep]", ["test_oracle_cache.py"]),
 ]
 
