@@ -17,7 +17,9 @@ Two timed regions of --steps steps each follow --warmup untimed steps: the
 first (no instrumentation) gives `value` and `ms_per_step`; the second runs
 with the library's per-kernel HIP-event tracing on and gives the kernel
 durations behind `roofline`.  Side legs: the prefill chunks of the mixed
-super-batch (MFMA utilisation), a step launched call by call vs replayed from
+super-batch (MFMA utilisation), a speculative-decoding step (64 sequences
+verifying 2..8 tokens each) through the multi-token decode kernel and, for
+comparison, through the chunked-prefill kernel, a step launched call by call vs replayed from
 a HIP graph (`graph`, tiny and batched decode), the host allocator's replay
 rate, and the CPU oracle (`cpu_baseline`).  `--copy-probe` instead runs only
 the known-size copy used to calibrate rocprofv3's HBM byte counters.
@@ -42,7 +44,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 CONTEXT = {"tiny_decode": "{35,16,1,50}", "batched_decode": "U[128,4096]",
            "long_context_decode": "U[32768,131072]",
            "mixed_superbatch": "16 decode U[256,4096] + 4x512 chunks on 0/1024/4096/8192 cached",
-           "shared_prefix_cow": "2048 shared + U[0,512] private"}
+           "shared_prefix_cow": "2048 shared + U[0,512] private",
+           "spec_verify": "U[128,4096], U{2..8} query tokens each"}
 
 
 def log(msg):
@@ -69,6 +72,15 @@ def decode_algorithmic_bytes(wl):
     e = elem_bytes(wl)
     table = sum((int(wl.seq_lens[i]) + 15) // 16 for i in seqs) * 4
     return kv_bytes(wl, seqs) + 2 * len(seqs) * wl.num_q_heads * wl.head_dim * e + table
+
+
+def multi_token_algorithmic_bytes(wl):
+    """Sequences with 2..16 query rows: K/V once per KV head + their q read + out written + table entries."""
+    seqs = [i for i in range(wl.num_seqs) if 2 <= wl.query_lens[i] <= 16]
+    e = elem_bytes(wl)
+    rows = sum(int(wl.query_lens[i]) for i in seqs)
+    table = sum((int(wl.seq_lens[i]) + 15) // 16 for i in seqs) * 4
+    return kv_bytes(wl, seqs) + 2 * rows * wl.num_q_heads * wl.head_dim * e + table
 
 
 def write_algorithmic_bytes(wl):
@@ -344,6 +356,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph step-replay leg")
+    ap.add_argument("--no-verify", action="store_true", help="skip the multi-token decode leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -454,6 +467,40 @@ def main():
                           "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl,
                           "kernel_ms": {k: round(mean(v), 5) for k, v in pper.items()}}
         del prun
+        torch.cuda.empty_cache()
+
+    if not args.no_verify:
+        log("multi-token decode leg: 64 sequences verifying 2..8 tokens (forward only), two routes")
+        vwl = workloads.spec_verify()
+        vrun = DeviceRun(vwl, fill="zero", copies=max(2, -(-(1 << 30) // kv_bytes(vwl))))
+        vsteps = max(10, args.steps // 2)
+        legs = {}
+        for route in ("verify", "prefill"):
+            if route == "prefill":
+                os.environ["PA_VERIFY"] = "prefill"
+            try:
+                run_steps(vrun, 3, stream, with_writes=False)
+                vms, _ = timed_region(vrun, vsteps, stream, with_writes=False)
+                legs[route] = (vms, traced_region(pa, vrun, vsteps, stream, with_writes=False))
+            finally:
+                os.environ.pop("PA_VERIFY", None)
+        vms, vper = legs["verify"]
+        vkern = mean(vper["decode_verify"])
+        valgo = multi_token_algorithmic_bytes(vwl)
+        vach = valgo / (vkern * 1e-3) / 1e9
+        res["multi_token_decode"] = {
+            "workload": "spec_verify: " + CONTEXT["spec_verify"] + ", 32/8 heads, D128, bf16, causal",
+            "ms_per_forward": round(vms, 5),
+            "kv_GBs": round(kv_bytes(vwl) / (vms * 1e-3) / 1e9, 2),
+            "query_tokens_per_s": round(vwl.num_tokens / (vms * 1e-3), 1),
+            "kernel_ms": {k: round(mean(v), 5) for k, v in vper.items()},
+            "roofline": {"kernel": "decode_verify", "bound": "hbm", "achieved": round(vach, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vach / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_launch": int(valgo), "launch_ms": round(vkern, 5)},
+            "prefill_route": {"ms_per_forward": round(legs["prefill"][0], 5),
+                              "kernel_ms": {k: round(mean(v), 5) for k, v in legs["prefill"][1].items()}},
+        }
+        del vrun
         torch.cuda.empty_cache()
 
     if not args.no_graph:

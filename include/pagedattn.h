@@ -154,9 +154,13 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  * where K_t / V_t is token t of sequence i, in block block_tables[i][t / 16]
  * at row t % 16.  Accumulation is fp32; out is rounded once (nearest-even for
  * bf16).  Sequences with n_i = 1 run the split-KV decode path (their keys cut
- * into parts whose partial results are merged by log-sum-exp); sequences with
- * n_i > 1 run the chunked-prefill path (bf16: matrix cores; long key ranges
- * likewise cut into pieces and merged).
+ * into parts whose partial results are merged by log-sum-exp); with bf16 and
+ * head_dim 128, sequences with a few query tokens (2 .. 16, 2 .. 8 when eight
+ * query heads share a KV head, bounded also by max_query_len: a speculative-
+ * decoding step, "vLLM PagedAttention: eine Revolution ..." (de.news.hada.io),
+ * bullet "Guided and Speculative Decoding") run a multi-token decode path of
+ * the same split-KV kind; longer ones run the chunked-prefill path (bf16:
+ * matrix cores; long key ranges likewise cut into pieces and merged).
  *
  *   out, q           device, [num_tokens][num_q_heads][head_dim], c->dtype
  *   k_cache, v_cache device pools (read only)
@@ -191,6 +195,12 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *            size (a multiple of 16, <= 8192); auto aims at ~4096 (sequence,
  *            KV head, partition) work-groups with partitions of 128..2048 tokens
  *   PA_DECODE_WAVES=1|2|4   partitioned decode: waves per work-group
+ *   PA_VERIFY=prefill       send the multi-token sequences to the chunked-prefill path
+ *   PA_VERIFY=all           send single-token sequences through the multi-token
+ *            decode path too (one launch for both kinds)
+ *   PA_VERIFY_TOTAL_WAVES=<1..65536>  multi-token decode: waves in all (default 1024)
+ *   PA_VERIFY_DEPTH=2|3|4   multi-token decode: K/V tiles in flight per wave
+ *            (default 3, or 2 when four work-groups would not fit a CU's LDS)
  *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
  *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
  *            max(1024, a quarter of the longest sequence)

@@ -335,11 +335,6 @@ struct BalancedArgs {
 
 inline size_t balanced_lds_bytes(int num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
 
-__device__ __forceinline__ int64_t stream_start(int r, int64_t total, int Wg) { return (int64_t)r * total / Wg; }
-// Rank whose range holds tile t: the largest r with stream_start(r) <= t.
-__device__ __forceinline__ int stream_owner(int64_t t, int64_t total, int Wg) {
-  return (int)(((t + 1) * Wg - 1) / total);
-}
 
 // Combine the four row groups (lanes j, j+16, j+32, j+48): afterwards every
 // lane (r, j) holds the wave's max M and sum lt of head j % G and, for every

@@ -1,0 +1,581 @@
+// Multi-token decode on the matrix cores: sequences that add a few query
+// tokens in one step, as a speculative-decoding step does when it scores the
+// tokens a smaller draft model proposed ("vLLM PagedAttention: eine
+// Revolution ..." (de.news.hada.io), bullet "Guided and Speculative
+// Decoding"; "Внутреннее устройство vLLM" (artificials.ru), closing paragraph:
+// several tokens predicted at once).  Query token jq of a sequence holding L
+// tokens after this step's write sits at position L - n + jq and, causally,
+// sees keys 0 .. L - n + jq (same page, forward-pass paragraph: attention
+// masks and exact positional indices keep each row on its own sequence).
+//
+// Such a step reads a sequence's whole cache for a handful of query rows, so
+// it is bound by memory bandwidth like single-token decode, and it reuses the
+// balanced one-round scheme of the single-token kernel: per KV head, the
+// 16-token tiles of all these sequences form one stream cut into equal ranges,
+// one single-wave work-group per range; tiles are staged through LDS by the
+// buffer unit NS deep; the parts of a sequence split between waves are merged
+// afterwards in rank order by merge_verify_kernel.
+//
+// What differs is the work per tile.  The MFMA columns are (token, query head)
+// pairs -- column c -> token c / G, query head g G + c % G -- in CG groups of
+// 16, so up to 16 CG / G tokens of a sequence share every K/V tile read:
+//   S^T = K Q^T     v_mfma_f32_16x16x32_bf16 per 32 dims: A = K rows from
+//                   LDS (lane l: key l % 16, dims 8 (l / 16) of the step), B =
+//                   the column group's query rows; lane (r, j) receives the
+//                   scores of keys 4r .. 4r+3 for column j.
+//   O^T += V^T P^T  v_mfma_f32_16x16x16_bf16 per 16 dims: B = P^T is exactly
+//                   the lane's own four weights (rounded to bf16); A = V^T is
+//                   read from a row-major [16 keys][16 dims] sub-tile with
+//                   ds_read_b64_tr_b16, which hands lane (r, m) keys 4r .. 4r+3
+//                   of dim m when the 16 lanes of row group r point at those
+//                   four key rows (four lanes per row, four dims each).
+// A column's softmax state is kept by its four lanes together: one running
+// max (equal in all four; moved, after a reduction across them, only when a
+// score beats it by the rescale slack) and a partial sum each, so a rescale
+// touches only the lane's own accumulators and the common tile needs no
+// cross-lane traffic.
+// The sum adds the same bf16-rounded weights the P.V product uses.
+//
+// Keys past a column's visible end get weight 0 (select, on the tiles that
+// need it); the copies of a sequence's last tile go through a buffer range
+// that ends at its last token, so stale slots arrive as zeros and nothing
+// past the sequence reaches an MFMA.
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "device.h"
+#include "ops.h"
+#include "status.h"
+
+namespace pa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;                 // one bf16 token row of one KV head
+constexpr int kTileBytes = kBlock * kRowBytes;    // one (block, KV head) tile: 4 KiB
+constexpr int kMaxVerifySeqs = 1024;              // per-sequence tables kept in LDS
+constexpr int kMaxColGroups = 4;
+constexpr int kMaxVerifyTokens = 16;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+struct VerifyArgs {
+  AttnArgs a;
+  int32_t min_q;            // sequences with min_q .. max_q query tokens
+  int32_t max_q;
+  int32_t waves_per_head;   // Wg
+  int32_t slots;            // partial slots per KV head: num_seqs + Wg
+  float* p_acc;             // [Hkv][slots][CG][8 db][64 lanes][4]: fragment order (see finish)
+  float* p_ml;              // [Hkv][slots][16 CG][2]  (max in base-2 units, sum)
+  int2* seqinfo;            // [num_seqs]: (first rank, parts)
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Dynamic LDS: tile prefix sums [S + 1], query row << 5 | (tokens - 1) [S], length [S].
+inline size_t verify_dyn_lds(int num_seqs) { return (size_t)(3 * num_seqs + 1) * sizeof(int); }
+// Static LDS of one instantiation: lookup windows, query rows, NS stages.
+inline size_t verify_static_lds(int cg, int ns) { return 3 * 512 + (size_t)cg * 4096 + (size_t)ns * 8192; }
+
+// True for the sequences this kernel and its merge handle (the same test in both).
+__device__ __forceinline__ bool verify_item(const VerifyArgs& k, int i, int& q0, int& n, int& len) {
+  const AttnArgs& a = k.a;
+  q0 = a.qsl[i];
+  n = a.qsl[i + 1] - q0;
+  len = min(a.seq_lens[i], a.bt_stride * kBlock);
+  return n >= k.min_q && n <= k.max_q && q0 >= 0 && q0 + n <= a.num_tokens && len >= n;
+}
+
+__device__ __forceinline__ s16x4_t lds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p);
+}
+
+// fp32 -> bf16 bits, round to nearest even, for finite non-negative weights.
+__device__ __forceinline__ uint32_t weight_bits(float p) {
+  const uint32_t u = __float_as_uint(p);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <int CG>
+struct VerifyState {
+  float m[CG];          // running max (base 2) of the lane's column, the same in its four lanes
+  float l[CG];          // this lane's share of the column's weight sum
+  f32x4_t acc[CG][8];   // O^T: column j, dims 16 db + 4 r .. +3
+};
+
+template <int G, int CG, int NS>
+__global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
+  static_assert(16 % G == 0, "query heads per KV head must divide 16");
+  static_assert(NS >= 2 && NS <= 4, "tiles in flight");
+  constexpr int C = 16 * CG;
+  extern __shared__ int s_dyn[];
+  const AttnArgs& a = k.a;
+  const int S = a.num_seqs;
+  int* s_cum = s_dyn;
+  int* s_meta = s_dyn + S + 1;
+  int* s_len = s_meta + S;
+  __shared__ int s_raw[2][64];                   // lookup windows: block-table entry (copied), sequence, logical block
+  __shared__ int s_sj[2][2][64];
+  __shared__ __attribute__((aligned(16))) uint4 s_q[CG * 4 * 64];   // query rows: [cg][ks][lane]
+  __shared__ __attribute__((aligned(16))) uint4 s_t0[512];          // tile stages: K [ks][lane], V [db][16 keys][16 dims]
+  __shared__ __attribute__((aligned(16))) uint4 s_t1[512];
+  __shared__ __attribute__((aligned(16))) uint4 s_t2[NS > 2 ? 512 : 1];
+  __shared__ __attribute__((aligned(16))) uint4 s_t3[NS > 3 ? 512 : 1];
+  const int Hkv = a.num_kv_heads;
+  const int g = blockIdx.x % Hkv, rank = blockIdx.x / Hkv;
+  const int lane = threadIdx.x;
+
+  // Tiles of every sequence this kernel handles (0 for the others), then
+  // exclusive prefix sums in place.
+  for (int c0 = 0; c0 < S; c0 += 256) {
+    int T[4], M[4], Ln[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      T[u] = 0;
+      M[u] = 0;
+      Ln[u] = 0;
+      int q0, n, len;
+      if (i < S && verify_item(k, i, q0, n, len)) {
+        T[u] = (len + kBlock - 1) / kBlock;
+        M[u] = (q0 << 5) | (n - 1);
+        Ln[u] = len;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      if (i < S) {
+        s_cum[i] = T[u];
+        s_meta[i] = M[u];
+        s_len[i] = Ln[u];
+      }
+    }
+  }
+  int carry = 0;
+  for (int c0 = 0; c0 < S; c0 += 64) {
+    const int i = c0 + lane;
+    const int T = i < S ? s_cum[i] : 0;
+    int x = T;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    if (i < S) s_cum[i] = carry + x - T;
+    carry += __shfl(x, 63);
+  }
+  if (lane == 0) s_cum[S] = carry;
+  __syncthreads();
+  const int64_t total = carry;
+  const int Wg = (int)min((int64_t)k.waves_per_head, total);
+  if (rank >= Wg) return;
+  const int tb = (int)stream_start(rank, total, Wg);
+  const int cnt = (int)(stream_start(rank + 1, total, Wg) - tb);
+
+  const u32x4_t rbt = rsrc_words((const uint8_t*)a.block_tables,
+                                 (int)min((int64_t)S * a.bt_stride * 4, (int64_t)0x7fffffff));
+  auto lookup = [&](int window) {
+    const int u = window * 64 + lane;
+    int seq = 0, jt = 0;
+    if (u < cnt) {
+      const int t = tb + u;
+      int lo = 0, hi = S - 1;   // largest i with s_cum[i] <= t (that sequence has tiles)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_cum[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      seq = lo;
+      jt = t - s_cum[lo];
+      lds_copy4(rbt, &s_raw[window & 1][0], (seq * a.bt_stride + jt) * 4);
+    }
+    s_sj[window & 1][0][lane] = seq;
+    s_sj[window & 1][1][lane] = jt;
+  };
+  lookup(0);
+  lookup(1);
+  PA_VM_WAIT(0);
+  int window = 0;
+
+  const int j = lane & 15, r = lane >> 4;
+  const int hq0 = g * G;
+  // Query rows of sequence `seq` -> s_q: copy (cg, ks) has lane (r, j) fetch
+  // dims 32 ks + 8 r .. +8 of column 16 cg + j.  The buffer range ends at the
+  // sequence's last query row, so columns past its tokens read zeros.
+  auto copy_q = [&](int seq) {
+    const int meta = __builtin_amdgcn_readfirstlane(s_meta[seq]);
+    const int q0 = meta >> 5, nq = (meta & 31) + 1;
+    const u32x4_t rq = rsrc_words((const uint8_t*)a.q + (size_t)q0 * a.num_q_heads * kRowBytes,
+                                  nq * a.num_q_heads * kRowBytes);
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      const int col = 16 * cg + j;
+      const int off = ((col / G) * a.num_q_heads + hq0 + col % G) * kRowBytes + r * 16;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lds_copy16(rq, s_q + (cg * 4 + ks) * 64, off + ks * 64);
+    }
+  };
+  copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]));
+  int q_tile = -(NS - 1);   // tile whose issue followed the last query copy
+
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * kTileBytes;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * kTileBytes;
+  const size_t block_stride = (size_t)Hkv * kTileBytes;
+  // K piece ks: lane (r, j) copies key j, dims 32 ks + 8 r .. +8.
+  const int koff = j * kRowBytes + r * 16;
+  // V piece e (dim blocks 2e, 2e+1): lane 32 dsel + 2 key + half copies key
+  // `key`, dims 16 (2e + dsel) + 8 half .. +8, landing in row `key` of the
+  // [16 keys][16 dims] sub-tile of dim block 2e + dsel.
+  const int voff = ((lane & 31) >> 1) * kRowBytes + (lane >> 5) * 32 + (lane & 1) * 16;
+  auto stage = [&](int sI) -> uint4* { return sI == 0 ? s_t0 : sI == 1 ? s_t1 : sI == 2 ? s_t2 : s_t3; };
+  auto issue = [&](int u, int sI) {
+    const int w = (u >> 6) & 1, e = u & 63;
+    const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[w][e]), a.num_blocks);
+    const int seq = __builtin_amdgcn_readfirstlane(s_sj[w][0][e]);
+    const int jt = __builtin_amdgcn_readfirstlane(s_sj[w][1][e]);
+    // Rows past the sequence read as zero.
+    const int bytes = __builtin_amdgcn_readfirstlane(min(s_len[seq] - jt * kBlock, kBlock) * kRowBytes);
+    const size_t off = (size_t)bid * block_stride;
+    const u32x4_t rk = rsrc_words(kc + off, bytes);
+    const u32x4_t rv = rsrc_words(vc + off, bytes);
+    uint4* dst = stage(sI);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_copy16(rv, dst + 256 + p * 64, voff + p * 64);
+  };
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, cnt - 1), s0);
+
+  // Transpose-read address of this lane inside a [16 keys][16 dims] sub-tile:
+  // row group r points at key rows 4r .. 4r+3, four lanes per row, four dims each.
+  const int tr_off = (4 * r + j / 4) * 32 + (j & 3) * 8;
+
+  VerifyState<CG> st;
+  bf16x8_t qf[CG][4];
+  int cur = -1, cur_j0 = 0, cur_jl = 0, cur_q0 = 0, cur_n = 0, cga = 0, first_end = 0;
+  int col_end[CG];
+
+  auto finish = [&](int seq, bool whole) {
+    const size_t slot = (size_t)g * k.slots + (size_t)(seq + rank);
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      if (cg >= cga) break;
+      float lt = st.l[cg];
+      lt += __shfl_xor(lt, 16);
+      lt += __shfl_xor(lt, 32);
+      const int col = 16 * cg + j;
+      const int jq = col / G;
+      if (jq >= cur_n) continue;
+      if (whole) {
+        const float inv = 1.0f / lt;
+        uint8_t* op = (uint8_t*)a.out + ((size_t)(cur_q0 + jq) * a.num_q_heads + hq0 + col % G) * kRowBytes + r * 8;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4_t x = st.acc[cg][db];
+          *reinterpret_cast<uint2*>(op + db * 32) =
+              make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
+        }
+      } else {
+        // Partials in fragment order: dim block db of column group cg is one
+        // contiguous 1 KiB piece, lane l's four values at 16 l, so every store
+        // instruction writes whole cache lines.
+        float* dst = k.p_acc + ((slot * CG + cg) * 8 * 64 + lane) * 4;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const f32x4_t x = st.acc[cg][db];
+          *reinterpret_cast<float4*>(dst + db * 256) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+        if (r == 0) *reinterpret_cast<float2*>(k.p_ml + (slot * C + col) * 2) = make_float2(st.m[cg], lt);
+      }
+    }
+  };
+
+  for (int u0 = 0; u0 < cnt; u0 += NS) {
+#pragma unroll
+    for (int sI = 0; sI < NS; ++sI) {
+      const int u = u0 + sI;
+      if (u >= cnt) break;
+      if ((u >> 6) != window) {
+        // Window w begins: look up window w + 1 into the slot window w - 1 used.
+        ++window;
+        lookup(window + 1);
+      }
+      const int seq = __builtin_amdgcn_readfirstlane(s_sj[window & 1][0][u & 63]);
+      const int jt = __builtin_amdgcn_readfirstlane(s_sj[window & 1][1][u & 63]);
+      if (seq != cur) {
+        if (cur >= 0) finish(cur, cur_j0 == 0 && cur_jl + 1 == s_cum[cur + 1] - s_cum[cur]);
+        cur = seq;
+        const int meta = s_meta[seq];
+        const int L = s_len[seq];
+        cur_q0 = meta >> 5;
+        cur_n = (meta & 31) + 1;
+        cga = min(CG, (cur_n * G + 15) / 16);
+        first_end = a.causal ? L - cur_n + 1 : L;
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg)
+          col_end[cg] = a.causal ? min(L, L - cur_n + (16 * cg + j) / G + 1) : L;
+        cur_j0 = jt;
+        if (jt == 0 && g == 0 && lane == 0) {
+          const int last = stream_owner((int64_t)s_cum[seq + 1] - 1, total, Wg);
+          k.seqinfo[seq] = make_int2(rank, last - rank + 1);
+        }
+        // This sequence's query copy was followed by the issues of tiles
+        // q_tile .. u - 1 (eight copies each; at least one tile).
+        __builtin_amdgcn_sched_barrier(0);
+        wait_tiles(min(u - q_tile, NS - 1));
+        const lds_u32x4_t* qs = (const lds_u32x4_t*)s_q;
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg)
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) qf[cg][ks] = __builtin_bit_cast(bf16x8_t, qs[(cg * 4 + ks) * 64 + lane]);
+        // The copy of the next sequence's rows overwrites s_q: the reads above come first.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        int nx = seq + 1;                      // next sequence with tiles, if this range reaches it
+        while (nx < S && s_cum[nx + 1] == s_cum[nx]) ++nx;
+        if (nx < S && s_cum[nx] < tb + cnt) {
+          copy_q(nx);
+          q_tile = u;
+        }
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+          st.m[cg] = kNegBig;
+          st.l[cg] = 0.0f;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) st.acc[cg][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      // The stage refilled here was read by the previous fold; the copies
+      // stay after those reads and ahead of the reads of this tile's stage,
+      // which wait for this tile's copies: NS - 1 tiles were issued after them.
+      __builtin_amdgcn_sched_barrier(0);
+      issue(min(u + NS - 1, cnt - 1), (sI + NS - 1) % NS);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_tiles(NS - 1);
+      cur_jl = jt;
+      const lds_u32x4_t* src = (const lds_u32x4_t*)stage(sI);
+      uint4 kq[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
+
+      // Scores of the active column groups, base-2 units, masked past each column's end.
+      const int tok0 = jt * kBlock;
+      float sc[CG][4];
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (cg >= cga) break;
+        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[ks]), qf[cg][ks], s, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[cg][e] = s[e] * a.scale_log2;
+        if (tok0 + kBlock > first_end) {   // wave-uniform: only a sequence's last tiles reach a column's end
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[cg][e] = tok0 + 4 * r + e < col_end[cg] ? sc[cg][e] : -INFINITY;
+        }
+      }
+      // Lazy rescale: only when some lane's scores beat its column's reference
+      // by the slack (rare after a segment's first tile) are the four lanes of
+      // each column reduced to the column's tile max and the reference moved.
+      bool need = false;
+      float mx[CG];
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (cg >= cga) break;
+        mx[cg] = fmaxf(fmaxf(sc[cg][0], sc[cg][1]), fmaxf(sc[cg][2], sc[cg][3]));
+        need |= mx[cg] > st.m[cg] + kRescaleSlack;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+          if (cg >= cga) break;
+          float x = fmaxf(mx[cg], __shfl_xor(mx[cg], 16));
+          x = fmaxf(x, __shfl_xor(x, 32));
+          const float mn = x > st.m[cg] + kRescaleSlack ? x : st.m[cg];
+          const float alpha = fast_exp2(st.m[cg] - mn);
+          st.m[cg] = mn;
+          st.l[cg] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) st.acc[cg][db] *= alpha;
+        }
+      }
+      // Weights (bf16, as the product uses them), their sums, and O^T += V^T P^T.
+      s16x4_t pb[CG];
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (cg >= cga) break;
+        float sum = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t b = weight_bits(fast_exp2(sc[cg][e] - st.m[cg]));
+          pb[cg][e] = (short)b;
+          sum += __uint_as_float(b << 16);
+        }
+        st.l[cg] += sum;
+      }
+      const uint8_t* vst = (const uint8_t*)stage(sI) + 4096 + tr_off;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const s16x4_t vt = lds_read_tr(vst + db * 512);
+#pragma unroll
+        for (int cg = 0; cg < CG; ++cg) {
+          if (cg >= cga) break;
+          st.acc[cg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[cg], st.acc[cg][db], 0, 0, 0);
+        }
+      }
+    }
+  }
+  finish(cur, cur_j0 == 0 && cur_jl + 1 == s_cum[cur + 1] - s_cum[cur]);
+}
+
+// Merge of the parts of split sequences: one work-group per (sequence, KV
+// head); thread item = one float4 of the fragment-ordered partials (column
+// group cg, dim block db, lane (r, j): column 16 cg + j, dims 16 db + 4 r ..
+// +3), so consecutive threads read consecutive 16 bytes; the parts are folded
+// in rank order by the log-sum-exp rule in one pass, four parts' loads in
+// flight.
+template <int CG>
+__global__ __launch_bounds__(256) void merge_verify_kernel(VerifyArgs k) {
+  constexpr int C = 16 * CG, U = 4;
+  const AttnArgs& a = k.a;
+  const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv;
+  const int i = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  int q0, n, len;
+  if (!verify_item(k, i, q0, n, len)) return;
+  const int2 si = k.seqinfo[i];          // written by this call's verify kernel
+  const int P = si.y;
+  if (P <= 1) return;                    // written out by the verify kernel
+  const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);
+  const int groups = (n * G + 15) / 16;
+  for (int it = threadIdx.x; it < groups * 8 * 64; it += 256) {
+    const int ln = it & 63, db = (it >> 6) & 7, cg = it >> 9;
+    const int col = 16 * cg + (ln & 15);
+    if (col >= n * G) continue;
+    const float2* ml = reinterpret_cast<const float2*>(k.p_ml) + slot0 * C + col;
+    const float* acc = k.p_acc + (slot0 * CG * 8 * 64 + it) * 4;
+    float M = -INFINITY, den = 0.0f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < P; p0 += U) {
+      float2 v[U];
+      float4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u < P) {
+          v[u] = ml[(size_t)(p0 + u) * C];
+          x[u] = *reinterpret_cast<const float4*>(acc + (size_t)(p0 + u) * C * kD);   // one slot = C x D floats
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u >= P) break;
+        const float Mn = fmaxf(M, v[u].x);
+        const float sa = fast_exp2(M - Mn), sb = fast_exp2(v[u].x - Mn);
+        den = fmaf(den, sa, v[u].y * sb);
+        num.x = fmaf(num.x, sa, x[u].x * sb);
+        num.y = fmaf(num.y, sa, x[u].y * sb);
+        num.z = fmaf(num.z, sa, x[u].z * sb);
+        num.w = fmaf(num.w, sa, x[u].w * sb);
+        M = Mn;
+      }
+    }
+    const float inv = 1.0f / den;
+    uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + col / G) * a.num_q_heads + g * G + col % G) * kRowBytes +
+                  (16 * db + 4 * (ln >> 4)) * 2;
+    *reinterpret_cast<uint2*>(op) = make_uint2(pack_bf16x2(num.x * inv, num.y * inv),
+                                               pack_bf16x2(num.z * inv, num.w * inv));
+  }
+}
+
+template <int G, int CG, int NS>
+pa_status launch_verify_gc(const VerifyArgs& k, hipStream_t s) {
+  const int W = k.waves_per_head * k.a.num_kv_heads;
+  int mark = trace_begin(s);
+  hipLaunchKernelGGL((decode_verify_kernel<G, CG, NS>), dim3(W), dim3(64), verify_dyn_lds(k.a.num_seqs), s, k);
+  trace_end(s, mark, "decode_verify");
+  pa_status st = launch_status("pa_forward (multi-token decode)");
+  if (st != PA_OK) return st;
+  mark = trace_begin(s);
+  hipLaunchKernelGGL((merge_verify_kernel<CG>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(256), 0, s, k);
+  trace_end(s, mark, "merge_verify");
+  return launch_status("pa_forward (multi-token decode merge)");
+}
+
+template <int G, int CG>
+pa_status launch_verify_g(const VerifyArgs& k, int depth, hipStream_t s) {
+  if (depth >= 4) return launch_verify_gc<G, CG, 4>(k, s);
+  if (depth == 3) return launch_verify_gc<G, CG, 3>(k, s);
+  return launch_verify_gc<G, CG, 2>(k, s);
+}
+
+}  // namespace
+
+VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len) {
+  VerifyPlan vp{};
+  const int32_t G = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
+  // PA_VERIFY=prefill sends these sequences to the chunked-prefill kernel;
+  // PA_VERIFY=all routes single-token sequences here too (one launch for all).
+  const char* env = std::getenv("PA_VERIFY");
+  if (env != nullptr && std::strcmp(env, "prefill") == 0) return vp;
+  const int32_t min_q = env != nullptr && std::strcmp(env, "all") == 0 ? 1 : 2;
+  if (!decode_mfma_supported(dtype, head_dim, G) || num_seqs < 1 || num_seqs > kMaxVerifySeqs ||
+      max_query_len < min_q || max_seq_len <= 0 || num_tokens >= (1 << 26))
+    return vp;
+  // Columns (token, query head) in groups of 16: enough groups for the
+  // longest multi-token sequence up to 16 tokens and 4 groups.
+  const int cap = std::min(kMaxVerifyTokens, 16 * kMaxColGroups / G);
+  const int want = std::min<int>(max_query_len, cap);
+  int cg = (want * G + 15) / 16;
+  if (cg == 3) cg = 4;
+  vp.on = true;
+  vp.min_q = min_q;
+  vp.col_groups = cg;
+  vp.max_q = std::min(cap, 16 * cg / G);
+  // As the single-token decode: 1024 single-wave work-groups in all.
+  int64_t target = 1024;
+  if (const char* tw = std::getenv("PA_VERIFY_TOTAL_WAVES")) {
+    const int v = std::atoi(tw);
+    if (v >= 1 && v <= 65536) target = v;
+  }
+  const int64_t whole_tiles = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
+  const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(target / num_kv_heads, (int64_t)num_seqs * whole_tiles));
+  vp.waves_per_head = (int32_t)wg;
+  // Three tiles in flight while four work-groups still fit in a CU's LDS, else
+  // two; PA_VERIFY_DEPTH=2..4 overrides.
+  vp.depth = verify_static_lds(cg, 3) + verify_dyn_lds(num_seqs) <= 40 * 1024 ? 3 : 2;
+  if (const char* dp = std::getenv("PA_VERIFY_DEPTH")) {
+    const int v = std::atoi(dp);
+    if (v >= 2 && v <= 4) vp.depth = v;
+  }
+  const size_t slots = (size_t)num_seqs + (size_t)wg;
+  vp.info_bytes = round256((size_t)num_seqs * 2 * sizeof(int32_t));
+  vp.acc_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * head_dim * sizeof(float));
+  vp.ml_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * 2 * sizeof(float));
+  return vp;
+}
+
+pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,
+                               int32_t* part_table, hipStream_t s) {
+  VerifyArgs k{a, vp.min_q, vp.max_q, vp.waves_per_head, a.num_seqs + vp.waves_per_head, p_acc, p_ml, (int2*)part_table};
+  const int G = a.num_q_heads / a.num_kv_heads;
+  switch (G * 16 + vp.col_groups) {
+    case 1 * 16 + 1: return launch_verify_g<1, 1>(k, vp.depth, s);
+    case 2 * 16 + 1: return launch_verify_g<2, 1>(k, vp.depth, s);
+    case 2 * 16 + 2: return launch_verify_g<2, 2>(k, vp.depth, s);
+    case 4 * 16 + 1: return launch_verify_g<4, 1>(k, vp.depth, s);
+    case 4 * 16 + 2: return launch_verify_g<4, 2>(k, vp.depth, s);
+    case 4 * 16 + 4: return launch_verify_g<4, 4>(k, vp.depth, s);
+    case 8 * 16 + 1: return launch_verify_g<8, 1>(k, vp.depth, s);
+    case 8 * 16 + 2: return launch_verify_g<8, 2>(k, vp.depth, s);
+    case 8 * 16 + 4: return launch_verify_g<8, 4>(k, vp.depth, s);
+    default:
+      return fail(PA_ERR_UNSUPPORTED, "pa_forward: multi-token decode with %d query heads per KV head, %d column groups",
+                  G, vp.col_groups);
+  }
+}
+
+}  // namespace pa

@@ -172,6 +172,14 @@ __device__ __forceinline__ void wait_tiles(int t) {
 }
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
 
+// Balanced split of a stream of `total` tiles over Wg ranks: rank r takes
+// tiles [stream_start(r), stream_start(r + 1)).
+__device__ __forceinline__ int64_t stream_start(int r, int64_t total, int Wg) { return (int64_t)r * total / Wg; }
+// Rank whose range holds tile t: the largest r with stream_start(r) <= t.
+__device__ __forceinline__ int stream_owner(int64_t t, int64_t total, int Wg) {
+  return (int)(((t + 1) * Wg - 1) / total);
+}
+
 // Widen eight bf16 (one 16-byte chunk) to fp32.
 __device__ __forceinline__ void widen_bf16x8(uint4 w, float* f) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);

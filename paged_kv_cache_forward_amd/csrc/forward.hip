@@ -5,8 +5,10 @@
 // single unpadded batch, each row restricted to its own sequence.  Rows of
 // sequences with one query token go to the split-KV decode kernel (plus the
 // log-sum-exp merge when a sequence spans several partitions); sequences with
-// more query tokens go to the chunked-prefill kernel.  Grids are sized from the
-// host scalars max_seq_len / max_query_len, so nothing waits on the device.
+// a few query tokens (2 .. the verify plan's max_q: a speculative-decoding
+// step) to the multi-token decode kernel; longer ones to the chunked-prefill
+// kernel.  Grids are sized from the host scalars max_seq_len / max_query_len,
+// so nothing waits on the device.
 #include <cmath>
 #include <vector>
 
@@ -19,9 +21,11 @@ namespace pa {
 struct ForwardShape {
   int32_t group;
   DecodePlan plan;
+  VerifyPlan vplan;
   PrefillPlan pplan;
   bool use_mfma_prefill;
   bool any_prefill;
+  size_t workspace_bytes() const { return plan.workspace_bytes() + vplan.workspace_bytes() + pplan.workspace_bytes(); }
 };
 
 static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
@@ -40,7 +44,9 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
   if (fs->group != 1 && fs->group != 2 && fs->group != 4 && fs->group != 8)
     return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (built for 1, 2, 4, 8)", who, fs->group);
   fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
-  fs->any_prefill = max_query_len > 1;
+  fs->vplan = make_verify_plan(num_seqs, num_tokens, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype,
+                               max_seq_len, max_query_len);
+  fs->any_prefill = max_query_len > 1 && !(fs->vplan.on && max_query_len <= fs->vplan.max_q);
   fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
   fs->pplan = make_prefill_plan(num_tokens, num_q_heads, c->head_dim, max_seq_len, max_query_len,
                                 fs->use_mfma_prefill);
@@ -89,7 +95,7 @@ extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens
   if (shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_workspace_size",
                &fs) != PA_OK)
     return 0;
-  return fs.plan.workspace_bytes() + fs.pplan.workspace_bytes();
+  return fs.workspace_bytes();
 }
 
 extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -107,7 +113,7 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   if (block_table_stride <= 0) return fail(PA_ERR_ARG, "pa_forward: block_table_stride %d", block_table_stride);
   if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "pa_forward: scale is not finite");
   if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "pa_forward: causal must be 0 or 1");
-  const size_t ws_need = fs.plan.workspace_bytes() + fs.pplan.workspace_bytes();
+  const size_t ws_need = fs.workspace_bytes();
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
     return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", ws_need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
@@ -137,10 +143,14 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   a.head_dim = c->head_dim;
   a.scale_log2 = scale * kLog2e;
   a.causal = causal;
+  a.prefill_min_q = fs.vplan.on ? fs.vplan.max_q + 1 : 2;
 
   int32_t* p_info = nullptr;
   float* p_acc = nullptr;
   float* p_ml = nullptr;
+  int32_t* v_info = nullptr;
+  float* v_acc = nullptr;
+  float* v_ml = nullptr;
   float* pre_o = nullptr;
   float* pre_ml = nullptr;
   if (ws_need > 0) {
@@ -148,13 +158,23 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
     p_info = (int32_t*)base;
     p_acc = (float*)(base + fs.plan.info_bytes);
     p_ml = (float*)(base + fs.plan.info_bytes + fs.plan.acc_bytes);
-    pre_o = (float*)(base + fs.plan.workspace_bytes());
-    pre_ml = (float*)(base + fs.plan.workspace_bytes() + fs.pplan.o_bytes);
+    uint8_t* vbase = base + fs.plan.workspace_bytes();
+    v_info = (int32_t*)vbase;
+    v_acc = (float*)(vbase + fs.vplan.info_bytes);
+    v_ml = (float*)(vbase + fs.vplan.info_bytes + fs.vplan.acc_bytes);
+    uint8_t* pbase = vbase + fs.vplan.workspace_bytes();
+    pre_o = (float*)pbase;
+    pre_ml = (float*)(pbase + fs.pplan.o_bytes);
   }
   if (fs.use_mfma_prefill) {
     st = launch_prefill(a, max_query_len, fs.pplan, pre_o, pre_ml, s);
     if (st != PA_OK) return st;
   }
+  if (fs.vplan.on) {
+    st = launch_decode_verify(a, fs.vplan, v_acc, v_ml, v_info, s);
+    if (st != PA_OK) return st;
+  }
+  if (fs.vplan.on && fs.vplan.min_q <= 1) return PA_OK;   // single-token sequences taken by the launch above
   if (fs.plan.balanced) return launch_decode_balanced(a, fs.plan, p_acc, p_ml, p_info, s);
   if (fs.plan.mfma)
     st = launch_decode_mfma(a, fs.plan, p_acc, p_ml, s);

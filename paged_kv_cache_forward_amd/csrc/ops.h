@@ -43,6 +43,7 @@ struct AttnArgs {
   int32_t head_dim;
   float scale_log2;            // softmax scale * log2(e): scores are kept in base-2 units
   int32_t causal;
+  int32_t prefill_min_q;       // the prefill kernel takes sequences with at least this many query tokens
 };
 
 // Plan for the decode path (sequences with one query token).
@@ -89,6 +90,29 @@ pa_status launch_decode_mfma(const AttnArgs& a, const DecodePlan& plan, float* p
 bool decode_balanced_supported(int32_t num_seqs);
 pa_status launch_decode_balanced(const AttnArgs& a, const DecodePlan& plan, float* p_acc, float* p_ml,
                                  int32_t* part_table, hipStream_t s);
+
+// Plan for the multi-token decode path (sequences with 2 .. max_q query
+// tokens, bf16, head_dim 128, at most 1024 sequences): balanced like the
+// single-token decode, columns = (token, query head) pairs in col_groups
+// groups of 16.  Workspace (offsets 256-byte aligned):
+//   [part table: int32 [num_seqs][2]]
+//   [partial acc: fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][head_dim]]
+//   [partial (max, sum): fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][2]]
+struct VerifyPlan {
+  bool on;
+  int32_t min_q;           // 2, or 1 when it also takes the single-token sequences
+  int32_t col_groups;      // 1, 2 or 4
+  int32_t max_q;           // longest sequence (query tokens) it takes; longer ones go to prefill
+  int32_t waves_per_head;
+  int32_t depth;           // K/V tiles in flight per wave (2 or 3)
+  size_t info_bytes, acc_bytes, ml_bytes;
+  size_t workspace_bytes() const { return info_bytes + acc_bytes + ml_bytes; }
+};
+
+VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len);
+pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,
+                               int32_t* part_table, hipStream_t s);
 
 // Split-KV plan for the chunked-prefill kernel: the key range of every
 // (sequence, query tile, KV head) work-group is cut into pieces of piece_keys

@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   const int g = it.g, qt = it.qt, i = it.i;
   const int q0 = a.qsl[i];
   const int n = a.qsl[i + 1] - q0;
-  if (n <= 1 || q0 < 0 || q0 + n > a.num_tokens) return;
+  if (n < max(a.prefill_min_q, 2) || q0 < 0 || q0 + n > a.num_tokens) return;
   const int tok0 = qt * TOK;
   if (tok0 >= n) return;
   const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
@@ -413,7 +413,7 @@ __global__ __launch_bounds__(2 * kRowsPerWG) void prefill_merge_kernel(PrefillAr
   const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.qtiles, a.num_seqs);
   const int q0 = a.qsl[it.i];
   const int n = a.qsl[it.i + 1] - q0;
-  if (n <= 1 || q0 < 0 || q0 + n > a.num_tokens) return;
+  if (n < max(a.prefill_min_q, 2) || q0 < 0 || q0 + n > a.num_tokens) return;
   const int tok0 = it.qt * TOK;
   if (tok0 >= n) return;
   const int L = min(a.seq_lens[it.i], a.bt_stride * kBlock);

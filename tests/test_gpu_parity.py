@@ -64,7 +64,8 @@ def test_mini_workloads(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["tiny_decode", "batched_decode", "mixed_superbatch", "shared_prefix_cow"])
+@pytest.mark.parametrize("name", ["tiny_decode", "batched_decode", "mixed_superbatch", "shared_prefix_cow",
+                                  "spec_verify"])
 def test_named_workloads_full_size(name):
     wl = workloads.named(name)
     check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch"))
@@ -154,6 +155,68 @@ def test_balanced_wave_counts(waves, depth, monkeypatch):
     monkeypatch.setenv("PA_DECODE_DEPTH", depth)
     for name in ("decode_gqa8", "decode_bf16", "mixed_bf16", "shared_bf16"):
         check_parity(workloads.mini(name), pools=False)
+
+
+VERIFY_MINIS = ("verify_bf16", "verify_gqa8", "verify_mha")
+
+
+@pytest.mark.parametrize("waves", ["1", "7", "64", "1024", "65536"])
+def test_multi_token_decode_wave_counts(waves, monkeypatch):
+    """The multi-token decode meets the tolerance for any number of waves per KV head
+    (one wave for everything, ragged cuts, one tile per wave, more waves than tiles)."""
+    monkeypatch.delenv("PA_VERIFY", raising=False)
+    monkeypatch.setenv("PA_VERIFY_TOTAL_WAVES", waves)
+    for name in VERIFY_MINIS:
+        check_parity(workloads.mini(name), pools=False)
+
+
+def test_multi_token_decode_routes():
+    """Sequences of 2 .. 16 query tokens: column groups 1, 2 and 4 (set by the longest
+    one), the cap per group size (longer sequences go to prefill in the same call),
+    non-causal rows, and a batch whose longest sequence picks one column group."""
+    ensure_library()
+    cases = [
+        ("verify_g4_cg1", dict(Hq=32, Hkv=8, cached=[40, 0, 700], new=[2, 4, 3])),
+        ("verify_g4_cg2", dict(Hq=32, Hkv=8, cached=[40, 1, 2000, 17], new=[5, 8, 2, 1])),
+        ("verify_g8_cap", dict(Hq=64, Hkv=8, cached=[100, 9, 300], new=[8, 9, 2])),
+        ("verify_g2", dict(Hq=16, Hkv=8, cached=[64, 129, 5], new=[16, 3, 11])),
+        ("verify_g1_long", dict(Hq=8, Hkv=8, cached=[3000, 16], new=[16, 17])),
+    ]
+    for k, (name, kw) in enumerate(cases):
+        wl = workloads.independent(name, 40 + k, D=128, dtype="bf16", pool_extra=2, **kw)
+        check_parity(wl, pools=False)
+    wl = workloads.independent("verify_noncausal", 46, Hq=32, Hkv=8, D=128, dtype="bf16",
+                               cached=[20, 500, 0], new=[6, 3, 16], pool_extra=2, causal=False)
+    check_parity(wl, pools=False)
+
+
+def test_multi_token_decode_against_the_prefill_route(monkeypatch):
+    """PA_VERIFY=prefill sends the same sequences through the chunked-prefill kernel; both routes meet the tolerance."""
+    monkeypatch.setenv("PA_VERIFY", "prefill")
+    for name in VERIFY_MINIS:
+        check_parity(workloads.mini(name), pools=False)
+
+
+def test_single_token_rows_through_the_multi_token_kernel(monkeypatch):
+    """PA_VERIFY=all sends single-token sequences through the multi-token decode kernel too."""
+    monkeypatch.setenv("PA_VERIFY", "all")
+    for name in ("decode_bf16", "decode_gqa8", "mixed_bf16", "shared_bf16") + VERIFY_MINIS:
+        check_parity(workloads.mini(name), pools=False)
+
+
+def test_multi_token_decode_invariances():
+    """Placement, stale-slot contents and table padding change no output bit of the multi-token decode."""
+    wl = workloads.mini("verify_bf16")
+    base = _device_run(wl)
+    ref_bits = base.host(base.out)
+    alt = np.random.default_rng(98).permutation(wl.num_blocks).astype(np.int32)
+    moved = _device_run(wl, free_order=alt)
+    assert moved.tables != base.tables
+    assert np.array_equal(moved.host(moved.out), ref_bits)
+    zero = _device_run(wl, fill="zero")
+    assert np.array_equal(zero.host(zero.out), ref_bits)
+    wide = _device_run(wl, table_stride=max(len(t) for t in base.tables) + 7)
+    assert np.array_equal(wide.host(wide.out), ref_bits)
 
 
 @pytest.mark.parametrize("split", ["off", "64", "192", "1024"])

@@ -273,12 +273,23 @@ def shared_prefix_cow():
                          num_seqs=256, prefix=2048, suffix_max=512, num_blocks=8192)
 
 
+def spec_verify():
+    """64 sequences, context U{128..4096} after the step, each verifying U{2..8} new tokens
+    (speculative decoding: the draft tokens plus one), causal; 32/8 heads, D 128, bf16; pool 20000."""
+    rng = np.random.Generator(np.random.PCG64(1006))
+    L = _lengths(rng, 128, 4096, 64)
+    n = _lengths(rng, 2, 8, 64)
+    return independent("spec_verify", 6, Hq=32, Hkv=8, D=128, dtype="bf16",
+                       cached=L - n, new=n, num_blocks=20000)
+
+
 NAMED = {
     "tiny_decode": tiny_decode,
     "batched_decode": batched_decode,
     "long_context_decode": long_context_decode,
     "mixed_superbatch": mixed_superbatch,
     "shared_prefix_cow": shared_prefix_cow,
+    "spec_verify": spec_verify,
 }
 
 
@@ -340,6 +351,22 @@ def mini(name):
         new = np.array([50, 70, 1])
         return independent(name, 20, Hq=32, Hkv=8, D=128, dtype="bf16", cached=cached,
                            new=new, pool_extra=2, causal=False)
+    if name == "verify_bf16":
+        # multi-token decode: 2..16 query tokens per sequence, ragged tails, a sequence with no cache
+        cached = np.array([0, 1, 15, 16, 300, 1021, 2500, 47, 5])
+        new = np.array([2, 3, 8, 16, 5, 4, 7, 2, 1])
+        return independent(name, 22, Hq=32, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=3)
+    if name == "verify_gqa8":
+        cached = np.array([700, 3, 2047, 64])
+        new = np.array([8, 6, 2, 9])
+        return independent(name, 23, Hq=64, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=2)
+    if name == "verify_mha":
+        cached = np.array([130, 0, 999])
+        new = np.array([16, 4, 11])
+        return independent(name, 24, Hq=8, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=2)
     if name == "shared_bf16":
         return shared_prefix(name, 21, Hq=32, Hkv=8, D=128, dtype="bf16", num_seqs=9,
                              prefix=160, suffix_max=70, num_blocks=200)
@@ -348,4 +375,4 @@ def mini(name):
 
 MINI = ["decode_f32", "decode_bf16", "decode_gqa8", "decode_d64_bf16", "decode_d128_f32",
         "mixed_bf16", "mixed_gqa8", "mixed_mha_d64", "prefill_f32", "noncausal_bf16",
-        "shared_bf16"]
+        "shared_bf16", "verify_bf16", "verify_gqa8", "verify_mha"]
