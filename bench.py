@@ -183,6 +183,7 @@ KERNEL_SOURCES = {
     "decode_valu": ("decode.hip", "device.h"),
     "prefill": ("prefill.hip", "device.h"),
     "write_kv": ("cache_ops.hip", "device.h"),
+    "decode_verify": ("decode_verify.hip", "device.h"),
 }
 
 
@@ -496,6 +497,7 @@ def main():
             "kernel_ms": {k: round(mean(v), 5) for k, v in vper.items()},
             "roofline": {"kernel": "decode_verify", "bound": "hbm", "achieved": round(vach, 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(vach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_verify", vwl.name),
                          "algorithmic_bytes_per_launch": int(valgo), "launch_ms": round(vkern, 5)},
             "prefill_route": {"ms_per_forward": round(legs["prefill"][0], 5),
                               "kernel_ms": {k: round(mean(v), 5) for k, v in legs["prefill"][1].items()}},
