@@ -31,6 +31,8 @@ Modules:
   alloc      -- RefAllocator: block allocator with refcounts, copy-on-write
                 and the prefix cache
   prefix     -- chained FNV-1a 64 block hashes for prefix caching
+  quant      -- fp8 (E4M3 codes, power-of-two row scales) cache format: encode,
+                decode, quantised write and dequantised gather
   cache      -- cache write through a slot mapping; whole-block copies
   attention  -- paged attention over a varlen super-batch; split/merge pieces
 
@@ -43,6 +45,16 @@ from .numerics import to_f64
 from .blocks import blocks_needed, unused_slots, unused_fraction
 from .alloc import RefAllocator, OutOfBlocks
 from .prefix import fnv1a64, block_hash, chain
+from .quant import (
+    decode_e4m3,
+    encode_e4m3,
+    row_exponent,
+    quantize_rows,
+    dequantize_rows,
+    fp8_pool,
+    ref_write_kv_fp8,
+    gather_logical_fp8,
+)
 from .cache import ref_write_kv, ref_copy_blocks
 from .attention import (
     gather_logical,
@@ -62,6 +74,14 @@ __all__ = [
     "fnv1a64",
     "block_hash",
     "chain",
+    "decode_e4m3",
+    "encode_e4m3",
+    "row_exponent",
+    "quantize_rows",
+    "dequantize_rows",
+    "fp8_pool",
+    "ref_write_kv_fp8",
+    "gather_logical_fp8",
     "ref_write_kv",
     "ref_copy_blocks",
     "gather_logical",

@@ -34,6 +34,7 @@ through its block table, and n_i = query_start_loc[i+1] - query_start_loc[i].
 import numpy as np
 
 from .numerics import to_f64
+from .quant import gather_logical_fp8
 
 
 def gather_logical(cache, table, length, block_size):
@@ -53,13 +54,16 @@ def ref_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start
     """Attention output in float64, ``[num_tokens][Hq][D]``.
 
     ``q`` is ``[num_tokens][Hq][D]``, the caches ``[NB][Hkv][B][D]``, all stored
-    as ``dtype`` ("f32" or "bf16" bit patterns).  ``block_tables[i]`` lists the
+    as ``dtype`` ("f32" or "bf16" bit patterns).  With ``dtype`` "fp8" the
+    caches are quantised pools (``oracle.quant``: ``[NB][Hkv][B*D + B]`` uint8)
+    read as their exact dequantised values, and ``q`` is bf16.  ``block_tables[i]`` lists the
     physical blocks of sequence i in logical order.  Rows of every sequence
     are attended independently; rows belonging to no sequence stay zero.
     """
     q = np.asarray(q)
     num_tokens, num_q_heads, head_dim = q.shape
     num_kv_heads = k_cache.shape[1]
+    q_dtype = "bf16" if dtype == "fp8" else dtype
     if num_q_heads % num_kv_heads:
         raise ValueError("query heads must be a multiple of KV heads")
     group = num_q_heads // num_kv_heads
@@ -72,9 +76,13 @@ def ref_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start
             raise ValueError(f"sequence {i}: seq_len {L} != cached {c} + new {n}")
         if n == 0:
             continue
-        K = to_f64(gather_logical(k_cache, block_tables[i], L, block_size), dtype)
-        V = to_f64(gather_logical(v_cache, block_tables[i], L, block_size), dtype)
-        Q = to_f64(q[r0:r1], dtype)
+        if dtype == "fp8":
+            K = gather_logical_fp8(k_cache, block_tables[i], L, block_size, "k")
+            V = gather_logical_fp8(v_cache, block_tables[i], L, block_size, "v")
+        else:
+            K = to_f64(gather_logical(k_cache, block_tables[i], L, block_size), dtype)
+            V = to_f64(gather_logical(v_cache, block_tables[i], L, block_size), dtype)
+        Q = to_f64(q[r0:r1], q_dtype)
 
         pos = c + np.arange(n)[:, None]          # absolute position of each row
         t = np.arange(L)[None, :]

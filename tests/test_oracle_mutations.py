@@ -40,6 +40,13 @@ MUTATIONS = [
     ("no-eviction", "alloc.py", "        b = self.free.popleft()\n        self._unregister(b)", "        b = self.free.popleft()", ["test_oracle_prefix.py"]),
     ("register-overwrites", "alloc.py", "if blk not in self.reg and h not in self.cache:", "if blk not in self.reg:", ["test_oracle_prefix.py"]),
     ("in-place-write-kept", "alloc.py", "self._unregister(table[j])   # written in place", "pass   # written in place", ["test_oracle_prefix.py"]),
+    ("e4m3-bias", "quant.py", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)", "return sign * (1.0 + m / 8.0) * 2.0 ** (e - 8)", ["test_oracle_quant.py"]),
+    ("e4m3-subnormal-step", "quant.py", "q_sub = np.rint(a * 2.0 ** 9)", "q_sub = np.rint(a * 2.0 ** 8)", ["test_oracle_quant.py"]),
+    ("round-half-up", "quant.py", "q = np.rint((2.0 * m - 1.0) * 8.0)", "q = np.floor((2.0 * m - 1.0) * 8.0 + 0.5)", ["test_oracle_quant.py"]),
+    ("no-carry", "quant.py", "    E = E + carry\n", "", ["test_oracle_quant.py"]),
+    ("scale-not-minimal", "quant.py", "e = np.where(safe <= np.ldexp(E4M3_MAX, e - 1), e - 1, e)", "e = e + 1", ["test_oracle_quant.py"]),
+    ("v-not-transposed", "quant.py", "return rows * D + d if kind == \"k\" else d * block_size + rows", "return rows * D + d", ["test_oracle_quant.py"]),
+    ("scale-bias", "quant.py", "e = np.asarray(exp_codes, dtype=np.int64) - SCALE_BIAS", "e = np.asarray(exp_codes, dtype=np.int64) - SCALE_BIAS - 1", ["test_oracle_quant.py"]),
     ("v-from-k", "cache.py", "v_cache[blocks, :, rows, :] = np.asarray(v)[keep]", "v_cache[blocks, :, rows, :] = np.asarray(k)[keep]", ["test_oracle_cache.py"]),
 ]
 
