@@ -19,7 +19,8 @@ with the library's per-kernel HIP-event tracing on and gives the kernel
 durations behind `roofline`.  Side legs: the prefill chunks of the mixed
 super-batch (MFMA utilisation), a speculative-decoding step (64 sequences
 verifying 2..8 tokens each) through the multi-token decode kernel and, for
-comparison, through the chunked-prefill kernel, a step launched call by call vs replayed from
+comparison, through the chunked-prefill kernel, the default decode step on a
+quantised fp8 cache (`fp8_decode`), a step launched call by call vs replayed from
 a HIP graph (`graph`, tiny and batched decode), the host allocator's replay
 rate, and the CPU oracle (`cpu_baseline`).  `--copy-probe` instead runs only
 the known-size copy used to calibrate rocprofv3's HBM byte counters.
@@ -45,7 +46,8 @@ CONTEXT = {"tiny_decode": "{35,16,1,50}", "batched_decode": "U[128,4096]",
            "long_context_decode": "U[32768,131072]",
            "mixed_superbatch": "16 decode U[256,4096] + 4x512 chunks on 0/1024/4096/8192 cached",
            "shared_prefix_cow": "2048 shared + U[0,512] private",
-           "spec_verify": "U[128,4096], U{2..8} query tokens each"}
+           "spec_verify": "U[128,4096], U{2..8} query tokens each",
+           "batched_decode_fp8": "U[128,4096], fp8 cache"}
 
 
 def log(msg):
@@ -60,10 +62,16 @@ def decode_rows(wl):
     return [i for i in range(wl.num_seqs) if wl.query_lens[i] == 1]
 
 
+def kv_row_bytes(wl):
+    """Stored bytes of one token's K (or V) row for one KV head: head_dim elements, or for an
+    fp8 cache head_dim E4M3 codes + one scale byte."""
+    return wl.head_dim + 1 if wl.cache == "fp8" else wl.head_dim * elem_bytes(wl)
+
+
 def kv_bytes(wl, seqs=None):
     """K and V bytes of the visible context, read once per KV head (paging leaves bytes per token unchanged)."""
     seqs = range(wl.num_seqs) if seqs is None else seqs
-    return sum(int(wl.seq_lens[i]) for i in seqs) * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl)
+    return sum(int(wl.seq_lens[i]) for i in seqs) * 2 * wl.num_kv_heads * kv_row_bytes(wl)
 
 
 def decode_algorithmic_bytes(wl):
@@ -358,6 +366,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph step-replay leg")
     ap.add_argument("--no-verify", action="store_true", help="skip the multi-token decode leg")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode leg")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -503,6 +512,32 @@ def main():
                               "kernel_ms": {k: round(mean(v), 5) for k, v in legs["prefill"][1].items()}},
         }
         del vrun
+        torch.cuda.empty_cache()
+
+    if not args.no_fp8:
+        log("fp8 leg: the default batched decode on a quantised (E4M3 + row scales) cache, whole steps")
+        fwl = workloads.batched_decode_fp8()
+        frun = DeviceRun(fwl, fill="zero", copies=max(2, -(-(1 << 30) // kv_bytes(fwl))))
+        fsteps = max(10, args.steps // 2)
+        run_steps(frun, 3, stream)
+        fms, _ = timed_region(frun, fsteps, stream)
+        fper = traced_region(pa, frun, fsteps, stream)
+        fkern = mean(fper["decode_verify"])
+        falgo = decode_algorithmic_bytes(fwl)
+        fach = falgo / (fkern * 1e-3) / 1e9
+        res["fp8_decode"] = {
+            "workload": "batched_decode_fp8: 64 seqs, context U[128,4096], 32/8 heads, D128, fp8 (E4M3, one "
+                        "power-of-two scale per token and KV head) cache, bf16 q/out",
+            "ms_per_step": round(fms, 5),
+            "kv_GBs": round(kv_bytes(fwl) / (fms * 1e-3) / 1e9, 2),
+            "tokens_per_s": round(fwl.num_tokens / (fms * 1e-3), 1),
+            "kernel_ms": {k: round(mean(v), 5) for k, v in fper.items()},
+            "roofline": {"kernel": "decode_verify", "bound": "hbm", "achieved": round(fach, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fach / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_verify", fwl.name),
+                         "algorithmic_bytes_per_launch": int(falgo), "launch_ms": round(fkern, 5)},
+        }
+        del frun
         torch.cuda.empty_cache()
 
     if not args.no_graph:

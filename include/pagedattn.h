@@ -42,6 +42,22 @@
  *     [num_blocks][num_kv_heads][block_size = 16][head_dim]   row-major,
  * so one (block, KV head) tile of 16 tokens is contiguous.  Slot s of the
  * pool is row s % 16 of block s / 16.
+ *
+ * Quantised pools (dtype PA_FP8, head_dim 128).  [SLAVA] section "Gemeinsame
+ * Nutzung erfordert mehr als Speicherzuweisung" names cache quantisation as
+ * the remedy when the K/V data itself does not fit; [AIU] "L'avenir de
+ * PagedAttention et vLLM" expects paged K/V combined with quantisation.  Each
+ * (token, KV head) row of head_dim values is stored as E4M3 codes (the FN
+ * encoding of the OCP 8-bit floating point specification) with one
+ * power-of-two scale 2^e, e = the smallest integer in [-126, 127] with
+ * max|x| <= 448 * 2^e (0 for a zero row), kept as an E8M0 byte e + 127; the
+ * codes are x * 2^-e rounded to nearest, ties to even mantissa.  A pool is
+ * num_blocks * num_kv_heads * (16 * head_dim + 16) bytes in two planes:
+ *     codes      [num_blocks][num_kv_heads][16 * head_dim]   (tiles 128-byte aligned)
+ *     exponents  [num_blocks][num_kv_heads][16]              (one byte per row)
+ * K codes are row-major in their tile (byte row * head_dim + d); V codes are
+ * stored transposed (byte d * 16 + row), the layout the P.V product reads.
+ * The value a cached element stands for is decode(code) * 2^e, exactly.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -62,7 +78,7 @@ typedef enum {
   PA_ERR_HIP = 5           /* HIP runtime error */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
 /* Shape of one K (or V) pool.  block_size must be 16 for device calls. */
 typedef struct {
@@ -70,7 +86,8 @@ typedef struct {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t block_size;
-  int32_t dtype;           /* pa_dtype: element type of pools, k/v, q and out */
+  int32_t dtype;           /* pa_dtype: element type of pools, k/v, q and out;
+                              PA_FP8: quantised pools, k/v/q/out bf16 */
 } pa_cache_desc;
 
 /* Library version string (static storage). */
@@ -91,6 +108,7 @@ const char* pa_last_error(void);
  * tokens are written before attention reads them.
  *
  *   k, v          device, [num_tokens][num_kv_heads][head_dim], contiguous, c->dtype
+ *                 (bf16 for a PA_FP8 cache, which this call quantises row by row)
  *   k_cache,
  *   v_cache       device pools (layout above), modified in place
  *   slot_mapping  device int64 [num_tokens]; slot < 0 means "skip this token"
@@ -98,7 +116,8 @@ const char* pa_last_error(void);
  *                 Precondition: no two tokens name the same slot.
  *   num_tokens    >= 0 (0 is a no-op)
  *
- * A bit copy: the stored bytes equal the input bytes exactly.
+ * A bit copy: the stored bytes equal the input bytes exactly (PA_FP8: the
+ * quantisation above, exactly; a row's codes and scale are written together).
  * Errors: PA_ERR_ARG, PA_ERR_UNSUPPORTED (block_size != 16 or head_dim*elem
  * not a multiple of 16 bytes), PA_ERR_RANGE (check mode: duplicate or
  * out-of-pool slot), PA_ERR_HIP.

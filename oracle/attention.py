@@ -55,14 +55,14 @@ def ref_paged_attention(q, k_cache, v_cache, block_tables, seq_lens, query_start
 
     ``q`` is ``[num_tokens][Hq][D]``, the caches ``[NB][Hkv][B][D]``, all stored
     as ``dtype`` ("f32" or "bf16" bit patterns).  With ``dtype`` "fp8" the
-    caches are quantised pools (``oracle.quant``: ``[NB][Hkv][B*D + B]`` uint8)
-    read as their exact dequantised values, and ``q`` is bf16.  ``block_tables[i]`` lists the
+    caches are quantised pools
+    read as their exact dequantised values (``oracle.quant.Fp8Pool``), and ``q`` is bf16.  ``block_tables[i]`` lists the
     physical blocks of sequence i in logical order.  Rows of every sequence
     are attended independently; rows belonging to no sequence stay zero.
     """
     q = np.asarray(q)
     num_tokens, num_q_heads, head_dim = q.shape
-    num_kv_heads = k_cache.shape[1]
+    num_kv_heads = k_cache.num_kv_heads if dtype == "fp8" else k_cache.shape[1]
     q_dtype = "bf16" if dtype == "fp8" else dtype
     if num_q_heads % num_kv_heads:
         raise ValueError("query heads must be a multiple of KV heads")

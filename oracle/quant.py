@@ -19,10 +19,11 @@ with quantisation.  They fix no format.  Readings (each listed in the design doc):
   * Rounding: to the nearest E4M3 value, ties to an even mantissa (the
     usual IEEE rule).  Because |x * 2^-e| <= 448 nothing saturates.
   * Dequantised value: decode(code) * 2^e, exact in float64.
-  * Pool layout per (block, KV head) tile, uint8, 16 * D + 16 bytes:
-      K pool: codes row-major, byte row * D + d; exponents at 16 * D + row.
-      V pool: codes transposed, byte d * 16 + row; exponents at 16 * D + row.
-    A pool is ``[num_blocks][num_kv_heads][16 * D + 16]``.
+  * Pool layout: num_blocks * num_kv_heads * (16 * D + 16) bytes in two
+    planes.  First the codes, ``[num_blocks][num_kv_heads][16 * D]``: per
+    (block, KV head) tile the K codes row-major (byte row * D + d), the V codes
+    transposed (byte d * 16 + row).  Then the exponents,
+    ``[num_blocks][num_kv_heads][16]``, one byte per row.
 """
 
 import math
@@ -98,9 +99,31 @@ def dequantize_rows(codes, exp_codes):
     return np.ldexp(DECODE_TABLE[np.asarray(codes, dtype=np.int64)], e[..., None])
 
 
+class Fp8Pool:
+    """One quantised pool: ``flat`` holds the bytes; ``codes`` and ``exps`` are views of its two planes.
+
+    Indexing by block reads or replaces that block's codes and exponents
+    together, so a whole-block copy is ``pool[dst] = pool[src]``.
+    """
+
+    def __init__(self, num_blocks, num_kv_heads, head_dim, block_size=16, fill=0xFF):
+        n = num_blocks * num_kv_heads
+        self.flat = np.full(n * (block_size * head_dim + block_size), fill, dtype=np.uint8)
+        self.codes = self.flat[:n * block_size * head_dim].reshape(num_blocks, num_kv_heads, block_size * head_dim)
+        self.exps = self.flat[n * block_size * head_dim:].reshape(num_blocks, num_kv_heads, block_size)
+        self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size = (num_blocks, num_kv_heads,
+                                                                              head_dim, block_size)
+
+    def __getitem__(self, blk):
+        return self.codes[blk].copy(), self.exps[blk].copy()
+
+    def __setitem__(self, blk, value):
+        self.codes[blk], self.exps[blk] = value
+
+
 def fp8_pool(num_blocks, num_kv_heads, head_dim, block_size=16, fill=0xFF):
-    """A pool ``[num_blocks][num_kv_heads][block_size * head_dim + block_size]`` of uint8."""
-    return np.full((num_blocks, num_kv_heads, block_size * head_dim + block_size), fill, dtype=np.uint8)
+    """An empty pool (every byte ``fill``; 0xff is a NaN code and a NaN scale)."""
+    return Fp8Pool(num_blocks, num_kv_heads, head_dim, block_size, fill)
 
 
 def _code_index(kind, rows, D, block_size):
@@ -121,7 +144,7 @@ def ref_write_kv_fp8(k_pool, v_pool, k, v, slot_mapping, block_size):
     live = slots[keep]
     if np.unique(live).size != live.size:
         raise ValueError("duplicate slots in one write")
-    if live.size and live.max() // block_size >= k_pool.shape[0]:
+    if live.size and live.max() // block_size >= k_pool.num_blocks:
         raise ValueError("slot beyond the pool")
     blk, row = live // block_size, live % block_size
     hkv, D = np.asarray(k).shape[1], np.asarray(k).shape[2]
@@ -129,8 +152,8 @@ def ref_write_kv_fp8(k_pool, v_pool, k, v, slot_mapping, block_size):
     for pool, x, kind in ((k_pool, k, "k"), (v_pool, v, "v")):
         codes, exps = quantize_rows(np.asarray(x, dtype=np.float64)[keep])      # [n][Hkv][D], [n][Hkv]
         idx = _code_index(kind, row, D, block_size)[:, None, :]                 # [n][1][D]
-        pool[blk[:, None, None], heads, idx] = codes
-        pool[blk[:, None], np.arange(hkv)[None, :], block_size * D + row[:, None]] = exps
+        pool.codes[blk[:, None, None], heads, idx] = codes
+        pool.exps[blk[:, None], np.arange(hkv)[None, :], row[:, None]] = exps
 
 
 def gather_logical_fp8(pool, table, length, block_size, kind):
@@ -138,12 +161,11 @@ def gather_logical_fp8(pool, table, length, block_size, kind):
 
     ``kind`` is "k" (row-major codes) or "v" (transposed codes).
     """
-    nb, hkv, tile = pool.shape
-    D = (tile - block_size) // block_size
+    hkv, D = pool.num_kv_heads, pool.head_dim
     t = np.arange(length)
     blk = np.asarray(table, dtype=np.int64)[t // block_size]
     row = t % block_size
     idx = _code_index(kind, row, D, block_size)[:, None, :]
-    codes = pool[blk[:, None, None], np.arange(hkv)[None, :, None], idx]           # [L][Hkv][D]
-    exps = pool[blk[:, None], np.arange(hkv)[None, :], block_size * D + row[:, None]]
+    codes = pool.codes[blk[:, None, None], np.arange(hkv)[None, :, None], idx]     # [L][Hkv][D]
+    exps = pool.exps[blk[:, None], np.arange(hkv)[None, :], row[:, None]]
     return dequantize_rows(codes, exps)

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_ARG, PA_ERR_UNSUPPORTED, PA_ERR_OOM, PA_ERR_RANGE, PA_ERR_HIP = range(6)
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8 = 0, 1, 2
 _STATUS = {1: "PA_ERR_ARG", 2: "PA_ERR_UNSUPPORTED", 3: "PA_ERR_OOM", 4: "PA_ERR_RANGE", 5: "PA_ERR_HIP"}
 
 
@@ -160,16 +160,35 @@ def _stream(stream):
 
 
 def cache_desc(k_cache):
-    """Descriptor of a pool tensor shaped [num_blocks][num_kv_heads][16][head_dim]."""
+    """Descriptor of a pool tensor: [num_blocks][num_kv_heads][16][head_dim] (fp32 / bf16), or a
+    quantised pool, uint8 of shape [num_blocks][num_kv_heads][16 * head_dim + 16]: a size only; its
+    bytes are the plane of E4M3 code tiles, then the plane of row exponents (pagedattn.h)."""
+    torch = _torch()
+    if k_cache.dtype == torch.uint8:
+        if k_cache.dim() != 3 or (k_cache.shape[2] - 16) % 16:
+            raise ValueError("an fp8 pool is uint8 [num_blocks][num_kv_heads][16 * head_dim + 16]")
+        nb, hkv, tile = k_cache.shape
+        return CacheDesc(nb, hkv, (tile - 16) // 16, 16, PA_FP8)
     nb, hkv, bs, d = k_cache.shape
     return CacheDesc(nb, hkv, d, bs, _dtype_code(k_cache))
+
+
+def fp8_pool_shape(num_blocks, num_kv_heads, head_dim):
+    """Shape of a quantised (fp8) pool tensor (uint8)."""
+    return (num_blocks, num_kv_heads, 16 * head_dim + 16)
+
+
+def _row_dtype(k_cache):
+    """Element type of k/v/q/out rows for this cache (bf16 for an fp8 pool)."""
+    torch = _torch()
+    return torch.bfloat16 if k_cache.dtype == torch.uint8 else k_cache.dtype
 
 
 def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     torch = _torch()
     desc = cache_desc(k_cache)
-    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
-        raise TypeError("k, v and the caches must share one dtype")
+    if k.dtype != _row_dtype(k_cache) or v.dtype != k.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype (bf16 rows for an fp8 cache)")
     if v_cache.shape != k_cache.shape or v.shape != k.shape:
         raise ValueError("K and V shapes differ")
     T = k.shape[0]
@@ -213,8 +232,8 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
     torch = _torch()
     desc = cache_desc(k_cache)
     T, Hq, D = q.shape
-    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_cache.dtype:
-        raise ValueError("out must match q, and q the cache dtype")
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != _row_dtype(k_cache):
+        raise ValueError("out must match q, and q the cache dtype (bf16 for an fp8 cache)")
     S = seq_lens.shape[0]
     if query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S:
         raise ValueError("metadata shapes do not match num_seqs")

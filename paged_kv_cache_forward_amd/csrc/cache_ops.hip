@@ -10,6 +10,12 @@
 // Both kernels move 16-byte chunks: one lane per chunk, consecutive lanes on
 // consecutive source bytes, so every wave reads and writes whole 1 KiB runs
 // (a token's row for one KV head is head_dim * elem bytes, 256 B for bf16 D128).
+//
+// Quantised (fp8) pools: "Was ändert PagedAttention ..." section "Gemeinsame
+// Nutzung erfordert mehr als Speicherzuweisung" (cache quantisation) and
+// "PagedAttention et vLLM" section "L'avenir de PagedAttention et vLLM".  The
+// write quantises each (token, KV head) row with its own power-of-two scale:
+// one wave per row, two dims per lane (head_dim 128).
 #include <vector>
 
 #include "device.h"
@@ -43,18 +49,87 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const uint8_t* __restrict
   st16(dst + dst_chunk * 16, ld16(src + idx * 16));
 }
 
-// grid.x = pair, grid.y = 0 for K, 1 for V; each block copies one block tile.
+// grid.x = pair, grid.y = 0 for K, 1 for V (and, for fp8 pools, 2 / 3 for the
+// K / V exponent planes, which start at plane2 bytes and hold chunks2 16-byte
+// chunks per block); each work-group copies one block's region.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_cache,
                                                           uint8_t* __restrict__ v_cache,
                                                           const int32_t* __restrict__ pairs,
-                                                          int chunks_per_block, int num_blocks) {
+                                                          int chunks_per_block, int num_blocks, int64_t plane2,
+                                                          int chunks2) {
   const int src = pairs[2 * blockIdx.x];
   const int dst = pairs[2 * blockIdx.x + 1];
   if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
-  uint8_t* cache = blockIdx.y == 0 ? k_cache : v_cache;
-  const uint8_t* s = cache + (int64_t)src * chunks_per_block * 16;
-  uint8_t* d = cache + (int64_t)dst * chunks_per_block * 16;
-  for (int c = threadIdx.x; c < chunks_per_block; c += blockDim.x) st16(d + c * 16, ld16(s + c * 16));
+  uint8_t* cache = (blockIdx.y & 1) == 0 ? k_cache : v_cache;
+  const int per = blockIdx.y < 2 ? chunks_per_block : chunks2;
+  if (blockIdx.y >= 2) cache += plane2;
+  const uint8_t* s = cache + (int64_t)src * per * 16;
+  uint8_t* d = cache + (int64_t)dst * per * 16;
+  for (int c = threadIdx.x; c < per; c += blockDim.x) st16(d + c * 16, ld16(s + c * 16));
+}
+
+// Smallest e in [-126, 127] with amax <= 448 * 2^e (0 for amax = 0).  amax =
+// f * 2^E with f in [1, 2): 448 = 1.75 * 2^8, so e = E - 8, plus one when f > 1.75.
+// A subnormal amax (below 2^-126) takes the lower limit.
+__device__ __forceinline__ int fp8_row_exponent(float amax) {
+  if (amax == 0.0f) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)(b >> 23) - 127;
+  const int e = E - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return min(max(e, -126), 127);
+}
+
+// E4M3 (OCP, FN) code of x * 2^-e, which lies in [-448, 448]: nearest value,
+// ties to an even mantissa; the sign of zero is kept.  Below 2^-6 the code
+// counts steps of 2^-9 (eight steps are the smallest normal, code 0x08);
+// above, mantissa (f - 1) * 8 of y = f * 2^E, a carry moving to the next binade.
+__device__ __forceinline__ uint32_t fp8_code(float x, int e) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(ldexpf(x, -e));
+  if (a < 0x1p-6f) return sign | (uint32_t)rintf(a * 512.0f);
+  int E = (int)(__float_as_uint(a) >> 23) - 127;
+  uint32_t q = (uint32_t)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
+  if (q == 8u) {
+    q = 0u;
+    ++E;
+  }
+  return sign | ((uint32_t)(E + 7) << 3) | q;
+}
+
+// grid.x covers (token, KV head) rows four waves per block, grid.y = 0 for K, 1 for V.
+// A pool is a plane of code tiles (kBlock * 128 bytes per (block, KV head))
+// followed by a plane of row exponents (kBlock bytes per tile).
+__global__ __launch_bounds__(256) void write_kv_fp8_kernel(const uint32_t* __restrict__ k,
+                                                           const uint32_t* __restrict__ v,
+                                                           uint8_t* __restrict__ k_cache,
+                                                           uint8_t* __restrict__ v_cache,
+                                                           const int64_t* __restrict__ slots, int64_t rows,
+                                                           int num_kv_heads, int64_t num_slots) {
+  constexpr int D = 128, TILE = kBlock * D;
+  const int64_t rw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, KV head) row, wave-uniform
+  const int lane = threadIdx.x & 63;
+  if (rw >= rows) return;
+  const int64_t t = rw / num_kv_heads;
+  const int h = (int)(rw - t * num_kv_heads);
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding token, or a slot outside the pool
+  const bool is_v = blockIdx.y != 0;
+  const uint32_t w = (is_v ? v : k)[rw * (D / 2) + lane];   // dims 2 lane, 2 lane + 1 (bf16)
+  const float x0 = bf16_lo(w), x1 = bf16_hi(w);
+  const int e = fp8_row_exponent(wave_max(fmaxf(fabsf(x0), fabsf(x1))));
+  const uint32_t c0 = fp8_code(x0, e), c1 = fp8_code(x1, e);
+  const int64_t blk = slot / kBlock;
+  const int row = (int)(slot - blk * kBlock);
+  uint8_t* pool = is_v ? v_cache : k_cache;
+  uint8_t* tile = pool + (blk * num_kv_heads + h) * TILE;
+  if (is_v) {                                  // transposed: byte d * 16 + row
+    tile[(2 * lane) * kBlock + row] = (uint8_t)c0;
+    tile[(2 * lane + 1) * kBlock + row] = (uint8_t)c1;
+  } else {
+    *reinterpret_cast<uint16_t*>(tile + row * D + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
+  }
+  const int64_t exps = (num_slots / kBlock) * num_kv_heads * TILE;   // exponent plane
+  if (lane == 0) pool[exps + (blk * num_kv_heads + h) * kBlock + row] = (uint8_t)(e + 127);
 }
 
 pa_status check_desc(const pa_cache_desc* c, const char* who) {
@@ -64,8 +139,10 @@ pa_status check_desc(const pa_cache_desc* c, const char* who) {
                 who, c->num_blocks, c->num_kv_heads, c->head_dim);
   if (c->block_size != kBlock)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (device path is built for 16)", who, c->block_size);
-  if (c->dtype != PA_F32 && c->dtype != PA_BF16)
+  if (c->dtype != PA_F32 && c->dtype != PA_BF16 && c->dtype != PA_FP8)
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", who, c->dtype);
+  if (c->dtype == PA_FP8 && c->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with head_dim %d (built for 128)", who, c->head_dim);
   if ((c->head_dim * elem_bytes(c->dtype)) % 16 != 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d x elem not a multiple of 16 bytes", who, c->head_dim);
   return PA_OK;
@@ -106,6 +183,17 @@ extern "C" pa_status pa_write_kv(const void* k, const void* v, void* k_cache, vo
       if (seen[h[t]]) return fail(PA_ERR_RANGE, "pa_write_kv: token %d repeats slot %lld", t, (long long)h[t]);
       seen[h[t]] = 1;
     }
+  }
+  if (c->dtype == PA_FP8) {
+    const int64_t rows = (int64_t)num_tokens * c->num_kv_heads;
+    const int64_t nblk = (rows + 3) / 4;
+    if (nblk > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: too many tokens in one call");
+    const int mark = trace_begin(s);
+    hipLaunchKernelGGL(write_kv_fp8_kernel, dim3((unsigned)nblk, 2), dim3(256), 0, s, (const uint32_t*)k,
+                       (const uint32_t*)v, (uint8_t*)k_cache, (uint8_t*)v_cache, slot_mapping, rows,
+                       c->num_kv_heads, num_slots);
+    trace_end(s, mark, "write_kv");
+    return launch_status("pa_write_kv");
   }
   const int row_bytes = c->head_dim * elem_bytes(c->dtype);
   const int chunks_per_row = row_bytes / 16;
@@ -148,10 +236,15 @@ extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t*
       dst[b] = 1;
     }
   }
-  const int chunks_per_block = c->num_kv_heads * kBlock * c->head_dim * elem_bytes(c->dtype) / 16;
+  // fp8 pools: the code plane (tiles of 16 x head_dim bytes), then the exponent plane (16 bytes per tile).
+  const bool f8 = c->dtype == PA_FP8;
+  const int64_t code_block = (int64_t)c->num_kv_heads * kBlock * c->head_dim * elem_bytes(c->dtype);
+  const int chunks_per_block = (int)(code_block / 16);
+  const int64_t plane2 = f8 ? code_block * c->num_blocks : 0;
+  const int chunks2 = f8 ? c->num_kv_heads * kBlock / 16 : 0;
   const int mark = trace_begin(s);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, 2), dim3(256), 0, s, (uint8_t*)k_cache,
-                     (uint8_t*)v_cache, pairs, chunks_per_block, c->num_blocks);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, f8 ? 4 : 2), dim3(256), 0, s, (uint8_t*)k_cache,
+                     (uint8_t*)v_cache, pairs, chunks_per_block, c->num_blocks, plane2, chunks2);
   trace_end(s, mark, "copy_blocks");
   return launch_status("pa_copy_blocks");
 }

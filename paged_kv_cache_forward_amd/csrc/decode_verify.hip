@@ -54,11 +54,16 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;                 // one bf16 token row of one KV head
 constexpr int kTileBytes = kBlock * kRowBytes;    // one (block, KV head) tile: 4 KiB
+// fp8 pools: a plane of code tiles, per (block, KV head) 16 x 128 E4M3 codes
+// (K row-major, V transposed: byte d * 16 + row), 128-byte aligned; then a
+// plane of row exponents, 16 bytes per tile (E8M0, 2^(c - 127)).
+constexpr int kTileBytesF8 = kBlock * kD;
 constexpr int kMaxVerifySeqs = 1024;              // per-sequence tables kept in LDS
 constexpr int kMaxColGroups = 4;
 constexpr int kMaxVerifyTokens = 16;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 struct VerifyArgs {
   AttnArgs a;
@@ -91,10 +96,25 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p);
 }
 
-// fp32 -> bf16 bits, round to nearest even, for finite non-negative weights.
-__device__ __forceinline__ uint32_t weight_bits(float p) {
-  const uint32_t u = __float_as_uint(p);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Wait until at most OPS * t vector memory operations (t tiles' copies) are outstanding.
+template <int OPS>
+__device__ __forceinline__ void wait_ops(int t) {
+  if (t <= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPS) : "memory");
+  else if (t == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPS) : "memory");
+  else if (t == 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPS) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * OPS) : "memory");
+}
+
+// E8M0 exponent code -> 2^(c - 127) (codes 1..254; 255 gives inf, masked by the callers).
+__device__ __forceinline__ float e8m0(uint32_t c) { return __uint_as_float(c << 23); }
+
+// Eight E4M3 codes (memory order, two dwords) -> eight bf16, each times `scale`
+// (a power of two, so exact).
+__device__ __forceinline__ uint4 cvt8_fp8(uint32_t w0, uint32_t w1, float scale) {
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, false)),
+                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, scale, true)));
 }
 
 template <int CG>
@@ -104,11 +124,14 @@ struct VerifyState {
   f32x4_t acc[CG][8];   // O^T: column j, dims 16 db + 4 r .. +3
 };
 
-template <int G, int CG, int NS>
+template <int G, int CG, int NS, bool F8>
 __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   static_assert(16 % G == 0, "query heads per KV head must divide 16");
-  static_assert(NS >= 2 && NS <= 4, "tiles in flight");
+  static_assert(NS >= 2 && NS <= 5, "tiles in flight");
   constexpr int C = 16 * CG;
+  constexpr int TILE = F8 ? kTileBytesF8 : kTileBytes;   // bytes of one (block, KV head) code tile
+  constexpr int OPS = F8 ? 6 : 8;                        // copies per tile
+  constexpr int STAGE_U4 = F8 ? 260 : 512;               // one LDS stage, in 16-byte units
   extern __shared__ int s_dyn[];
   const AttnArgs& a = k.a;
   const int S = a.num_seqs;
@@ -118,10 +141,9 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   __shared__ int s_raw[2][64];                   // lookup windows: block-table entry (copied), sequence, logical block
   __shared__ int s_sj[2][2][64];
   __shared__ __attribute__((aligned(16))) uint4 s_q[CG * 4 * 64];   // query rows: [cg][ks][lane]
-  __shared__ __attribute__((aligned(16))) uint4 s_t0[512];          // tile stages: K [ks][lane], V [db][16 keys][16 dims]
-  __shared__ __attribute__((aligned(16))) uint4 s_t1[512];
-  __shared__ __attribute__((aligned(16))) uint4 s_t2[NS > 2 ? 512 : 1];
-  __shared__ __attribute__((aligned(16))) uint4 s_t3[NS > 3 ? 512 : 1];
+  // Tile stages.  bf16: K [ks][lane], V [db][16 keys][16 dims].  fp8: K codes
+  // [piece][lane], V codes [dim][16 keys], then 16 K and 16 V row exponents.
+  __shared__ __attribute__((aligned(16))) uint4 s_st[NS][STAGE_U4];
   const int Hkv = a.num_kv_heads;
   const int g = blockIdx.x % Hkv, rank = blockIdx.x / Hkv;
   const int lane = threadIdx.x;
@@ -202,8 +224,10 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   const int j = lane & 15, r = lane >> 4;
   const int hq0 = g * G;
   // Query rows of sequence `seq` -> s_q: copy (cg, ks) has lane (r, j) fetch
-  // dims 32 ks + 8 r .. +8 of column 16 cg + j.  The buffer range ends at the
-  // sequence's last query row, so columns past its tokens read zeros.
+  // the eight dims of column 16 cg + j that k-step ks pairs with this lane's
+  // K operand: 32 ks + 8 r .. +8 (bf16 cache), 64 (ks / 2) + 16 r + 8 (ks % 2)
+  // .. +8 (fp8 cache, whose K codes arrive 16 per lane).  The buffer range ends
+  // at the sequence's last query row, so columns past its tokens read zeros.
   auto copy_q = [&](int seq) {
     const int meta = __builtin_amdgcn_readfirstlane(s_meta[seq]);
     const int q0 = meta >> 5, nq = (meta & 31) + 1;
@@ -214,37 +238,61 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       const int col = 16 * cg + j;
       const int off = ((col / G) * a.num_q_heads + hq0 + col % G) * kRowBytes + r * 16;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) lds_copy16(rq, s_q + (cg * 4 + ks) * 64, off + ks * 64);
+      for (int ks = 0; ks < 4; ++ks)
+        lds_copy16(rq, s_q + (cg * 4 + ks) * 64, F8 ? off + r * 16 + (ks / 2) * 128 + (ks % 2) * 16 : off + ks * 64);
     }
   };
   copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]));
   int q_tile = -(NS - 1);   // tile whose issue followed the last query copy
 
-  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * kTileBytes;
-  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * kTileBytes;
-  const size_t block_stride = (size_t)Hkv * kTileBytes;
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * TILE;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * TILE;
+  const size_t block_stride = (size_t)Hkv * TILE;
+  // fp8: the exponent plane follows all code tiles.
+  const uint8_t* kx = (const uint8_t*)a.k_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
+  const uint8_t* vx = (const uint8_t*)a.v_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
   // K piece ks: lane (r, j) copies key j, dims 32 ks + 8 r .. +8.
   const int koff = j * kRowBytes + r * 16;
   // V piece e (dim blocks 2e, 2e+1): lane 32 dsel + 2 key + half copies key
   // `key`, dims 16 (2e + dsel) + 8 half .. +8, landing in row `key` of the
   // [16 keys][16 dims] sub-tile of dim block 2e + dsel.
   const int voff = ((lane & 31) >> 1) * kRowBytes + (lane >> 5) * 32 + (lane & 1) * 16;
-  auto stage = [&](int sI) -> uint4* { return sI == 0 ? s_t0 : sI == 1 ? s_t1 : sI == 2 ? s_t2 : s_t3; };
+  auto stage = [&](int sI) -> uint4* { return s_st[sI]; };
   auto issue = [&](int u, int sI) {
     const int w = (u >> 6) & 1, e = u & 63;
     const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[w][e]), a.num_blocks);
-    const int seq = __builtin_amdgcn_readfirstlane(s_sj[w][0][e]);
-    const int jt = __builtin_amdgcn_readfirstlane(s_sj[w][1][e]);
-    // Rows past the sequence read as zero.
-    const int bytes = __builtin_amdgcn_readfirstlane(min(s_len[seq] - jt * kBlock, kBlock) * kRowBytes);
     const size_t off = (size_t)bid * block_stride;
-    const u32x4_t rk = rsrc_words(kc + off, bytes);
-    const u32x4_t rv = rsrc_words(vc + off, bytes);
     uint4* dst = stage(sI);
+    if constexpr (F8) {
+      // K codes: piece p, lane (r, j) = key j's dims 64 p + 16 r .. +16.  V codes
+      // (stored transposed): piece p, lane l = dim 64 p + l, all 16 keys.  Then
+      // lanes 0..3 copy the 16 K and the 16 V row exponents.  Keys past the
+      // sequence are masked where they are used.
+      const u32x4_t rk = rsrc_words(kc + off, TILE);
+      const u32x4_t rv = rsrc_words(vc + off, TILE);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+      for (int p = 0; p < 2; ++p) lds_copy16(rk, dst + p * 64, j * kD + r * 16 + p * 64);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) lds_copy16(rv, dst + 256 + p * 64, voff + p * 64);
+      for (int p = 0; p < 2; ++p) lds_copy16(rv, dst + 128 + p * 64, (p * 64 + lane) * kBlock);
+      const size_t xoff = (size_t)bid * Hkv * kBlock;
+      const u32x4_t rkx = rsrc_words(kx + xoff, kBlock);
+      const u32x4_t rvx = rsrc_words(vx + xoff, kBlock);
+      if (lane < 4) {
+        lds_copy4(rkx, dst + 256, 4 * lane);
+        lds_copy4(rvx, (uint8_t*)(dst + 256) + 16, 4 * lane);
+      }
+    } else {
+      const int seq = __builtin_amdgcn_readfirstlane(s_sj[w][0][e]);
+      const int jt = __builtin_amdgcn_readfirstlane(s_sj[w][1][e]);
+      // Rows past the sequence read as zero.
+      const int bytes = __builtin_amdgcn_readfirstlane(min(s_len[seq] - jt * kBlock, kBlock) * kRowBytes);
+      const u32x4_t rk = rsrc_words(kc + off, bytes);
+      const u32x4_t rv = rsrc_words(vc + off, bytes);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) lds_copy16(rv, dst + 256 + p * 64, voff + p * 64);
+    }
   };
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, cnt - 1), s0);
@@ -255,14 +303,14 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
 
   VerifyState<CG> st;
   bf16x8_t qf[CG][4];
-  int cur = -1, cur_j0 = 0, cur_jl = 0, cur_q0 = 0, cur_n = 0, cga = 0, first_end = 0;
+  int cur = -1, cur_j0 = 0, cur_jl = 0, cur_q0 = 0, cur_n = 0, cga = 0, first_end = 0, cur_len = 0;
   int col_end[CG];
 
   auto finish = [&](int seq, bool whole) {
     const size_t slot = (size_t)g * k.slots + (size_t)(seq + rank);
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      if (cg >= cga) break;
+      if (cg > 0 && cg >= cga) break;   // group 0 is always active
       float lt = st.l[cg];
       lt += __shfl_xor(lt, 16);
       lt += __shfl_xor(lt, 32);
@@ -308,10 +356,13 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       if (seq != cur) {
         if (cur >= 0) finish(cur, cur_j0 == 0 && cur_jl + 1 == s_cum[cur + 1] - s_cum[cur]);
         cur = seq;
-        const int meta = s_meta[seq];
-        const int L = s_len[seq];
+        // Per-segment values are wave-uniform: kept in scalar registers so the
+        // per-tile branches on them are scalar branches.
+        const int meta = __builtin_amdgcn_readfirstlane(s_meta[seq]);
+        const int L = __builtin_amdgcn_readfirstlane(s_len[seq]);
         cur_q0 = meta >> 5;
         cur_n = (meta & 31) + 1;
+        cur_len = L;
         cga = min(CG, (cur_n * G + 15) / 16);
         first_end = a.causal ? L - cur_n + 1 : L;
 #pragma unroll
@@ -325,7 +376,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
         // This sequence's query copy was followed by the issues of tiles
         // q_tile .. u - 1 (eight copies each; at least one tile).
         __builtin_amdgcn_sched_barrier(0);
-        wait_tiles(min(u - q_tile, NS - 1));
+        wait_ops<OPS>(min(u - q_tile, NS - 1));
         const lds_u32x4_t* qs = (const lds_u32x4_t*)s_q;
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg)
@@ -354,25 +405,43 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       __builtin_amdgcn_sched_barrier(0);
       issue(min(u + NS - 1, cnt - 1), (sI + NS - 1) % NS);
       __builtin_amdgcn_sched_barrier(0);
-      wait_tiles(NS - 1);
+      wait_ops<OPS>(NS - 1);
       cur_jl = jt;
       const lds_u32x4_t* src = (const lds_u32x4_t*)stage(sI);
+      const uint8_t* sb = (const uint8_t*)stage(sI);
+      const int tok0 = jt * kBlock;
       uint4 kq[4];
+      uint32_t vexp = 0;
+      if constexpr (F8) {
+        // k-step ks = 2 p + h takes half h of piece p, converted exactly to bf16
+        // with key j's exponent.
+        const uint4 k0 = __builtin_bit_cast(uint4, src[lane]), k1 = __builtin_bit_cast(uint4, src[64 + lane]);
+        const float ks_scale = e8m0(sb[4096 + j]);
+        vexp = *reinterpret_cast<const uint32_t*>(sb + 4112 + 4 * r);   // V exponents of keys 4r .. 4r+3
+        kq[0] = cvt8_fp8(k0.x, k0.y, ks_scale);
+        kq[1] = cvt8_fp8(k0.z, k0.w, ks_scale);
+        kq[2] = cvt8_fp8(k1.x, k1.y, ks_scale);
+        kq[3] = cvt8_fp8(k1.z, k1.w, ks_scale);
+      } else {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
+        for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
+      }
 
       // Scores of the active column groups, base-2 units, masked past each column's end.
-      const int tok0 = jt * kBlock;
       float sc[CG][4];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        if (cg >= cga) break;
-        f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        if (cg > 0 && cg >= cga) break;   // group 0 is always active
+        // Two independent accumulation chains (k-steps 0, 2 and 1, 3), added at the end.
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[ks]), qf[cg][ks], s, 0, 0, 0);
+        for (int ks = 0; ks < 4; ks += 2) {
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[ks]), qf[cg][ks], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kq[ks + 1]), qf[cg][ks + 1], s1,
+                                                        0, 0, 0);
+        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sc[cg][e] = s[e] * a.scale_log2;
+        for (int e = 0; e < 4; ++e) sc[cg][e] = (s0[e] + s1[e]) * a.scale_log2;
         if (tok0 + kBlock > first_end) {   // wave-uniform: only a sequence's last tiles reach a column's end
 #pragma unroll
           for (int e = 0; e < 4; ++e) sc[cg][e] = tok0 + 4 * r + e < col_end[cg] ? sc[cg][e] : -INFINITY;
@@ -385,14 +454,14 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       float mx[CG];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        if (cg >= cga) break;
+        if (cg > 0 && cg >= cga) break;   // group 0 is always active
         mx[cg] = fmaxf(fmaxf(sc[cg][0], sc[cg][1]), fmaxf(sc[cg][2], sc[cg][3]));
         need |= mx[cg] > st.m[cg] + kRescaleSlack;
       }
       if (__any(need)) {
 #pragma unroll
         for (int cg = 0; cg < CG; ++cg) {
-          if (cg >= cga) break;
+          if (cg > 0 && cg >= cga) break;   // group 0 is always active
           float x = fmaxf(mx[cg], __shfl_xor(mx[cg], 16));
           x = fmaxf(x, __shfl_xor(x, 32));
           const float mn = x > st.m[cg] + kRescaleSlack ? x : st.m[cg];
@@ -404,28 +473,57 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
         }
       }
       // Weights (bf16, as the product uses them), their sums, and O^T += V^T P^T.
+      // fp8: the product takes each weight times its key's V exponent (exact),
+      // the sum the weight alone; keys past the sequence get weight 0 and
+      // their (stale) codes are zeroed.
+      f32x4_t vsc = {1.0f, 1.0f, 1.0f, 1.0f};
+      uint32_t vkeep = 0xffffffffu;
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vsc[e] = e8m0((vexp >> (8 * e)) & 0xffu);
+        if (tok0 + kBlock > cur_len) {   // wave-uniform: the sequence's last tile
+          const int live = min(max(cur_len - tok0 - 4 * r, 0), 4);   // valid keys among 4r .. 4r+3
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vsc[e] = e < live ? vsc[e] : 0.0f;
+          vkeep = live >= 4 ? 0xffffffffu : live == 0 ? 0u : (1u << (8 * live)) - 1u;
+        }
+      }
       s16x4_t pb[CG];
 #pragma unroll
       for (int cg = 0; cg < CG; ++cg) {
-        if (cg >= cga) break;
-        float sum = 0.0f;
+        if (cg > 0 && cg >= cga) break;   // group 0 is always active
+        f32x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t b = weight_bits(fast_exp2(sc[cg][e] - st.m[cg]));
-          pb[cg][e] = (short)b;
-          sum += __uint_as_float(b << 16);
-        }
-        st.l[cg] += sum;
+        for (int e = 0; e < 4; ++e) w[e] = fast_exp2(sc[cg][e] - st.m[cg]);
+        const bf16x4_t wb = __builtin_convertvector(w, bf16x4_t);   // nearest even
+        f32x4_t wr = __builtin_convertvector(wb, f32x4_t);          // exact
+        st.l[cg] += (wr[0] + wr[1]) + (wr[2] + wr[3]);
+        if constexpr (F8) pb[cg] = __builtin_bit_cast(s16x4_t, __builtin_convertvector(wr * vsc, bf16x4_t));
+        else pb[cg] = __builtin_bit_cast(s16x4_t, wb);
       }
-      const uint8_t* vst = (const uint8_t*)stage(sI) + 4096 + tr_off;
+      // All eight V^T operands are read before the first product, so their LDS
+      // latencies overlap.
+      const uint8_t* vst = F8 ? sb + 2048 + 16 * j + 4 * r : sb + 4096 + tr_off;
+      s16x4_t vt[8];
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const s16x4_t vt = lds_read_tr(vst + db * 512);
-#pragma unroll
-        for (int cg = 0; cg < CG; ++cg) {
-          if (cg >= cga) break;
-          st.acc[cg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb[cg], st.acc[cg][db], 0, 0, 0);
+        if constexpr (F8) {
+          // Lane (r, m): dim 16 db + m, keys 4r .. 4r+3 -- four codes of one transposed row.
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(vst + 256 * db) & vkeep;
+          const uint2 h = make_uint2(
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+          vt[db] = __builtin_bit_cast(s16x4_t, h);
+        } else {
+          vt[db] = lds_read_tr(vst + db * 512);
         }
+      }
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (cg > 0 && cg >= cga) break;   // group 0 is always active
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          st.acc[cg][db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt[db], pb[cg], st.acc[cg][db], 0, 0, 0);
       }
     }
   }
@@ -490,11 +588,11 @@ __global__ __launch_bounds__(256) void merge_verify_kernel(VerifyArgs k) {
   }
 }
 
-template <int G, int CG, int NS>
+template <int G, int CG, int NS, bool F8>
 pa_status launch_verify_gc(const VerifyArgs& k, hipStream_t s) {
   const int W = k.waves_per_head * k.a.num_kv_heads;
   int mark = trace_begin(s);
-  hipLaunchKernelGGL((decode_verify_kernel<G, CG, NS>), dim3(W), dim3(64), verify_dyn_lds(k.a.num_seqs), s, k);
+  hipLaunchKernelGGL((decode_verify_kernel<G, CG, NS, F8>), dim3(W), dim3(64), verify_dyn_lds(k.a.num_seqs), s, k);
   trace_end(s, mark, "decode_verify");
   pa_status st = launch_status("pa_forward (multi-token decode)");
   if (st != PA_OK) return st;
@@ -505,13 +603,18 @@ pa_status launch_verify_gc(const VerifyArgs& k, hipStream_t s) {
 }
 
 template <int G, int CG>
-pa_status launch_verify_g(const VerifyArgs& k, int depth, hipStream_t s) {
-  if (depth >= 4) return launch_verify_gc<G, CG, 4>(k, s);
-  if (depth == 3) return launch_verify_gc<G, CG, 3>(k, s);
-  return launch_verify_gc<G, CG, 2>(k, s);
+pa_status launch_verify_g(const VerifyArgs& k, int depth, bool f8, hipStream_t s) {
+  if (f8) return depth >= 5 ? launch_verify_gc<G, CG, 5, true>(k, s) : launch_verify_gc<G, CG, 3, true>(k, s);
+  if (depth >= 4) return launch_verify_gc<G, CG, 4, false>(k, s);
+  if (depth == 3) return launch_verify_gc<G, CG, 3, false>(k, s);
+  return launch_verify_gc<G, CG, 2, false>(k, s);
 }
 
 }  // namespace
+
+bool verify_fp8_supported(int32_t head_dim, int32_t group) {
+  return head_dim == kD && (group == 1 || group == 2 || group == 4 || group == 8);
+}
 
 VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len) {
@@ -519,11 +622,14 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   const int32_t G = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
   // PA_VERIFY=prefill sends these sequences to the chunked-prefill kernel;
   // PA_VERIFY=all routes single-token sequences here too (one launch for all).
+  // A quantised (fp8) cache always comes here, single-token sequences included.
+  const bool fp8 = dtype == PA_FP8;
   const char* env = std::getenv("PA_VERIFY");
-  if (env != nullptr && std::strcmp(env, "prefill") == 0) return vp;
-  const int32_t min_q = env != nullptr && std::strcmp(env, "all") == 0 ? 1 : 2;
-  if (!decode_mfma_supported(dtype, head_dim, G) || num_seqs < 1 || num_seqs > kMaxVerifySeqs ||
-      max_query_len < min_q || max_seq_len <= 0 || num_tokens >= (1 << 26))
+  if (!fp8 && env != nullptr && std::strcmp(env, "prefill") == 0) return vp;
+  const int32_t min_q = fp8 || (env != nullptr && std::strcmp(env, "all") == 0) ? 1 : 2;
+  const bool shape_ok = fp8 ? verify_fp8_supported(head_dim, G) : decode_mfma_supported(dtype, head_dim, G);
+  if (!shape_ok || num_seqs < 1 || num_seqs > kMaxVerifySeqs || max_query_len < min_q || max_seq_len <= 0 ||
+      num_tokens >= (1 << 26))
     return vp;
   // Columns (token, query head) in groups of 16: enough groups for the
   // longest multi-token sequence up to 16 tokens and 4 groups.
@@ -532,11 +638,14 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   int cg = (want * G + 15) / 16;
   if (cg == 3) cg = 4;
   vp.on = true;
+  vp.fp8 = fp8;
   vp.min_q = min_q;
   vp.col_groups = cg;
   vp.max_q = std::min(cap, 16 * cg / G);
-  // As the single-token decode: 1024 single-wave work-groups in all.
-  int64_t target = 1024;
+  // As the single-token decode: 1024 single-wave work-groups in all (one per
+  // SIMD).  fp8 with one column group: 2048 (two per SIMD fit its registers
+  // and LDS, and measured on MI355X they hide more of its per-tile latency).
+  int64_t target = fp8 && cg == 1 ? 2048 : 1024;
   if (const char* tw = std::getenv("PA_VERIFY_TOTAL_WAVES")) {
     const int v = std::atoi(tw);
     if (v >= 1 && v <= 65536) target = v;
@@ -544,12 +653,13 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   const int64_t whole_tiles = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
   const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(target / num_kv_heads, (int64_t)num_seqs * whole_tiles));
   vp.waves_per_head = (int32_t)wg;
-  // Three tiles in flight while four work-groups still fit in a CU's LDS, else
-  // two; PA_VERIFY_DEPTH=2..4 overrides.
-  vp.depth = verify_static_lds(cg, 3) + verify_dyn_lds(num_seqs) <= 40 * 1024 ? 3 : 2;
+  // bf16: three tiles in flight while four work-groups still fit in a CU's
+  // LDS, else two.  fp8: three (measured on MI355X: deeper rings of the
+  // half-size fp8 tiles were slower).  PA_VERIFY_DEPTH=2..5 overrides (fp8: 3 or 5).
+  vp.depth = fp8 ? 3 : verify_static_lds(cg, 3) + verify_dyn_lds(num_seqs) <= 40 * 1024 ? 3 : 2;
   if (const char* dp = std::getenv("PA_VERIFY_DEPTH")) {
     const int v = std::atoi(dp);
-    if (v >= 2 && v <= 4) vp.depth = v;
+    if (v >= 2 && v <= 5) vp.depth = v;
   }
   const size_t slots = (size_t)num_seqs + (size_t)wg;
   vp.info_bytes = round256((size_t)num_seqs * 2 * sizeof(int32_t));
@@ -562,16 +672,17 @@ pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p
                                int32_t* part_table, hipStream_t s) {
   VerifyArgs k{a, vp.min_q, vp.max_q, vp.waves_per_head, a.num_seqs + vp.waves_per_head, p_acc, p_ml, (int2*)part_table};
   const int G = a.num_q_heads / a.num_kv_heads;
+  const bool f8 = vp.fp8;
   switch (G * 16 + vp.col_groups) {
-    case 1 * 16 + 1: return launch_verify_g<1, 1>(k, vp.depth, s);
-    case 2 * 16 + 1: return launch_verify_g<2, 1>(k, vp.depth, s);
-    case 2 * 16 + 2: return launch_verify_g<2, 2>(k, vp.depth, s);
-    case 4 * 16 + 1: return launch_verify_g<4, 1>(k, vp.depth, s);
-    case 4 * 16 + 2: return launch_verify_g<4, 2>(k, vp.depth, s);
-    case 4 * 16 + 4: return launch_verify_g<4, 4>(k, vp.depth, s);
-    case 8 * 16 + 1: return launch_verify_g<8, 1>(k, vp.depth, s);
-    case 8 * 16 + 2: return launch_verify_g<8, 2>(k, vp.depth, s);
-    case 8 * 16 + 4: return launch_verify_g<8, 4>(k, vp.depth, s);
+    case 1 * 16 + 1: return launch_verify_g<1, 1>(k, vp.depth, f8, s);
+    case 2 * 16 + 1: return launch_verify_g<2, 1>(k, vp.depth, f8, s);
+    case 2 * 16 + 2: return launch_verify_g<2, 2>(k, vp.depth, f8, s);
+    case 4 * 16 + 1: return launch_verify_g<4, 1>(k, vp.depth, f8, s);
+    case 4 * 16 + 2: return launch_verify_g<4, 2>(k, vp.depth, f8, s);
+    case 4 * 16 + 4: return launch_verify_g<4, 4>(k, vp.depth, f8, s);
+    case 8 * 16 + 1: return launch_verify_g<8, 1>(k, vp.depth, f8, s);
+    case 8 * 16 + 2: return launch_verify_g<8, 2>(k, vp.depth, f8, s);
+    case 8 * 16 + 4: return launch_verify_g<8, 4>(k, vp.depth, f8, s);
     default:
       return fail(PA_ERR_UNSUPPORTED, "pa_forward: multi-token decode with %d query heads per KV head, %d column groups",
                   G, vp.col_groups);

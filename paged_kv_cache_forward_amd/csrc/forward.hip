@@ -43,9 +43,27 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
   fs->group = num_q_heads / c->num_kv_heads;
   if (fs->group != 1 && fs->group != 2 && fs->group != 4 && fs->group != 8)
     return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (built for 1, 2, 4, 8)", who, fs->group);
-  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
   fs->vplan = make_verify_plan(num_seqs, num_tokens, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype,
                                max_seq_len, max_query_len);
+  if (c->dtype == PA_FP8) {
+    // Quantised cache: every sequence goes through the multi-token decode
+    // kernel, which reads fp8 tiles; longer chunks have no fp8 kernel yet.
+    fs->plan = DecodePlan{};
+    fs->pplan = PrefillPlan{};
+    fs->pplan.pieces = 1;
+    fs->any_prefill = fs->use_mfma_prefill = false;
+    if (!verify_fp8_supported(c->head_dim, fs->group))
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with head_dim %d", who, c->head_dim);
+    if (num_seqs > 1024)
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with %d sequences (built for up to 1024)", who, num_seqs);
+    if (!fs->vplan.on && num_seqs > 0 && num_tokens > 0 && max_seq_len > 0 && max_query_len > 0)
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with %d tokens in one call", who, num_tokens);
+    if (fs->vplan.on && max_query_len > fs->vplan.max_q)
+      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with sequences of %d query tokens (built for up to %d)", who,
+                  max_query_len, fs->vplan.max_q);
+    return PA_OK;
+  }
+  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
   fs->any_prefill = max_query_len > 1 && !(fs->vplan.on && max_query_len <= fs->vplan.max_q);
   fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
   fs->pplan = make_prefill_plan(num_tokens, num_q_heads, c->head_dim, max_seq_len, max_query_len,

@@ -9,7 +9,8 @@
 
 namespace pa {
 
-inline int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+inline int elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_FP8 ? 1 : 2; }
+
 
 pa_status check_desc(const pa_cache_desc* c, const char* who);
 pa_status launch_status(const char* who);
@@ -100,6 +101,7 @@ pa_status launch_decode_balanced(const AttnArgs& a, const DecodePlan& plan, floa
 //   [partial (max, sum): fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][2]]
 struct VerifyPlan {
   bool on;
+  bool fp8;                // quantised pools (then it takes every sequence it can)
   int32_t min_q;           // 2, or 1 when it also takes the single-token sequences
   int32_t col_groups;      // 1, 2 or 4
   int32_t max_q;           // longest sequence (query tokens) it takes; longer ones go to prefill
@@ -109,6 +111,7 @@ struct VerifyPlan {
   size_t workspace_bytes() const { return info_bytes + acc_bytes + ml_bytes; }
 };
 
+bool verify_fp8_supported(int32_t head_dim, int32_t group);
 VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len);
 pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,

@@ -57,7 +57,10 @@ class DeviceRun:
         self.alloc = pa.BlockAllocator(wl.num_blocks, wl.block_size, order)
         self.ids, self.ctx_slots, self.new_slots, self.cow = _drive(wl, self.alloc)
 
-        shape = (wl.pool_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
+        if wl.cache == "fp8":
+            shape = pa.fp8_pool_shape(wl.pool_blocks, wl.num_kv_heads, wl.head_dim)
+        else:
+            shape = (wl.pool_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
         self.k_cache = self._pool(shape, fill)
         self.v_cache = self._pool(shape, fill)
         self.q = self.upload(wl.q)
@@ -94,6 +97,8 @@ class DeviceRun:
 
     def _pool(self, shape, fill):
         torch = self.torch
+        if self.wl.cache == "fp8":   # 0xff: a NaN code and a NaN scale in every byte
+            return torch.full(shape, 0 if fill == "zero" else 0xFF, dtype=torch.uint8, device=self.dev)
         if fill == "zero":
             return torch.zeros(shape, dtype=self.tdtype, device=self.dev)
         if self.tdtype == torch.float32:

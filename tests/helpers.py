@@ -13,11 +13,22 @@ BF16_NAN = np.uint16(0x7FC0)
 
 
 def nan_pool(wl):
-    """K and V pools of ``wl.pool_blocks`` blocks, every element NaN."""
+    """K and V pools of ``wl.pool_blocks`` blocks, every element NaN (fp8: every code and scale byte 0xff)."""
+    if wl.cache == "fp8":
+        return (oracle.fp8_pool(wl.pool_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size),
+                oracle.fp8_pool(wl.pool_blocks, wl.num_kv_heads, wl.head_dim, wl.block_size))
     shape = (wl.pool_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
     if wl.dtype == "f32":
         return np.full(shape, np.nan, dtype=np.float32), np.full(shape, np.nan, dtype=np.float32)
     return np.full(shape, BF16_NAN, dtype=np.uint16), np.full(shape, BF16_NAN, dtype=np.uint16)
+
+
+def _write_fp8(k_pool, v_pool, k, v, slots, block_size, chunk=1 << 16):
+    """Quantised write of bf16 rows (widened exactly), in chunks of tokens to bound memory."""
+    for a in range(0, len(slots), chunk):
+        b = min(len(slots), a + chunk)
+        oracle.ref_write_kv_fp8(k_pool, v_pool, oracle.to_f64(k[a:b], "bf16"), oracle.to_f64(v[a:b], "bf16"),
+                                slots[a:b], block_size)
 
 
 class OracleRun:
@@ -28,9 +39,10 @@ class OracleRun:
         self.alloc = oracle.RefAllocator(wl.num_blocks, wl.block_size, wl.free_order)
         self.ids, self.ctx_slots, self.new_slots, self.cow = workloads.drive(wl, self.alloc)
         self.k_cache, self.v_cache = nan_pool(wl)
-        oracle.ref_write_kv(self.k_cache, self.v_cache, wl.ctx_k, wl.ctx_v, self.ctx_slots, wl.block_size)
+        write = _write_fp8 if wl.cache == "fp8" else oracle.ref_write_kv
+        write(self.k_cache, self.v_cache, wl.ctx_k, wl.ctx_v, self.ctx_slots, wl.block_size)
         oracle.ref_copy_blocks(self.k_cache, self.v_cache, self.cow)
-        oracle.ref_write_kv(self.k_cache, self.v_cache, wl.k_new, wl.v_new, self.new_slots, wl.block_size)
+        write(self.k_cache, self.v_cache, wl.k_new, wl.v_new, self.new_slots, wl.block_size)
         self.tables = [self.alloc.block_table(self.ids[h]) for h in wl.batch]
         self.out = None
         if compute_out:
@@ -43,14 +55,14 @@ class OracleRun:
         if seqs is None:
             return oracle.ref_paged_attention(
                 wl.q, self.k_cache, self.v_cache, self.tables, wl.seq_lens, qsl,
-                wl.cached_lens, wl.scale, wl.causal, wl.block_size, wl.dtype)
+                wl.cached_lens, wl.scale, wl.causal, wl.block_size, wl.cache)
         out = np.full((wl.num_tokens, wl.num_q_heads, wl.head_dim), np.nan)
         for i in seqs:
             r0, r1 = int(qsl[i]), int(qsl[i + 1])
             sub = oracle.ref_paged_attention(
                 wl.q[r0:r1], self.k_cache, self.v_cache, [self.tables[i]],
                 wl.seq_lens[i:i + 1], np.array([0, r1 - r0]), wl.cached_lens[i:i + 1],
-                wl.scale, wl.causal, wl.block_size, wl.dtype)
+                wl.scale, wl.causal, wl.block_size, wl.cache)
             out[r0:r1] = sub
         return out
 

@@ -44,6 +44,9 @@ def check_parity(wl, seqs=None, pools=True):
     if pools:
         for dev_pool, ref_pool in ((gpu.k_cache, ref.k_cache), (gpu.v_cache, ref.v_cache)):
             h = gpu.host(dev_pool)
+            if wl.cache == "fp8":       # two planes (codes, then row exponents), compared byte for byte
+                assert np.array_equal(h.reshape(-1), ref_pool.flat)
+                continue
             assert h.shape == ref_pool.shape
             assert np.array_equal(h.view(np.uint8), ref_pool.view(np.uint8))
     got = gpu.out_f64()
@@ -65,10 +68,10 @@ def test_mini_workloads(name):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_decode", "batched_decode", "mixed_superbatch", "shared_prefix_cow",
-                                  "spec_verify"])
+                                  "spec_verify", "batched_decode_fp8"])
 def test_named_workloads_full_size(name):
     wl = workloads.named(name)
-    check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch"))
+    check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch", "batched_decode_fp8"))
 
 
 @pytest.mark.timeout(1200)
@@ -319,3 +322,96 @@ def test_error_paths(monkeypatch):
     pa.pa_forward(run.out, run.q, run.k_cache, run.v_cache, bad, run.seq_lens, run.qsl,
                   run.cached_lens, wl.max_seq_len, 1, wl.scale, True, workspace=run.workspace)
     torch.cuda.synchronize()
+
+
+# -- quantised (fp8) cache ------------------------------------------------------
+
+FP8_MINIS = ("decode_fp8", "verify_fp8", "fp8_gqa8", "fp8_mha_noncausal")
+
+
+def test_fp8_write_edge_rows():
+    """Quantised write, bit for bit against the oracle: zero rows, -0, bf16 subnormals, the
+    largest bf16 values, exact rounding ties, padding and out-of-pool slots."""
+    pa = ensure_library()
+    import torch
+    from helpers import _write_fp8
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7)
+    NB, Hkv, D, B = 5, 2, 128, 16
+    rows = [np.zeros(D), -np.zeros(D), np.full(D, 2.0 ** -130), np.linspace(-3e38, 3e38, D),
+            np.concatenate([[448.0], 1 + np.arange(1, D) / 16.0 * 0.0625]),        # amax 448: ties at 1/16 steps
+            np.concatenate([[1.0], np.full(D - 1, 1 + 1 / 16)]),
+            np.concatenate([[2.0 ** -120], np.full(D - 1, 3 * 2.0 ** -130)]),
+            rng.standard_normal(D) * 1e-3, rng.standard_normal(D) * 1e3]
+    T = len(rows)
+    x = np.stack(rows)[:, None, :].repeat(Hkv, axis=1)
+    x[:, 1] *= -0.75
+    k = workloads.bf16_bits(x.astype(np.float32))
+    v = workloads.bf16_bits((x[:, :, ::-1] * 0.5).astype(np.float32))
+    slots = np.array([3, -1, 17, 79, 40, NB * B + 2, 65, 0, 50], dtype=np.int64)
+    kp = oracle.fp8_pool(NB, Hkv, D)
+    vp = oracle.fp8_pool(NB, Hkv, D)
+    keep = slots < NB * B
+    _write_fp8(kp, vp, k[keep], v[keep], slots[keep], B)
+    kd = torch.full(pa.fp8_pool_shape(NB, Hkv, D), 0xFF, dtype=torch.uint8, device=dev)
+    vd = torch.full_like(kd, 0xFF)
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    pa.pa_write_kv(dev_bf16(k), dev_bf16(v), kd, vd, torch.from_numpy(slots).to(dev))
+    assert np.array_equal(kd.cpu().numpy().reshape(-1), kp.flat)
+    assert np.array_equal(vd.cpu().numpy().reshape(-1), vp.flat)
+
+
+def test_fp8_copy_blocks_bit_exact():
+    pa = ensure_library()
+    import torch
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(8)
+    kc, vc = oracle.fp8_pool(9, 8, 128), oracle.fp8_pool(9, 8, 128)
+    kc.flat[:] = rng.integers(0, 256, size=kc.flat.shape, dtype=np.uint8)
+    vc.flat[:] = rng.integers(0, 256, size=vc.flat.shape, dtype=np.uint8)
+    pairs = [(1, 4), (2, 7), (8, 0)]
+    shape = pa.fp8_pool_shape(9, 8, 128)
+    kd = torch.from_numpy(kc.flat.reshape(shape).copy()).to(dev)
+    vd = torch.from_numpy(vc.flat.reshape(shape).copy()).to(dev)
+    pa.pa_copy_blocks(kd, vd, torch.tensor(pairs, dtype=torch.int32, device=dev))
+    oracle.ref_copy_blocks(kc, vc, pairs)
+    assert np.array_equal(kd.cpu().numpy().reshape(-1), kc.flat)
+    assert np.array_equal(vd.cpu().numpy().reshape(-1), vc.flat)
+
+
+@pytest.mark.parametrize("waves,depth", [("1", "5"), ("7", "3"), ("1024", "5"), ("65536", "3")])
+def test_fp8_wave_counts_and_depths(waves, depth, monkeypatch):
+    monkeypatch.setenv("PA_VERIFY_TOTAL_WAVES", waves)
+    monkeypatch.setenv("PA_VERIFY_DEPTH", depth)
+    for name in FP8_MINIS:
+        check_parity(workloads.mini(name), pools=False)
+
+
+def test_fp8_invariances():
+    """Placement, stale bytes (0xff codes and scales vs zeros) and table padding change no output bit."""
+    wl = workloads.mini("verify_fp8")
+    base = _device_run(wl)
+    ref_bits = base.host(base.out)
+    alt = np.random.default_rng(97).permutation(wl.num_blocks).astype(np.int32)
+    moved = _device_run(wl, free_order=alt)
+    assert moved.tables != base.tables
+    assert np.array_equal(moved.host(moved.out), ref_bits)
+    zero = _device_run(wl, fill="zero")
+    assert np.array_equal(zero.host(zero.out), ref_bits)
+    wide = _device_run(wl, table_stride=max(len(t) for t in base.tables) + 7)
+    assert np.array_equal(wide.host(wide.out), ref_bits)
+
+
+def test_fp8_unsupported_shapes():
+    """Chunks longer than the multi-token cap have no fp8 kernel yet: refused before any launch."""
+    pa = ensure_library()
+    import ctypes
+    desc = pa.CacheDesc(100, 8, 128, 16, pa.PA_FP8)
+    assert pa.lib.pa_forward_workspace_size(4, 600, 32, 4096, 512, ctypes.byref(desc)) == 0
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 600, 32, 4096, 512,
+                           ctypes.byref(desc), 0.1, 1, None, 0, None)
+    assert st == pa.PA_ERR_UNSUPPORTED and "fp8" in pa.lib.pa_last_error().decode()
+    desc64 = pa.CacheDesc(100, 8, 64, 16, pa.PA_FP8)
+    st = pa.lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(desc64), None)
+    assert st == pa.PA_ERR_UNSUPPORTED

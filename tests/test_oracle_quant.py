@@ -116,7 +116,8 @@ def test_write_layout_against_row_by_row_reconstruction():
     slots = rng.permutation(NB * B)[:T]
     slots[4] = -1                                   # padding token: skipped
     oracle.ref_write_kv_fp8(kp, vp, k, v, slots, B)
-    touched = np.zeros(kp.shape, dtype=bool)
+    touched = np.zeros(kp.flat.shape, dtype=bool)
+    n = NB * Hkv
     for t, s in enumerate(slots):
         if s < 0:
             continue
@@ -124,13 +125,15 @@ def test_write_layout_against_row_by_row_reconstruction():
         for h in range(Hkv):
             kc, ke = oracle.quantize_rows(k[t, h][None])
             vc, ve = oracle.quantize_rows(v[t, h][None])
+            tile = (blk * Hkv + h) * B * D                           # code plane: tiles of B*D bytes
             for d in range(D):
-                assert kp[blk, h, row * D + d] == kc[0, d]          # K row-major
-                assert vp[blk, h, d * B + row] == vc[0, d]          # V transposed
-                touched[blk, h, row * D + d] = True
-            assert kp[blk, h, B * D + row] == ke[0] and vp[blk, h, B * D + row] == ve[0]
-            touched[blk, h, B * D + row] = True
-    assert np.all(kp[~touched] == 0xFF)                              # nothing else written
+                assert kp.flat[tile + row * D + d] == kc[0, d]       # K row-major
+                assert vp.flat[tile + d * B + row] == vc[0, d]       # V transposed
+                touched[tile + row * D + d] = True
+            ex = n * B * D + (blk * Hkv + h) * B + row               # exponent plane after the codes
+            assert kp.flat[ex] == ke[0] and vp.flat[ex] == ve[0]
+            touched[ex] = True
+    assert np.all(kp.flat[~touched] == 0xFF)                         # nothing else written
     # gathering through a table returns each token's own dequantised row
     table = list(range(NB))
     Kg = oracle.gather_logical_fp8(kp, table, NB * B, B, "k")

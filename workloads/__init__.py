@@ -68,6 +68,11 @@ class Workload:
     trace: list
     block_size: int = BLOCK_SIZE
     notes: dict = field(default_factory=dict)
+    cache_dtype: str = ""         # "" = the same as dtype; "fp8" = quantised pools, bf16 rows
+
+    @property
+    def cache(self):
+        return self.cache_dtype or self.dtype
 
     @property
     def num_seqs(self):
@@ -145,7 +150,7 @@ def block_table_array(wl, alloc, ids, stride=None):
 # -- builders ----------------------------------------------------------------
 
 def independent(name, seed, *, Hq, Hkv, D, dtype, cached, new, num_blocks=None,
-                pool_factor=None, pool_extra=0, causal=True, scale=None, notes=None):
+                pool_factor=None, pool_extra=0, causal=True, scale=None, notes=None, cache_dtype=""):
     """Sequences with private blocks: sequence i holds cached[i] tokens and adds new[i].
 
     The trace creates every sequence and appends its cached tokens in batch
@@ -182,7 +187,7 @@ def independent(name, seed, *, Hq, Hkv, D, dtype, cached, new, num_blocks=None,
         num_blocks=num_blocks, free_order=free_order, batch=list(range(S)),
         seq_lens=(cached + new).astype(np.int32), cached_lens=cached.astype(np.int32),
         query_lens=new.astype(np.int32), q=q, k_new=k_new, v_new=v_new,
-        ctx_k=ctx_k, ctx_v=ctx_v, trace=trace, notes=dict(notes or {}))
+        ctx_k=ctx_k, ctx_v=ctx_v, trace=trace, notes=dict(notes or {}), cache_dtype=cache_dtype)
 
 
 def shared_prefix(name, seed, *, Hq, Hkv, D, dtype, num_seqs, prefix, suffix_max,
@@ -283,6 +288,13 @@ def spec_verify():
                        cached=L - n, new=n, num_blocks=20000)
 
 
+def batched_decode_fp8():
+    """batched_decode on a quantised (fp8) cache: the same rows, stored as E4M3 codes with row scales."""
+    L = _lengths(np.random.Generator(np.random.PCG64(1002)), 128, 4096, 64)
+    return independent("batched_decode_fp8", 2, Hq=32, Hkv=8, D=128, dtype="bf16",
+                       cached=L - 1, new=np.ones(64, dtype=np.int64), num_blocks=20000, cache_dtype="fp8")
+
+
 NAMED = {
     "tiny_decode": tiny_decode,
     "batched_decode": batched_decode,
@@ -290,6 +302,7 @@ NAMED = {
     "mixed_superbatch": mixed_superbatch,
     "shared_prefix_cow": shared_prefix_cow,
     "spec_verify": spec_verify,
+    "batched_decode_fp8": batched_decode_fp8,
 }
 
 
@@ -367,6 +380,26 @@ def mini(name):
         new = np.array([16, 4, 11])
         return independent(name, 24, Hq=8, Hkv=8, D=128, dtype="bf16", cached=cached,
                            new=new, pool_extra=2)
+    if name == "decode_fp8":
+        rng = np.random.Generator(np.random.PCG64(25))
+        L = np.concatenate([[1, 16, 17, 513], rng.integers(2, 2500, size=4)])
+        return independent(name, 25, Hq=32, Hkv=8, D=128, dtype="bf16", cached=L - 1,
+                           new=np.ones(len(L), dtype=np.int64), pool_extra=5, cache_dtype="fp8")
+    if name == "verify_fp8":
+        cached = np.array([0, 1, 15, 16, 300, 1021, 47, 5])
+        new = np.array([2, 3, 8, 16, 1, 4, 2, 1])
+        return independent(name, 26, Hq=32, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=3, cache_dtype="fp8")
+    if name == "fp8_gqa8":
+        cached = np.array([700, 3, 2047, 64, 0])
+        new = np.array([1, 6, 2, 8, 1])
+        return independent(name, 27, Hq=64, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=2, cache_dtype="fp8")
+    if name == "fp8_mha_noncausal":
+        cached = np.array([130, 0, 999])
+        new = np.array([16, 4, 1])
+        return independent(name, 28, Hq=8, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=2, cache_dtype="fp8", causal=False)
     if name == "shared_bf16":
         return shared_prefix(name, 21, Hq=32, Hkv=8, D=128, dtype="bf16", num_seqs=9,
                              prefix=160, suffix_max=70, num_blocks=200)
@@ -375,4 +408,5 @@ def mini(name):
 
 MINI = ["decode_f32", "decode_bf16", "decode_gqa8", "decode_d64_bf16", "decode_d128_f32",
         "mixed_bf16", "mixed_gqa8", "mixed_mha_d64", "prefill_f32", "noncausal_bf16",
-        "shared_bf16", "verify_bf16", "verify_gqa8", "verify_mha"]
+        "shared_bf16", "verify_bf16", "verify_gqa8", "verify_mha", "decode_fp8", "verify_fp8", "fp8_gqa8",
+        "fp8_mha_noncausal"]
