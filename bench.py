@@ -539,6 +539,23 @@ def main():
         }
         del frun
         torch.cuda.empty_cache()
+        # the four 512-token chunks of the mixed batch on an fp8 cache (forward only)
+        mix = workloads.mixed_superbatch()
+        sel = [i for i in range(mix.num_seqs) if mix.query_lens[i] > 1]
+        fpre = workloads.independent("mixed_prefill_chunks_fp8", 4, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                     cached=mix.cached_lens[sel], new=mix.query_lens[sel], pool_factor=1.25,
+                                     cache_dtype="fp8")
+        fprun = DeviceRun(fpre, fill="zero", copies=2)
+        run_steps(fprun, 3, stream, with_writes=False)
+        fpper = traced_region(pa, fprun, max(5, args.steps // 5), stream, with_writes=False)
+        fpms = mean(fpper["prefill"])
+        ftf = prefill_flops(fpre) / (fpms * 1e-3) / 1e12
+        res["fp8_decode"]["prefill"] = {"workload": "4 chunks x 512 tokens on 0/1024/4096/8192 cached, fp8 cache",
+                                        "kernel": "prefill", "ms": round(fpms, 5), "tflops": round(ftf, 2),
+                                        "mfma_util": round(ftf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                        "kernel_ms": {k: round(mean(v), 5) for k, v in fpper.items()}}
+        del fprun
+        torch.cuda.empty_cache()
 
     if not args.no_graph:
         log("graph leg: one step per launch vs replayed from a HIP graph (tiny and batched decode)")

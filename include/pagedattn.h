@@ -179,7 +179,9 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  * decoding step, "vLLM PagedAttention: eine Revolution ..." (de.news.hada.io),
  * bullet "Guided and Speculative Decoding") run a multi-token decode path of
  * the same split-KV kind; longer ones run the chunked-prefill path (bf16:
- * matrix cores; long key ranges likewise cut into pieces and merged).
+ * matrix cores; long key ranges likewise cut into pieces and merged).  On a
+ * PA_FP8 cache (head_dim 128) single-token sequences take the multi-token
+ * path too, and every path reads the exact dequantised values.
  *
  *   out, q           device, [num_tokens][num_q_heads][head_dim], c->dtype
  *   k_cache, v_cache device pools (read only)

@@ -46,21 +46,19 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
   fs->vplan = make_verify_plan(num_seqs, num_tokens, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype,
                                max_seq_len, max_query_len);
   if (c->dtype == PA_FP8) {
-    // Quantised cache: every sequence goes through the multi-token decode
-    // kernel, which reads fp8 tiles; longer chunks have no fp8 kernel yet.
+    // Quantised cache: sequences of up to max_q query tokens go through the
+    // multi-token decode kernel, longer ones through the chunked-prefill
+    // kernel; both read fp8 tiles.
     fs->plan = DecodePlan{};
-    fs->pplan = PrefillPlan{};
-    fs->pplan.pieces = 1;
-    fs->any_prefill = fs->use_mfma_prefill = false;
     if (!verify_fp8_supported(c->head_dim, fs->group))
       return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with head_dim %d", who, c->head_dim);
     if (num_seqs > 1024)
       return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with %d sequences (built for up to 1024)", who, num_seqs);
     if (!fs->vplan.on && num_seqs > 0 && num_tokens > 0 && max_seq_len > 0 && max_query_len > 0)
       return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with %d tokens in one call", who, num_tokens);
-    if (fs->vplan.on && max_query_len > fs->vplan.max_q)
-      return fail(PA_ERR_UNSUPPORTED, "%s: fp8 cache with sequences of %d query tokens (built for up to %d)", who,
-                  max_query_len, fs->vplan.max_q);
+    fs->any_prefill = fs->use_mfma_prefill = fs->vplan.on && max_query_len > fs->vplan.max_q;
+    fs->pplan = make_prefill_plan(num_tokens, num_q_heads, c->head_dim, max_seq_len, max_query_len,
+                                  fs->use_mfma_prefill);
     return PA_OK;
   }
   fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
@@ -185,7 +183,7 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
     pre_ml = (float*)(pbase + fs.pplan.o_bytes);
   }
   if (fs.use_mfma_prefill) {
-    st = launch_prefill(a, max_query_len, fs.pplan, pre_o, pre_ml, s);
+    st = launch_prefill(a, max_query_len, fs.pplan, pre_o, pre_ml, c->dtype == PA_FP8, s);
     if (st != PA_OK) return st;
   }
   if (fs.vplan.on) {

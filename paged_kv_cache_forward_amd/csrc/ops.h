@@ -135,10 +135,10 @@ struct PrefillPlan {
 PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
                               int32_t max_query_len, bool mfma);
 
-// Chunked-prefill (MFMA) kernel for bf16 sequences with more than one query
-// token, followed by its merge when the plan splits key ranges.
+// Chunked-prefill (MFMA) kernel for bf16 (or fp8-cache) sequences with more
+// than one query token, followed by its merge when the plan splits key ranges.
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
 pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
-                         hipStream_t s);
+                         bool fp8, hipStream_t s);
 
 }  // namespace pa

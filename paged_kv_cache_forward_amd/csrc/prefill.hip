@@ -93,6 +93,29 @@ __device__ __forceinline__ u32x4_t buf_ld16v(__amdgpu_buffer_rsrc_t r, int voff)
   return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
 }
 
+// fp8 caches (head_dim 128): a plane of code tiles, 16 x 128 E4M3 codes per
+// (block, KV head) -- K row-major, V transposed (byte d * 16 + row) -- then a
+// plane of row exponents (E8M0, 16 bytes per tile).  A stage holds a tile's
+// raw codes and exponents; fragments are converted to bf16 as they are read
+// (exactly: power-of-two scales).  Stage layout: K codes of the four blocks
+// (2 KiB each, piece p of block b at b * 2048 + p * 1024: lane (lq, lr) = key
+// lr, dims 64 p + 16 lq .. +16), V codes (2 KiB each, as stored), then the K
+// and the V exponents (16 bytes per block).
+constexpr int kF8Tile = kBlock * 128;
+constexpr int kF8V = 4 * kF8Tile, kF8KX = 8 * kF8Tile, kF8VX = kF8KX + 4 * kBlock;
+constexpr int kF8Stage = kF8VX + 4 * kBlock;
+
+__device__ __forceinline__ float e8m0f(uint32_t c) { return __uint_as_float(c << 23); }
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2_fp8(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI));
+}
+// Eight E4M3 codes (two dwords, memory order) -> eight bf16, times `scale`.
+__device__ __forceinline__ bf16x8_t cvt8_fp8(uint32_t w0, uint32_t w1, float scale) {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(cvt2_fp8<false>(w0, scale), cvt2_fp8<true>(w0, scale),
+                                                 cvt2_fp8<false>(w1, scale), cvt2_fp8<true>(w1, scale)));
+}
+
 __device__ __forceinline__ s16x4_t lds_read_tr(const lds_u8* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
 }
@@ -124,10 +147,12 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
   return it;
 }
 
-template <int D>
+template <int D, bool F8>
 __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillArgs pk) {
   using C = PCfg<D>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_stage[2 * C::BUF];
+  static_assert(!F8 || (D == 128 && kWavesPerBlock == 1), "fp8: head_dim 128, one wave per block");
+  constexpr int SBUF = F8 ? kF8Stage : C::BUF;   // bytes of one LDS stage
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_stage[2 * SBUF];
   __shared__ int s_bt[kBtCache];
   lds_u8* const lds = (lds_u8*)lds_stage;
 
@@ -173,7 +198,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   int cur_win = kt0 * (kKeys / kBlock) / kBtCache;
   fill_window(cur_win);
 
-  // Query fragments (B operand of S^T = K Q^T): lane holds 8 head-dim values of its row.
+  // Query fragments (B operand of S^T = K Q^T): lane holds 8 head-dim values of
+  // its row: dims 32 ks + 8 lq (bf16 cache); 64 (ks / 2) + 16 lq + 8 (ks % 2)
+  // (fp8 cache, matching the K fragments it converts 16 codes at a time).
   bf16x8_t qf[2][C::KS];
   int row_tok[2], row_head[2];
 #pragma unroll
@@ -186,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
         (const uint8_t*)a.q + ((size_t)(q0 + row_tok[rt]) * a.num_q_heads + row_head[rt]) * C::ROW;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const uint4 v = ok ? ld16(qp + ks * 64 + lq * 16) : make_uint4(0u, 0u, 0u, 0u);
+      const int qoff = F8 ? (ks / 2) * 128 + lq * 32 + (ks % 2) * 16 : ks * 64 + lq * 16;
+      const uint4 v = ok ? ld16(qp + qoff) : make_uint4(0u, 0u, 0u, 0u);
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -222,9 +250,13 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   const int lim0 = a.causal ? min(L, c + row_tok[0] + 1) : L;
   const int lim1 = a.causal ? min(L, c + row_tok[1] + 1) : L;
 
-  const size_t block_stride = (size_t)Hkv * C::TILE;
-  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * C::TILE;
-  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * C::TILE;
+  constexpr int CTILE = F8 ? kF8Tile : C::TILE;      // bytes of one (block, KV head) code tile
+  const size_t block_stride = (size_t)Hkv * CTILE;
+  const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * CTILE;
+  const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * CTILE;
+  // fp8: the exponent plane after all code tiles, 16 bytes per tile.
+  const uint8_t* kx = (const uint8_t*)a.k_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
+  const uint8_t* vx = (const uint8_t*)a.v_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
 
   __syncthreads();   // first block-table window ready
 
@@ -250,16 +282,34 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
     const int rows = __builtin_amdgcn_readfirstlane(blk < nblk ? min(max(L - blk * kBlock, 0), kBlock) : 0);
     const int bid = rows > 0 ? block_id(blk) : 0;
     const size_t off = (size_t)bid * block_stride;
+    const int b = w / kWavesPerBlock;
+    if constexpr (F8) {
+      // K codes (rows past the sequence read as zero), V codes (masked where
+      // read), and lanes 0..3 copy the block's 16 K and 16 V exponents.
+      const u32x4_t rk = rsrc_words(kc + off, rows * 128);
+      const u32x4_t rv = rsrc_words(vc + off, kF8Tile);
+      const u32x4_t rkx = rsrc_words(kx + (size_t)bid * Hkv * kBlock, kBlock);
+      const u32x4_t rvx = rsrc_words(vx + (size_t)bid * Hkv * kBlock, kBlock);
+      uint8_t* st8 = lds_stage + buf * SBUF;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) lds_copy16(rk, st8 + b * kF8Tile + p * 1024, lr * 128 + p * 64 + lq * 16);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) lds_copy16(rv, st8 + kF8V + b * kF8Tile + p * 1024, p * 1024 + lane * 16);
+      if (lane < 4) {
+        lds_copy4(rkx, st8 + kF8KX + b * kBlock, 4 * lane);
+        lds_copy4(rvx, st8 + kF8VX + b * kBlock, 4 * lane);
+      }
+      return;
+    }
     const u32x4_t rk = rsrc_words(kc + off, rows * C::ROW);
     const u32x4_t rv = rsrc_words(vc + off, rows * C::ROW);
-    const int b = w / kWavesPerBlock;
     if (kWavesPerBlock == 1 || part == 0) {   // the block's K pieces
-      uint8_t* kdst = lds_stage + buf * C::BUF + b * C::KS * 1024;
+      uint8_t* kdst = lds_stage + buf * SBUF + b * C::KS * 1024;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) lds_copy16(rk, kdst + ks * 1024, lr * C::ROW + ks * 64 + lq * 16);
     }
     if (kWavesPerBlock == 1 || part == 1) {   // its V pieces
-      uint8_t* vdst = lds_stage + buf * C::BUF + C::KBUF + b * (C::DT / 2) * 1024;
+      uint8_t* vdst = lds_stage + buf * SBUF + C::KBUF + b * (C::DT / 2) * 1024;
 #pragma unroll
       for (int dp = 0; dp < C::DT / 2; ++dp)
         lds_copy16(rv, vdst + dp * 1024, vr2 * C::ROW + (2 * dp + dsel) * 32 + vh * 16);
@@ -316,37 +366,93 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   auto compute = [&](int kt, int buf) {
     const int key0 = kt * kKeys;
     if (a.causal && key0 > c + wave_tok_last) return;   // past every row of this wave
-    const lds_u8* kl = k_lane + buf * C::BUF;
-    const lds_u8* vl = v_lane + buf * C::BUF;
+    const lds_u8* kl = k_lane + buf * SBUF;
+    const lds_u8* vl = v_lane + buf * SBUF;
+    const lds_u8* st8 = lds + buf * SBUF;
     f32x4_t s[2][4];
 #pragma unroll
     for (int kt16 = 0; kt16 < 4; ++kt16) {
       s[0][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       s[1][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F8) {
+        // Block kt16: each 16-code piece gives two k-steps, converted with key lr's scale.
+        const float ksc = e8m0f(st8[kF8KX + kt16 * kBlock + lr]);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8_t kf =
-            *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(kl + (kt16 * C::KS + ks) * 1024);
-        s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
-        s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
+        for (int p = 0; p < 2; ++p) {
+          const uint4 raw = __builtin_bit_cast(
+              uint4, *reinterpret_cast<const lds_u32x4_t*>(st8 + kt16 * kF8Tile + p * 1024 + lane * 16));
+          const bf16x8_t k0 = cvt8_fp8(raw.x, raw.y, ksc), k1 = cvt8_fp8(raw.z, raw.w, ksc);
+          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][2 * p], s[0][kt16], 0, 0, 0);
+          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][2 * p], s[1][kt16], 0, 0, 0);
+          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][2 * p + 1], s[0][kt16], 0, 0, 0);
+          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][2 * p + 1], s[1][kt16], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const bf16x8_t kf =
+              *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(kl + (kt16 * C::KS + ks) * 1024);
+          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
+          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
+        }
       }
       if (kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
     }
     bf16x8_t pb[2][2];
     softmax_tile(s, key0, pb);
+    if constexpr (F8) {
+      // P.V on the fp8 codes: the product takes each weight times its key's V
+      // exponent (exact), the row sums (ones tile) the weights alone.  Keys
+      // past the sequence: weight 0 and codes zeroed (stale bytes may be NaN codes).
+      bf16x8_t pv[2][2];
+      uint32_t keep[2][2];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+      for (int ks2 = 0; ks2 < 2; ++ks2)
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        // keys 32 ks2 + 4 lq + lr / 4 (block 2 ks2) and 16 further (block 2 ks2 + 1)
-        const lds_u8* vp = vl + (2 * ks2 * (C::DT / 2) + dt / 2) * 1024 + (dt & 1) * 512;
-        const s16x4_t v0 = lds_read_tr(vp);
-        const s16x4_t v1 = lds_read_tr(vp + (C::DT / 2) * 1024);
-        const bf16x8_t vf = __builtin_bit_cast(
-            bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
-        o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
-      }
+        for (int h = 0; h < 2; ++h) {
+          const int blk = 2 * ks2 + h;
+          const uint32_t xw = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+              st8 + kF8VX + blk * kBlock + 4 * lq);
+          int live = 4;
+          if (key0 + kKeys > L) live = min(max(L - key0 - 16 * blk - 4 * lq, 0), 4);   // wave-uniform test
+          keep[ks2][h] = live >= 4 ? 0xffffffffu : live == 0 ? 0u : (1u << (8 * live)) - 1u;
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sv = e < live ? e8m0f((xw >> (8 * e)) & 0xffu) : 0.0f;
+              pv[rt][ks2][4 * h + e] = static_cast<__bf16>(static_cast<float>(pb[rt][ks2][4 * h + e]) * sv);
+            }
+        }
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          // keys 4 lq .. +3 of blocks 2 ks2 and 2 ks2 + 1, dim 16 dt + lr: one dword of each block's row
+          const lds_u8* vp = st8 + kF8V + (16 * dt + lr) * kBlock + 4 * lq;
+          const uint32_t w0 = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+                                  vp + (2 * ks2) * kF8Tile) & keep[ks2][0];
+          const uint32_t w1 = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
+                                  vp + (2 * ks2 + 1) * kF8Tile) & keep[ks2][1];
+          const bf16x8_t vf = cvt8_fp8(w0, w1, 1.0f);
+          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[0][ks2], o[0][dt], 0, 0, 0);
+          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[1][ks2], o[1][dt], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          // keys 32 ks2 + 4 lq + lr / 4 (block 2 ks2) and 16 further (block 2 ks2 + 1)
+          const lds_u8* vp = vl + (2 * ks2 * (C::DT / 2) + dt / 2) * 1024 + (dt & 1) * 512;
+          const s16x4_t v0 = lds_read_tr(vp);
+          const s16x4_t v1 = lds_read_tr(vp + (C::DT / 2) * 1024);
+          const bf16x8_t vf = __builtin_bit_cast(
+              bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
+          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
+        }
+    }
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
       o[0][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ks2], o[0][C::DT], 0, 0, 0);
@@ -461,7 +567,9 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128) && group >= 1 && kRowsPerWG % group == 0;
+  if (group < 1 || kRowsPerWG % group != 0) return false;
+  if (dtype == PA_FP8) return head_dim == 128;
+  return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128);
 }
 
 PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t head_dim, int32_t max_seq_len,
@@ -489,7 +597,7 @@ PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t h
 }
 
 pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
-                         hipStream_t s) {
+                         bool fp8, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int TOK = kRowsPerWG / G;
   const int qtiles = (max_query_len + TOK - 1) / TOK;
@@ -502,11 +610,14 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   if (pp.pieces > 1 && (p_o == nullptr || p_ml == nullptr))
     return fail(PA_ERR_ARG, "pa_forward: prefill split needs workspace");
   PrefillArgs k{a, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
+  if (fp8 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: fp8 prefill head_dim %d", a.head_dim);
   int mark = trace_begin(s);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
+  if (fp8)
+    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
   else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
+    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
   trace_end(s, mark, "prefill");
   pa_status st = launch_status("pa_forward (prefill)");
   if (st != PA_OK || pp.pieces <= 1) return st;

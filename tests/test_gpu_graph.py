@@ -26,7 +26,8 @@ def _run(name):
     return run
 
 
-@pytest.mark.parametrize("name", ["decode_bf16", "decode_gqa8", "mixed_bf16", "shared_bf16", "decode_f32"])
+@pytest.mark.parametrize("name", ["decode_bf16", "decode_gqa8", "mixed_bf16", "shared_bf16", "decode_f32",
+                                  "verify_bf16", "decode_fp8", "verify_fp8"])
 def test_graph_replay_matches_eager(name, monkeypatch):
     import torch
     monkeypatch.delenv("PA_CHECK", raising=False)

@@ -68,10 +68,10 @@ def test_mini_workloads(name):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["tiny_decode", "batched_decode", "mixed_superbatch", "shared_prefix_cow",
-                                  "spec_verify", "batched_decode_fp8"])
+                                  "spec_verify", "batched_decode_fp8", "mixed_superbatch_fp8"])
 def test_named_workloads_full_size(name):
     wl = workloads.named(name)
-    check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch", "batched_decode_fp8"))
+    check_parity(wl, pools=name in ("tiny_decode", "mixed_superbatch", "batched_decode_fp8", "mixed_superbatch_fp8"))
 
 
 @pytest.mark.timeout(1200)
@@ -226,7 +226,8 @@ def test_multi_token_decode_invariances():
 def test_prefill_split_sizes(split, monkeypatch):
     """Every prefill key-range split meets the tolerance (pieces merged by the prefill merge kernel)."""
     monkeypatch.setenv("PA_PREFILL_SPLIT", split)
-    for name in ("mixed_bf16", "mixed_gqa8", "noncausal_bf16", "mixed_mha_d64"):
+    for name in ("mixed_bf16", "mixed_gqa8", "noncausal_bf16", "mixed_mha_d64", "mixed_fp8",
+                 "prefill_fp8_gqa8_noncausal"):
         check_parity(workloads.mini(name), pools=False)
 
 
@@ -326,7 +327,7 @@ def test_error_paths(monkeypatch):
 
 # -- quantised (fp8) cache ------------------------------------------------------
 
-FP8_MINIS = ("decode_fp8", "verify_fp8", "fp8_gqa8", "fp8_mha_noncausal")
+FP8_MINIS = ("decode_fp8", "verify_fp8", "fp8_gqa8", "fp8_mha_noncausal", "mixed_fp8")
 
 
 def test_fp8_write_edge_rows():
@@ -404,14 +405,13 @@ def test_fp8_invariances():
 
 
 def test_fp8_unsupported_shapes():
-    """Chunks longer than the multi-token cap have no fp8 kernel yet: refused before any launch."""
+    """fp8 caches are built for head_dim 128 only: other shapes are refused before any launch."""
     pa = ensure_library()
     import ctypes
-    desc = pa.CacheDesc(100, 8, 128, 16, pa.PA_FP8)
-    assert pa.lib.pa_forward_workspace_size(4, 600, 32, 4096, 512, ctypes.byref(desc)) == 0
-    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 600, 32, 4096, 512,
-                           ctypes.byref(desc), 0.1, 1, None, 0, None)
-    assert st == pa.PA_ERR_UNSUPPORTED and "fp8" in pa.lib.pa_last_error().decode()
     desc64 = pa.CacheDesc(100, 8, 64, 16, pa.PA_FP8)
+    assert pa.lib.pa_forward_workspace_size(4, 600, 32, 4096, 512, ctypes.byref(desc64)) == 0
+    st = pa.lib.pa_forward(None, None, None, None, None, 1, None, None, None, 4, 600, 32, 4096, 512,
+                           ctypes.byref(desc64), 0.1, 1, None, 0, None)
+    assert st == pa.PA_ERR_UNSUPPORTED and "fp8" in pa.lib.pa_last_error().decode()
     st = pa.lib.pa_write_kv(None, None, None, None, None, 4, ctypes.byref(desc64), None)
     assert st == pa.PA_ERR_UNSUPPORTED

@@ -295,6 +295,15 @@ def batched_decode_fp8():
                        cached=L - 1, new=np.ones(64, dtype=np.int64), num_blocks=20000, cache_dtype="fp8")
 
 
+def mixed_superbatch_fp8():
+    """mixed_superbatch on a quantised (fp8) cache: 16 decode rows and four 512-token chunks."""
+    L = _lengths(np.random.Generator(np.random.PCG64(1004)), 256, 4096, 16)
+    cached = np.concatenate([L - 1, [0, 1024, 4096, 8192]])
+    new = np.concatenate([np.ones(16, dtype=np.int64), [512] * 4])
+    return independent("mixed_superbatch_fp8", 4, Hq=32, Hkv=8, D=128, dtype="bf16",
+                       cached=cached, new=new, pool_factor=1.25, cache_dtype="fp8")
+
+
 NAMED = {
     "tiny_decode": tiny_decode,
     "batched_decode": batched_decode,
@@ -303,6 +312,7 @@ NAMED = {
     "shared_prefix_cow": shared_prefix_cow,
     "spec_verify": spec_verify,
     "batched_decode_fp8": batched_decode_fp8,
+    "mixed_superbatch_fp8": mixed_superbatch_fp8,
 }
 
 
@@ -400,6 +410,17 @@ def mini(name):
         new = np.array([16, 4, 1])
         return independent(name, 28, Hq=8, Hkv=8, D=128, dtype="bf16", cached=cached,
                            new=new, pool_extra=2, cache_dtype="fp8", causal=False)
+    if name == "mixed_fp8":
+        # decode rows, multi-token rows and prefill chunks (ragged, one starting at 0) on an fp8 cache
+        cached = np.array([300, 1, 2000, 15, 0, 45, 700, 129, 33])
+        new = np.array([1, 1, 3, 1, 37, 130, 200, 64, 17])
+        return independent(name, 29, Hq=32, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_factor=1.25, cache_dtype="fp8")
+    if name == "prefill_fp8_gqa8_noncausal":
+        cached = np.array([0, 900, 33, 5])
+        new = np.array([200, 77, 1, 16])
+        return independent(name, 30, Hq=64, Hkv=8, D=128, dtype="bf16", cached=cached,
+                           new=new, pool_extra=2, cache_dtype="fp8", causal=False)
     if name == "shared_bf16":
         return shared_prefix(name, 21, Hq=32, Hkv=8, D=128, dtype="bf16", num_seqs=9,
                              prefix=160, suffix_max=70, num_blocks=200)
@@ -409,4 +430,4 @@ def mini(name):
 MINI = ["decode_f32", "decode_bf16", "decode_gqa8", "decode_d64_bf16", "decode_d128_f32",
         "mixed_bf16", "mixed_gqa8", "mixed_mha_d64", "prefill_f32", "noncausal_bf16",
         "shared_bf16", "verify_bf16", "verify_gqa8", "verify_mha", "decode_fp8", "verify_fp8", "fp8_gqa8",
-        "fp8_mha_noncausal"]
+        "fp8_mha_noncausal", "mixed_fp8", "prefill_fp8_gqa8_noncausal"]
