@@ -222,6 +222,8 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_VERIFY_TOTAL_WAVES=<1..65536>  multi-token decode: waves in all (default 1024)
  *   PA_VERIFY_DEPTH=2|3|4   multi-token decode: K/V tiles in flight per wave
  *            (default 3, or 2 when four work-groups would not fit a CU's LDS)
+ *   PA_PREFILL_ROWS=32 (default) | 64   chunked prefill: (token, head) rows per
+ *            wave (64: head_dim 128 only)
  *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
  *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
  *            max(1024, a quarter of the longest sequence)

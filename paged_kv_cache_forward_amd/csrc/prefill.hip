@@ -57,7 +57,8 @@ namespace {
 constexpr int kWaves = 4;                    // waves per work-group (4 or 8)
 constexpr int kWavesPerBlock = kWaves / 4;   // waves copying each of a tile's four cache blocks
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWG = 32 * kWaves;      // (token, query head) rows per work-group: 32 per wave
+// (token, query head) rows per work-group: 16 RT per wave, RT = row tiles per wave.
+template <int RT> constexpr int rows_per_wg() { return 16 * RT * kWaves; }
 constexpr int kKeys = 64;         // keys per tile: four 16-token cache blocks
 constexpr int kBtCache = 1024;    // block-table entries staged in LDS (16384 tokens)
 
@@ -147,9 +148,13 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
   return it;
 }
 
-template <int D, bool F8>
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillArgs pk) {
+// RT = 2: 32 rows per wave, two waves per SIMD.  RT = 4: 64 rows per wave --
+// each K/V fragment read from LDS feeds twice the MFMAs -- with the output
+// accumulators in AGPRs at one wave per SIMD.
+template <int D, bool F8, int RT>
+__global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_kernel(PrefillArgs pk) {
   using C = PCfg<D>;
+  constexpr int kRowsPerWG = rows_per_wg<RT>();
   static_assert(!F8 || (D == 128 && kWavesPerBlock == 1), "fp8: head_dim 128, one wave per block");
   constexpr int SBUF = F8 ? kF8Stage : C::BUF;   // bytes of one LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t lds_stage[2 * SBUF];
@@ -201,11 +206,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   // Query fragments (B operand of S^T = K Q^T): lane holds 8 head-dim values of
   // its row: dims 32 ks + 8 lq (bf16 cache); 64 (ks / 2) + 16 lq + 8 (ks % 2)
   // (fp8 cache, matching the K fragments it converts 16 codes at a time).
-  bf16x8_t qf[2][C::KS];
-  int row_tok[2], row_head[2];
+  bf16x8_t qf[RT][C::KS];
+  int row_tok[RT], row_head[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int r = w * 32 + rt * 16 + lr;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = w * 16 * RT + rt * 16 + lr;
     row_tok[rt] = tok0 + r / G;
     row_head[rt] = g * G + r % G;
     const bool ok = row_tok[rt] < n;
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   const float cs = fmaxf(fabsf(a.scale_log2), 1e-30f);
   if (a.scale_log2 < 0.0f) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         uint4 u = __builtin_bit_cast(uint4, qf[rt][ks]);
@@ -239,16 +244,18 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   // row's sum of the (bf16) weights on the matrix cores, in every element.
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  float m[2] = {kNegBig, kNegBig};
-  f32x4_t o[2][C::DT + 1];
+  float m[RT];
+  f32x4_t o[RT][C::DT + 1];
+  int lim[RT];   // keys visible to row tile rt's row of this lane: t < lim
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = kNegBig;
+    lim[rt] = a.causal ? min(L, c + row_tok[rt] + 1) : L;
 #pragma unroll
     for (int dt = 0; dt <= C::DT; ++dt) o[rt][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
-  const int wave_tok_last = min(tok0 + (w * 32 + 31) / G, n - 1);
-  const int lim0 = a.causal ? min(L, c + row_tok[0] + 1) : L;
-  const int lim1 = a.causal ? min(L, c + row_tok[1] + 1) : L;
+  const int wave_tok_last = min(tok0 + (w * 16 * RT + 16 * RT - 1) / G, n - 1);
 
   constexpr int CTILE = F8 ? kF8Tile : C::TILE;      // bytes of one (block, KV head) code tile
   const size_t block_stride = (size_t)Hkv * CTILE;
@@ -327,10 +334,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   // compare against a per-row threshold and one select per score, only in
   // lanes that hold such keys (one code path: the register allocation stays
   // tight).
-  auto softmax_tile = [&](f32x4_t (&s)[2][4], int key0, bf16x8_t (&pb)[2][2]) {
+  auto softmax_tile = [&](f32x4_t (&s)[RT][4], int key0, bf16x8_t (&pb)[RT][2]) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int t = (rt == 0 ? lim0 : lim1) - key0 - lq * 4;   // key kt16 * 16 + e of this lane is visible iff < t
+    for (int rt = 0; rt < RT; ++rt) {
+      const int t = lim[rt] - key0 - lq * 4;   // key kt16 * 16 + e of this lane is visible iff < t
       if (t < 3 * 16 + 4) {   // some key of this lane is not visible (diagonal and last tiles)
 #pragma unroll
         for (int kt16 = 0; kt16 < 4; ++kt16)
@@ -369,11 +376,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
     const lds_u8* kl = k_lane + buf * SBUF;
     const lds_u8* vl = v_lane + buf * SBUF;
     const lds_u8* st8 = lds + buf * SBUF;
-    f32x4_t s[2][4];
+    f32x4_t s[RT][4];
 #pragma unroll
     for (int kt16 = 0; kt16 < 4; ++kt16) {
-      s[0][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      s[1][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) s[rt][kt16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if constexpr (F8) {
         // Block kt16: each 16-code piece gives two k-steps, converted with key lr's scale.
         const float ksc = e8m0f(st8[kF8KX + kt16 * kBlock + lr]);
@@ -382,29 +389,32 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
           const uint4 raw = __builtin_bit_cast(
               uint4, *reinterpret_cast<const lds_u32x4_t*>(st8 + kt16 * kF8Tile + p * 1024 + lane * 16));
           const bf16x8_t k0 = cvt8_fp8(raw.x, raw.y, ksc), k1 = cvt8_fp8(raw.z, raw.w, ksc);
-          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[0][2 * p], s[0][kt16], 0, 0, 0);
-          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[1][2 * p], s[1][kt16], 0, 0, 0);
-          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[0][2 * p + 1], s[0][kt16], 0, 0, 0);
-          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[1][2 * p + 1], s[1][kt16], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[rt][2 * p], s[rt][kt16], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[rt][2 * p + 1], s[rt][kt16], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const bf16x8_t kf =
               *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(kl + (kt16 * C::KS + ks) * 1024);
-          s[0][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[0][ks], s[0][kt16], 0, 0, 0);
-          s[1][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[1][ks], s[1][kt16], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][ks], s[rt][kt16], 0, 0, 0);
         }
       }
       if (kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
     }
-    bf16x8_t pb[2][2];
+    bf16x8_t pb[RT][2];
     softmax_tile(s, key0, pb);
     if constexpr (F8) {
       // P.V on the fp8 codes: the product takes each weight times its key's V
       // exponent (exact), the row sums (ones tile) the weights alone.  Keys
       // past the sequence: weight 0 and codes zeroed (stale bytes may be NaN codes).
-      bf16x8_t pv[2][2];
+      bf16x8_t pv[RT][2];
       uint32_t keep[2][2];
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2)
@@ -417,7 +427,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
           if (key0 + kKeys > L) live = min(max(L - key0 - 16 * blk - 4 * lq, 0), 4);   // wave-uniform test
           keep[ks2][h] = live >= 4 ? 0xffffffffu : live == 0 ? 0u : (1u << (8 * live)) - 1u;
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
+          for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const float sv = e < live ? e8m0f((xw >> (8 * e)) & 0xffu) : 0.0f;
@@ -435,8 +445,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
           const uint32_t w1 = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(
                                   vp + (2 * ks2 + 1) * kF8Tile) & keep[ks2][1];
           const bf16x8_t vf = cvt8_fp8(w0, w1, 1.0f);
-          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[0][ks2], o[0][dt], 0, 0, 0);
-          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[1][ks2], o[1][dt], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pv[rt][ks2], o[rt][dt], 0, 0, 0);
         }
     } else {
 #pragma unroll
@@ -449,14 +460,16 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
           const s16x4_t v1 = lds_read_tr(vp + (C::DT / 2) * 1024);
           const bf16x8_t vf = __builtin_bit_cast(
               bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[0][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[0][ks2], o[0][dt], 0, 0, 0);
-          o[1][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[1][ks2], o[1][dt], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt)
+            o[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rt][ks2], o[rt][dt], 0, 0, 0);
         }
     }
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      o[0][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[0][ks2], o[0][C::DT], 0, 0, 0);
-      o[1][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[1][ks2], o[1][C::DT], 0, 0, 0);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        o[rt][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rt][ks2], o[rt][C::DT], 0, 0, 0);
     }
   };
 
@@ -479,7 +492,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   }
 
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     const float lt = o[rt][C::DT][0];   // the row's weight sum (ones tile)
     if (row_tok[rt] >= n) continue;
     if (split) {
@@ -505,13 +518,14 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillAr
   }
 }
 
-// Prefill split-KV merge: one work-group of 256 threads per (KV head, query
-// tile, sequence) whose key range was split; two threads per (token, head)
-// row, each owning half of the head dim.  Pieces are combined in ascending
-// order with the log-sum-exp rule, so the result is deterministic.
-template <int D>
-__global__ __launch_bounds__(2 * kRowsPerWG) void prefill_merge_kernel(PrefillArgs pk) {
+// Prefill split-KV merge: one work-group per (KV head, query tile, sequence)
+// whose key range was split; two threads per (token, head) row, each owning
+// half of the head dim.  Pieces are combined in ascending order with the
+// log-sum-exp rule, so the result is deterministic.
+template <int D, int RT>
+__global__ __launch_bounds__(2 * rows_per_wg<RT>()) void prefill_merge_kernel(PrefillArgs pk) {
   constexpr int HALF = D / 2;
+  constexpr int kRowsPerWG = rows_per_wg<RT>();
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
@@ -567,7 +581,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-  if (group < 1 || kRowsPerWG % group != 0) return false;
+  if (group < 1 || rows_per_wg<2>() % group != 0) return false;
   if (dtype == PA_FP8) return head_dim == 128;
   return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128);
 }
@@ -599,7 +613,15 @@ PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t h
 pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
                          bool fp8, hipStream_t s) {
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int TOK = kRowsPerWG / G;
+  // Row tiles per wave: 2 (32 rows, two waves per SIMD).  PA_PREFILL_ROWS=64
+  // selects 64 rows per wave at one wave per SIMD (head_dim 128): half the LDS
+  // bytes per MFMA, but measured on MI355X 1.5x slower -- one wave per SIMD
+  // does not hide the LDS and MFMA latencies.
+  int rt = 2;
+  if (const char* env = std::getenv("PA_PREFILL_ROWS")) {
+    if (std::strcmp(env, "64") == 0 && a.head_dim == 128) rt = 4;
+  }
+  const int TOK = 16 * rt * kWaves / G;
   const int qtiles = (max_query_len + TOK - 1) / TOK;
   const int64_t tiles = (int64_t)qtiles * a.num_kv_heads * a.num_seqs;
   const int64_t wgs = tiles * pp.pieces;
@@ -612,20 +634,23 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   PrefillArgs k{a, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
   if (fp8 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: fp8 prefill head_dim %d", a.head_dim);
   int mark = trace_begin(s);
-  if (fp8)
-    hipLaunchKernelGGL((prefill_kernel<128, true>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<128, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
-  else
-    hipLaunchKernelGGL((prefill_kernel<64, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, k);
+  const dim3 grid((unsigned)wgs), block(kThreads);
+  if (fp8 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, true, 4>), grid, block, 0, s, k);
+  else if (fp8) hipLaunchKernelGGL((prefill_kernel<128, true, 2>), grid, block, 0, s, k);
+  else if (a.head_dim == 128 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, false, 4>), grid, block, 0, s, k);
+  else if (a.head_dim == 128) hipLaunchKernelGGL((prefill_kernel<128, false, 2>), grid, block, 0, s, k);
+  else hipLaunchKernelGGL((prefill_kernel<64, false, 2>), grid, block, 0, s, k);
   trace_end(s, mark, "prefill");
   pa_status st = launch_status("pa_forward (prefill)");
   if (st != PA_OK || pp.pieces <= 1) return st;
   mark = trace_begin(s);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL(prefill_merge_kernel<128>, dim3((unsigned)tiles), dim3(2 * kRowsPerWG), 0, s, k);
+  const dim3 mgrid((unsigned)tiles);
+  if (a.head_dim == 128 && rt == 4)
+    hipLaunchKernelGGL((prefill_merge_kernel<128, 4>), mgrid, dim3(2 * rows_per_wg<4>()), 0, s, k);
+  else if (a.head_dim == 128)
+    hipLaunchKernelGGL((prefill_merge_kernel<128, 2>), mgrid, dim3(2 * rows_per_wg<2>()), 0, s, k);
   else
-    hipLaunchKernelGGL(prefill_merge_kernel<64>, dim3((unsigned)tiles), dim3(2 * kRowsPerWG), 0, s, k);
+    hipLaunchKernelGGL((prefill_merge_kernel<64, 2>), mgrid, dim3(2 * rows_per_wg<2>()), 0, s, k);
   trace_end(s, mark, "prefill_merge");
   return launch_status("pa_forward (prefill merge)");
 }
