@@ -531,28 +531,30 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
 }
 
 // Merge of the parts of split sequences: one work-group per (sequence, KV
-// head); thread item = one float4 of the fragment-ordered partials (column
-// group cg, dim block db, lane (r, j): column 16 cg + j, dims 16 db + 4 r ..
-// +3), so consecutive threads read consecutive 16 bytes; the parts are folded
-// in rank order by the log-sum-exp rule in one pass, four parts' loads in
-// flight.
+// head, column group), one thread per float4 of the fragment-ordered partials
+// (dim block db, lane (r, j): column 16 cg + j, dims 16 db + 4 r .. +3), so
+// consecutive threads read consecutive 16 bytes; the parts are folded in
+// rank order by the log-sum-exp rule in one pass, eight parts' loads in
+// flight -- a sequence split into up to eight parts costs one memory round
+// trip.
 template <int CG>
-__global__ __launch_bounds__(256) void merge_verify_kernel(VerifyArgs k) {
-  constexpr int C = 16 * CG, U = 4;
+__global__ __launch_bounds__(512) void merge_verify_kernel(VerifyArgs k) {
+  constexpr int C = 16 * CG, U = 8;
   const AttnArgs& a = k.a;
   const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv;
-  const int i = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int i = blockIdx.x / Hkv, g = blockIdx.x % Hkv, cg = blockIdx.y;
   int q0, n, len;
   if (!verify_item(k, i, q0, n, len)) return;
+  if (cg * 16 >= n * G) return;          // column group beyond this sequence's rows
   const int2 si = k.seqinfo[i];          // written by this call's verify kernel
   const int P = si.y;
   if (P <= 1) return;                    // written out by the verify kernel
   const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);
-  const int groups = (n * G + 15) / 16;
-  for (int it = threadIdx.x; it < groups * 8 * 64; it += 256) {
-    const int ln = it & 63, db = (it >> 6) & 7, cg = it >> 9;
+  {
+    const int it = cg * 512 + threadIdx.x;
+    const int ln = it & 63, db = (it >> 6) & 7;
     const int col = 16 * cg + (ln & 15);
-    if (col >= n * G) continue;
+    if (col >= n * G) return;
     const float2* ml = reinterpret_cast<const float2*>(k.p_ml) + slot0 * C + col;
     const float* acc = k.p_acc + (slot0 * CG * 8 * 64 + it) * 4;
     float M = -INFINITY, den = 0.0f;
@@ -597,7 +599,7 @@ pa_status launch_verify_gc(const VerifyArgs& k, hipStream_t s) {
   pa_status st = launch_status("pa_forward (multi-token decode)");
   if (st != PA_OK) return st;
   mark = trace_begin(s);
-  hipLaunchKernelGGL((merge_verify_kernel<CG>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(256), 0, s, k);
+  hipLaunchKernelGGL((merge_verify_kernel<CG>), dim3(k.a.num_seqs * k.a.num_kv_heads, CG), dim3(512), 0, s, k);
   trace_end(s, mark, "merge_verify");
   return launch_status("pa_forward (multi-token decode merge)");
 }
