@@ -74,6 +74,19 @@ def kv_bytes(wl, seqs=None):
     return sum(int(wl.seq_lens[i]) for i in seqs) * 2 * wl.num_kv_heads * kv_row_bytes(wl)
 
 
+def unique_kv_bytes(wl, tables):
+    """K and V bytes of the distinct physical blocks the batch reads (a shared block counted once,
+    with the most tokens any sequence reads from it)."""
+    used = {}
+    for i, t in enumerate(tables):
+        L = int(wl.seq_lens[i])
+        for p, b in enumerate(t):
+            n = min(wl.block_size, L - p * wl.block_size)
+            if n > 0:
+                used[b] = max(used.get(b, 0), n)
+    return sum(used.values()) * 2 * wl.num_kv_heads * kv_row_bytes(wl)
+
+
 def decode_algorithmic_bytes(wl):
     """Decode rows: K/V + q read + out written + block-table entries."""
     seqs = decode_rows(wl)
@@ -355,6 +368,75 @@ def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
             "speedup": round(eager_us / graph_us, 3)}
 
 
+def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
+    """One workload's whole step (copies, writes, forward) and its decode kernel against the HBM roofline.
+
+    Pools rotate over >= 1 GB of copies as in the headline run; the step time
+    comes from events around untraced steps, per-kernel times from the
+    library's own events on the launch stream."""
+    log(f"config leg: {name}")
+    wl = workloads.named(name)
+    kvb = kv_bytes(wl)
+    run = DeviceRun(wl, fill="zero", copies=max(2, -(-(1 << 30) // max(kvb, 1))))
+    run_steps(run, 3, stream)
+    ms_step, _ = timed_region(run, steps, stream)
+    per = traced_region(pa, run, steps, stream)
+    out = {"seqs": wl.num_seqs, "query_tokens": wl.num_tokens, "sum_context_tokens": int(wl.seq_lens.sum()),
+           "dtype": wl.dtype, "ms_per_step": round(ms_step, 5),
+           "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
+           "kv_GBs_step": round(kvb / (ms_step * 1e-3) / 1e9, 2),
+           "kernel_ms": {k: round(mean(v), 5) for k, v in per.items()}}
+    dec = next((k for k in ("decode_mfma", "decode_valu", "decode_verify") if k in per), None)
+    if dec is not None and decode_rows(wl):
+        algo = decode_algorithmic_bytes(wl)
+        logical = algo
+        if name == "shared_prefix_cow":
+            # HBM has to deliver each shared block once: price the kernel on the distinct blocks
+            algo = algo - kv_bytes(wl, decode_rows(wl)) + unique_kv_bytes(wl, run.tables)
+        dms = mean(per[dec])
+        ach = algo / (dms * 1e-3) / 1e9
+        out["decode_roofline"] = {"kernel": dec, "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(dms, 5)}
+        if logical != algo:
+            out["decode_roofline"]["logical_bytes_per_launch"] = int(logical)
+            out["decode_roofline"]["logical_GBs"] = round(logical / (dms * 1e-3) / 1e9, 2)
+    if "prefill" in per:
+        pms = mean(per["prefill"])
+        tf = prefill_flops(wl) / (pms * 1e-3) / 1e12
+        out["prefill"] = {"ms": round(pms, 5), "tflops": round(tf, 2),
+                          "mfma_util": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if name == "shared_prefix_cow":
+        # the shared prefix is read by all 256 sequences; count its blocks once
+        uniq = unique_kv_bytes(wl, run.tables)
+        out["kv_unique_bytes"] = int(uniq)
+        out["kv_GBs_step_unique"] = round(uniq / (ms_step * 1e-3) / 1e9, 2)
+    if name == "long_context_decode":
+        # bulk cache write: the first 262144 context tokens stored again (same slots, same bytes)
+        n = min(len(wl.ctx_k), 1 << 18)
+        k = run.upload(wl.ctx_k[:n])
+        v = run.upload(wl.ctx_v[:n])
+        sl = torch.from_numpy(run.ctx_slots[:n]).to(run.dev)
+        torch.cuda.synchronize()
+        pa.pa_trace_read()
+        pa.pa_trace_enable(True)
+        try:
+            for _ in range(5):
+                pa.pa_write_kv(k, v, run.k_cache, run.v_cache, sl, stream=stream)
+            torch.cuda.synchronize()
+        finally:
+            pa.pa_trace_enable(False)
+        wms = mean([ms for kname, ms in pa.pa_trace_read() if kname == "write_kv"])
+        moved = n * (2 * 2 * wl.num_kv_heads * wl.head_dim * elem_bytes(wl) + 8)
+        out["bulk_write_kv"] = {"tokens": n, "bytes_moved": int(moved), "ms": round(wms, 5),
+                                "GBs": round(moved / (wms * 1e-3) / 1e9, 2),
+                                "frac": round(moved / (wms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del k, v, sl
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -367,6 +449,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph step-replay leg")
     ap.add_argument("--no-verify", action="store_true", help="skip the multi-token decode leg")
     ap.add_argument("--no-fp8", action="store_true", help="skip the fp8-cache decode leg")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration leg (tiny, long-context, mixed and shared-prefix steps)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
@@ -556,6 +640,10 @@ def main():
                                         "kernel_ms": {k: round(mean(v), 5) for k, v in fpper.items()}}
         del fprun
         torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        res["configs"] = {n: config_leg(pa, torch, workloads, DeviceRun, n, max(10, args.steps // 2), stream)
+                          for n in ("tiny_decode", "long_context_decode", "mixed_superbatch", "shared_prefix_cow")}
 
     if not args.no_graph:
         log("graph leg: one step per launch vs replayed from a HIP graph (tiny and batched decode)")

@@ -283,8 +283,8 @@ class BlockAllocator:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h and h.value:
-            _load().pa_alloc_destroy(h)
+        if h and h.value and _LIB is not None:   # at interpreter exit the module may be torn down first
+            _LIB.pa_alloc_destroy(h)
             self._h = ctypes.c_void_p()
 
     def create(self):
