@@ -134,6 +134,11 @@ struct PrefillArgs {
 // fastest (every work-group of one KV head on one XCD); pieces slowest and in
 // descending order, because only long key ranges have high pieces: the
 // longest work is dispatched first and the short pieces fill the tail.
+// Sequences go in descending batch order: a super-batch puts its decode
+// sequences before the prefill chunks, and the work-groups of a decode
+// sequence find no rows and exit, but each holds an LDS slot for a memory
+// round trip first; dispatched after the chunks' work-groups, they fill the
+// tail instead of delaying real work.
 struct PrefillItem {
   int g, p, qt, i;
 };
@@ -143,7 +148,7 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
   int r = wg / Hkv;
   it.qt = qtiles - 1 - r % qtiles;
   r /= qtiles;
-  it.i = r % num_seqs;
+  it.i = num_seqs - 1 - r % num_seqs;
   it.p = pieces - 1 - r / num_seqs;
   return it;
 }
@@ -519,12 +524,16 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_ke
 }
 
 // Prefill split-KV merge: one work-group per (KV head, query tile, sequence)
-// whose key range was split; two threads per (token, head) row, each owning
-// half of the head dim.  Pieces are combined in ascending order with the
-// log-sum-exp rule, so the result is deterministic.
+// whose key range was split; eight threads per (token, head) row, each owning
+// 16 dims (D / 8).  Pieces are folded four at a time with their loads issued
+// together (one memory round trip per four pieces), in ascending order with
+// the log-sum-exp rule, so the result is deterministic.
+constexpr int kMergeThreads = 256;
 template <int D, int RT>
-__global__ __launch_bounds__(2 * rows_per_wg<RT>()) void prefill_merge_kernel(PrefillArgs pk) {
-  constexpr int HALF = D / 2;
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs pk) {
+  constexpr int SL = D / 8;            // dims per thread
+  constexpr int NV = SL / 4;           // float4 per piece per thread
+  constexpr int U = 4;                 // pieces per round trip
   constexpr int kRowsPerWG = rows_per_wg<RT>();
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
@@ -542,38 +551,53 @@ __global__ __launch_bounds__(2 * rows_per_wg<RT>()) void prefill_merge_kernel(Pr
   const int kv_end = a.causal ? min(L, c + tok_last + 1) : L;
   if (kv_end <= pk.piece_keys || pk.pieces <= 1) return;   // written by the prefill kernel itself
   const int np = min((kv_end + pk.piece_keys - 1) / pk.piece_keys, pk.pieces);
-  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const int tok = tok0 + r / G, head = it.g * G + r % G;
-  if (tok >= n) return;
-  const size_t item0 = ((size_t)(q0 + tok) * a.num_q_heads + head) * pk.pieces;
-  const float2* ml = reinterpret_cast<const float2*>(pk.p_ml) + item0;
-  float M = ml[0].x;
-  for (int pp = 1; pp < np; ++pp) M = fmaxf(M, ml[pp].x);
-  float den = 0.0f;
-  float acc[HALF];
+  const int rows = (tok_last - tok0 + 1) * G;   // rows are token-major: the first `rows` are valid
+  for (int idx = threadIdx.x; idx < rows * 8; idx += kMergeThreads) {
+    const int r = idx >> 3, sl = idx & 7;
+    const int tok = tok0 + r / G, head = it.g * G + r % G;
+    const size_t item0 = ((size_t)(q0 + tok) * a.num_q_heads + head) * pk.pieces;
+    const float2* ml = reinterpret_cast<const float2*>(pk.p_ml) + item0;
+    float Mx = -INFINITY, den = 0.0f;
+    float acc[SL];
 #pragma unroll
-  for (int e = 0; e < HALF; ++e) acc[e] = 0.0f;
-  for (int pp = 0; pp < np; ++pp) {
-    const float2 v = ml[pp];
-    const float w = fast_exp2(v.x - M);
-    den = fmaf(w, v.y, den);
-    const float4* src = reinterpret_cast<const float4*>(pk.p_o + (item0 + pp) * D + half * HALF);
+    for (int e = 0; e < SL; ++e) acc[e] = 0.0f;
+    for (int p0 = 0; p0 < np; p0 += U) {
+      float2 v[U];
+      float4 x[U][NV];
 #pragma unroll
-    for (int q = 0; q < HALF / 4; ++q) {
-      const float4 x = src[q];
-      acc[4 * q] = fmaf(w, x.x, acc[4 * q]);
-      acc[4 * q + 1] = fmaf(w, x.y, acc[4 * q + 1]);
-      acc[4 * q + 2] = fmaf(w, x.z, acc[4 * q + 2]);
-      acc[4 * q + 3] = fmaf(w, x.w, acc[4 * q + 3]);
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u < np) {
+          v[u] = ml[p0 + u];
+          const float4* src = reinterpret_cast<const float4*>(pk.p_o + (item0 + p0 + u) * D + sl * SL);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) x[u][q] = src[q];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (p0 + u >= np) break;
+        // A piece past the row's causal limit holds (kNegBig, 0, 0): weight 0.
+        const float Mn = fmaxf(Mx, v[u].x);
+        const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(v[u].x - Mn);
+        den = fmaf(den, sa, v[u].y * sb);
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+          acc[4 * q + 0] = fmaf(acc[4 * q + 0], sa, x[u][q].x * sb);
+          acc[4 * q + 1] = fmaf(acc[4 * q + 1], sa, x[u][q].y * sb);
+          acc[4 * q + 2] = fmaf(acc[4 * q + 2], sa, x[u][q].z * sb);
+          acc[4 * q + 3] = fmaf(acc[4 * q + 3], sa, x[u][q].w * sb);
+        }
+        Mx = Mn;
+      }
     }
-  }
-  const float inv = 1.0f / den;
-  uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + tok) * a.num_q_heads + head) * (D * 2) + half * HALF * 2;
+    const float inv = 1.0f / den;
+    uint8_t* op = (uint8_t*)a.out + ((size_t)(q0 + tok) * a.num_q_heads + head) * (D * 2) + sl * SL * 2;
 #pragma unroll
-  for (int q = 0; q < HALF / 8; ++q)
-    *reinterpret_cast<uint4*>(op + q * 16) = make_uint4(
-        pack_bf16x2(acc[8 * q] * inv, acc[8 * q + 1] * inv), pack_bf16x2(acc[8 * q + 2] * inv, acc[8 * q + 3] * inv),
-        pack_bf16x2(acc[8 * q + 4] * inv, acc[8 * q + 5] * inv), pack_bf16x2(acc[8 * q + 6] * inv, acc[8 * q + 7] * inv));
+    for (int q = 0; q < SL / 8; ++q)
+      *reinterpret_cast<uint4*>(op + q * 16) = make_uint4(
+          pack_bf16x2(acc[8 * q] * inv, acc[8 * q + 1] * inv), pack_bf16x2(acc[8 * q + 2] * inv, acc[8 * q + 3] * inv),
+          pack_bf16x2(acc[8 * q + 4] * inv, acc[8 * q + 5] * inv), pack_bf16x2(acc[8 * q + 6] * inv, acc[8 * q + 7] * inv));
+  }
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -646,11 +670,11 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   mark = trace_begin(s);
   const dim3 mgrid((unsigned)tiles);
   if (a.head_dim == 128 && rt == 4)
-    hipLaunchKernelGGL((prefill_merge_kernel<128, 4>), mgrid, dim3(2 * rows_per_wg<4>()), 0, s, k);
+    hipLaunchKernelGGL((prefill_merge_kernel<128, 4>), mgrid, dim3(kMergeThreads), 0, s, k);
   else if (a.head_dim == 128)
-    hipLaunchKernelGGL((prefill_merge_kernel<128, 2>), mgrid, dim3(2 * rows_per_wg<2>()), 0, s, k);
+    hipLaunchKernelGGL((prefill_merge_kernel<128, 2>), mgrid, dim3(kMergeThreads), 0, s, k);
   else
-    hipLaunchKernelGGL((prefill_merge_kernel<64, 2>), mgrid, dim3(2 * rows_per_wg<2>()), 0, s, k);
+    hipLaunchKernelGGL((prefill_merge_kernel<64, 2>), mgrid, dim3(kMergeThreads), 0, s, k);
   trace_end(s, mark, "prefill_merge");
   return launch_status("pa_forward (prefill merge)");
 }
