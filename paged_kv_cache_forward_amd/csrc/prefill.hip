@@ -270,6 +270,13 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_ke
   const uint8_t* kx = (const uint8_t*)a.k_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
   const uint8_t* vx = (const uint8_t*)a.v_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
 
+  // The query fragments are loaded by ordinary global loads, which the
+  // compiler tracks: without a wait it can see here, it waits for them
+  // (vmcnt(0)) at their first use inside the tile loop, on every iteration,
+  // and that wait also drains the untracked copies of the next tile issued
+  // just before -- serialising copy and compute.  s_waitcnt vmcnt(0)
+  // (simm16 0x0F70: expcnt and lgkmcnt left at their maxima) retires them here.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();   // first block-table window ready
 
   auto block_id = [&](int b) -> int {   // b < nblk, inside the current window, wave-uniform
@@ -382,6 +389,16 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_ke
     const lds_u8* vl = v_lane + buf * SBUF;
     const lds_u8* st8 = lds + buf * SBUF;
     f32x4_t s[RT][4];
+    // bf16: the K fragments of 16-key block kt16 + 1 are read while block
+    // kt16's MFMAs run (two register sets), so each block's LDS reads are in
+    // flight behind the previous block's products instead of in front of
+    // their own.
+    typedef const __attribute__((address_space(3))) bf16x8_t lds_bf16x8;
+    bf16x8_t kfr[2][C::KS];
+    if constexpr (!F8) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kfr[0][ks] = *reinterpret_cast<lds_bf16x8*>(kl + ks * 1024);
+    }
 #pragma unroll
     for (int kt16 = 0; kt16 < 4; ++kt16) {
 #pragma unroll
@@ -402,16 +419,20 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_ke
             s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[rt][2 * p + 1], s[rt][kt16], 0, 0, 0);
         }
       } else {
+        if (kt16 + 1 < 4) {
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const bf16x8_t kf =
-              *reinterpret_cast<const __attribute__((address_space(3))) bf16x8_t*>(kl + (kt16 * C::KS + ks) * 1024);
+          for (int ks = 0; ks < C::KS; ++ks)
+            kfr[(kt16 + 1) & 1][ks] = *reinterpret_cast<lds_bf16x8*>(kl + ((kt16 + 1) * C::KS + ks) * 1024);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // the next block's reads stay ahead of these products
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt)
-            s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][ks], s[rt][kt16], 0, 0, 0);
-        }
+            s[rt][kt16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfr[kt16 & 1][ks], qf[rt][ks], s[rt][kt16], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
+      if (F8 && kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
     }
     bf16x8_t pb[RT][2];
     softmax_tile(s, key0, pb);
