@@ -456,8 +456,8 @@ def main():
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: this build is the "
-              "single-GPU hot path (DESIGN.md describes how it would shard).", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library is the "
+              "single-GPU hot path and this benchmark measures one GPU's share.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -14,7 +14,7 @@ What the pages fix:
   * [ART] paragraph on paged attention: blocks of 16 tokens; running out of
     blocks is a signal for preemption.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * The free list starts in a caller-given order (default 0..N-1).  Blocks are
     taken from its head; a block whose refcount drops to zero goes to its tail.
   * Sequence ids are 0, 1, 2, ... in creation order and are never reused.

@@ -4,7 +4,7 @@
 memory; a new request that starts with the same tokens finds the matches and
 reuses the stored K/V instead of recomputing them.
 
-The pages name no hash function.  Reading (listed in the design doc): FNV-1a 64,
+The pages name no hash function.  Reading taken here: FNV-1a 64,
 a published definition -- start from the offset basis 0xcbf29ce484222325 and,
 for each byte, xor it in and multiply by the prime 0x100000001b3 modulo 2^64.
 Block b of a token sequence hashes the 8 little-endian bytes of the previous

@@ -4,7 +4,7 @@ What the pages fix: [SLAVA] section "Gemeinsame Nutzung erfordert mehr als
 Speicherzuweisung" names cache quantisation as a remedy when the raw K/V data
 does not fit, and asks that comparisons use the same cache precision; [AIU]
 section "L'avenir de PagedAttention et vLLM" expects paged K/V to be combined
-with quantisation.  They fix no format.  Readings (each listed in the design doc):
+with quantisation.  They fix no format.  Readings taken here:
 
   * Element format: 8-bit floating point "E4M3" in the OCP 8-bit floating
     point specification (the FN variant: 1 sign, 4 exponent bits with bias 7,
