@@ -54,11 +54,9 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;                    // waves per work-group (4 or 8)
-constexpr int kWavesPerBlock = kWaves / 4;   // waves copying each of a tile's four cache blocks
-constexpr int kThreads = 64 * kWaves;
-// (token, query head) rows per work-group: 16 RT per wave, RT = row tiles per wave.
-template <int RT> constexpr int rows_per_wg() { return 16 * RT * kWaves; }
+// (token, query head) rows per work-group: 16 RT per wave, RT = row tiles per
+// wave, NW = waves per work-group (4 or 8).
+template <int NW, int RT> constexpr int rows_per_wg() { return 16 * RT * NW; }
 constexpr int kKeys = 64;         // keys per tile: four 16-token cache blocks
 constexpr int kBtCache = 1024;    // block-table entries staged in LDS (16384 tokens)
 
@@ -72,7 +70,7 @@ constexpr int kBtCache = 1024;    // block-table entries staged in LDS (16384 to
 //     16 b + r, dims 16 (2 dp + dsel) + 8 h .. +8; a transpose read for
 //     output columns dt = 2 dp + dsel then has each 16-lane group reading
 //     128 contiguous bytes.
-// Each of the tile's four cache blocks is copied by kWaves / 4 waves: with
+// Each of the tile's four cache blocks is copied by NW / 4 waves: with
 // four waves, wave b copies block b's KS K pieces and DT/2 V pieces; with
 // eight, waves 2b and 2b + 1 split them.
 template <int D>
@@ -123,6 +121,7 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const lds_u8* p) {
 
 struct PrefillArgs {
   AttnArgs a;
+  int32_t tok;          // tokens per query tile (rows per work-group / G)
   int32_t qtiles;       // query tiles of the longest chunk
   int32_t piece_keys;   // keys per split piece (multiple of kKeys)
   int32_t pieces;       // pieces of the longest key range
@@ -155,11 +154,16 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
 
 // RT = 2: 32 rows per wave, two waves per SIMD.  RT = 4: 64 rows per wave --
 // each K/V fragment read from LDS feeds twice the MFMAs -- with the output
-// accumulators in AGPRs at one wave per SIMD.
-template <int D, bool F8, int RT>
-__global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_kernel(PrefillArgs pk) {
+// accumulators in AGPRs at one wave per SIMD.  NW = 8: 256 rows per
+// work-group (one per CU), so each K/V tile is copied once for twice the rows
+// and a batch's query tiles are half as many.
+template <int D, bool F8, int RT, int NW>
+__global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_kernel(PrefillArgs pk) {
   using C = PCfg<D>;
-  constexpr int kRowsPerWG = rows_per_wg<RT>();
+  constexpr int kThreads = 64 * NW;
+  constexpr int kWavesPerBlock = NW / 4;   // waves copying each of a tile's four cache blocks
+  constexpr int kRowsPerWG = rows_per_wg<NW, RT>();
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   static_assert(!F8 || (D == 128 && kWavesPerBlock == 1), "fp8: head_dim 128, one wave per block");
   constexpr int SBUF = F8 ? kF8Stage : C::BUF;   // bytes of one LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t lds_stage[2 * SBUF];
@@ -550,16 +554,15 @@ __global__ __launch_bounds__(kThreads, RT >= 4 ? 1 : 8 / kWaves) void prefill_ke
 // together (one memory round trip per four pieces), in ascending order with
 // the log-sum-exp rule, so the result is deterministic.
 constexpr int kMergeThreads = 256;
-template <int D, int RT>
+template <int D>
 __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArgs pk) {
   constexpr int SL = D / 8;            // dims per thread
   constexpr int NV = SL / 4;           // float4 per piece per thread
   constexpr int U = 4;                 // pieces per round trip
-  constexpr int kRowsPerWG = rows_per_wg<RT>();
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
-  const int TOK = kRowsPerWG / G;
+  const int TOK = pk.tok;
   const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.qtiles, a.num_seqs);
   const int q0 = a.qsl[it.i];
   const int n = a.qsl[it.i + 1] - q0;
@@ -626,7 +629,7 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group) {
-  if (group < 1 || rows_per_wg<2>() % group != 0) return false;
+  if (group < 1 || rows_per_wg<4, 2>() % group != 0) return false;
   if (dtype == PA_FP8) return head_dim == 128;
   return dtype == PA_BF16 && (head_dim == 64 || head_dim == 128);
 }
@@ -666,36 +669,48 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   if (const char* env = std::getenv("PA_PREFILL_ROWS")) {
     if (std::strcmp(env, "64") == 0 && a.head_dim == 128) rt = 4;
   }
-  const int TOK = 16 * rt * kWaves / G;
+  // Waves per work-group (bf16, head_dim 128, 32 rows per wave).  The grid
+  // holds a work-group per (query tile, KV head, piece) for every sequence of
+  // the batch, and those of sequences that are not chunks find no rows and
+  // exit -- but each first holds an LDS slot.  When most sequences cannot be
+  // chunks (fewer query tokens than half of num_seqs * max_query_len), eight
+  // waves (256 rows) per work-group halve the query tiles and with them those
+  // empty work-groups; otherwise four waves, two work-groups per CU, keep
+  // the better overlap.  Measured on MI355X: 16 decode sequences + 4 chunks
+  // of 512, prefill 164 us (8 waves) vs 176 us (4); the 4 chunks alone, 158
+  // us vs 149 us.  PA_PREFILL_WAVES=4|8 overrides.
+  int nw = 4;
+  if (!fp8 && a.head_dim == 128 && rt == 2) {
+    if ((int64_t)a.num_tokens * 2 < (int64_t)a.num_seqs * max_query_len) nw = 8;
+    if (const char* env = std::getenv("PA_PREFILL_WAVES")) nw = std::atoi(env) == 8 ? 8 : 4;
+  }
+  const int TOK = 16 * rt * nw / G;
   const int qtiles = (max_query_len + TOK - 1) / TOK;
   const int64_t tiles = (int64_t)qtiles * a.num_kv_heads * a.num_seqs;
   const int64_t wgs = tiles * pp.pieces;
   if (a.head_dim != 64 && a.head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill head_dim %d", a.head_dim);
-  if (wgs > 0x7fffffff / 256)
+  if (wgs > 0x7fffffff / (64 * nw))
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill grid of %lld work-groups", (long long)wgs);
   if (pp.pieces > 1 && (p_o == nullptr || p_ml == nullptr))
     return fail(PA_ERR_ARG, "pa_forward: prefill split needs workspace");
-  PrefillArgs k{a, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
+  PrefillArgs k{a, TOK, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
   if (fp8 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: fp8 prefill head_dim %d", a.head_dim);
   int mark = trace_begin(s);
-  const dim3 grid((unsigned)wgs), block(kThreads);
-  if (fp8 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, true, 4>), grid, block, 0, s, k);
-  else if (fp8) hipLaunchKernelGGL((prefill_kernel<128, true, 2>), grid, block, 0, s, k);
-  else if (a.head_dim == 128 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, false, 4>), grid, block, 0, s, k);
-  else if (a.head_dim == 128) hipLaunchKernelGGL((prefill_kernel<128, false, 2>), grid, block, 0, s, k);
-  else hipLaunchKernelGGL((prefill_kernel<64, false, 2>), grid, block, 0, s, k);
+  const dim3 grid((unsigned)wgs), block(64 * nw);
+  if (fp8 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, true, 4, 4>), grid, block, 0, s, k);
+  else if (fp8) hipLaunchKernelGGL((prefill_kernel<128, true, 2, 4>), grid, block, 0, s, k);
+  else if (a.head_dim == 128 && rt == 4) hipLaunchKernelGGL((prefill_kernel<128, false, 4, 4>), grid, block, 0, s, k);
+  else if (a.head_dim == 128 && nw == 8) hipLaunchKernelGGL((prefill_kernel<128, false, 2, 8>), grid, block, 0, s, k);
+  else if (a.head_dim == 128) hipLaunchKernelGGL((prefill_kernel<128, false, 2, 4>), grid, block, 0, s, k);
+  else hipLaunchKernelGGL((prefill_kernel<64, false, 2, 4>), grid, block, 0, s, k);
   trace_end(s, mark, "prefill");
   pa_status st = launch_status("pa_forward (prefill)");
   if (st != PA_OK || pp.pieces <= 1) return st;
   mark = trace_begin(s);
   const dim3 mgrid((unsigned)tiles);
-  if (a.head_dim == 128 && rt == 4)
-    hipLaunchKernelGGL((prefill_merge_kernel<128, 4>), mgrid, dim3(kMergeThreads), 0, s, k);
-  else if (a.head_dim == 128)
-    hipLaunchKernelGGL((prefill_merge_kernel<128, 2>), mgrid, dim3(kMergeThreads), 0, s, k);
-  else
-    hipLaunchKernelGGL((prefill_merge_kernel<64, 2>), mgrid, dim3(kMergeThreads), 0, s, k);
+  if (a.head_dim == 128) hipLaunchKernelGGL((prefill_merge_kernel<128>), mgrid, dim3(kMergeThreads), 0, s, k);
+  else hipLaunchKernelGGL((prefill_merge_kernel<64>), mgrid, dim3(kMergeThreads), 0, s, k);
   trace_end(s, mark, "prefill_merge");
   return launch_status("pa_forward (prefill merge)");
 }

@@ -231,6 +231,23 @@ def test_prefill_split_sizes(split, monkeypatch):
         check_parity(workloads.mini(name), pools=False)
 
 
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("split", ["auto", "64"])
+def test_prefill_waves_per_work_group(waves, split, monkeypatch):
+    """Both prefill work-group shapes (4 waves = 128 rows, 8 waves = 256 rows) meet the tolerance,
+    with and without split key ranges, whichever the host rule would pick for the batch."""
+    monkeypatch.setenv("PA_PREFILL_WAVES", waves)
+    if split == "auto":
+        monkeypatch.delenv("PA_PREFILL_SPLIT", raising=False)
+    else:
+        monkeypatch.setenv("PA_PREFILL_SPLIT", split)
+    for name in ("mixed_bf16", "mixed_gqa8", "noncausal_bf16", "mixed_mha_d64", "mixed_fp8"):
+        check_parity(workloads.mini(name), pools=False)
+    wl = workloads.independent("long_chunks", 41, Hq=32, Hkv=8, D=128, dtype="bf16",
+                               cached=[0, 700, 1500], new=[300, 257, 129], pool_extra=4)
+    check_parity(wl, pools=False)
+
+
 def test_degenerate_batches():
     ensure_library()
     # sequences with no query rows between others, a length-1 context, and a 1-token chunk
