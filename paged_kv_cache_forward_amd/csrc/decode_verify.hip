@@ -622,13 +622,20 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
                             int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len) {
   VerifyPlan vp{};
   const int32_t G = num_kv_heads > 0 ? num_q_heads / num_kv_heads : 0;
-  // PA_VERIFY=prefill sends these sequences to the chunked-prefill kernel;
-  // PA_VERIFY=all routes single-token sequences here too (one launch for all).
-  // A quantised (fp8) cache always comes here, single-token sequences included.
+  // Whenever a batch may hold sequences of more than one query token, this
+  // launch takes the single-token sequences too, so a step launches one
+  // decode-like kernel and one merge instead of two of each (either of which
+  // may find nothing to do: the host cannot see the per-sequence counts).  A
+  // batch of single-token sequences only keeps the single-token decode.  A
+  // quantised (fp8) cache always comes here.  PA_VERIFY=prefill sends the
+  // multi-token sequences to the chunked-prefill kernel; PA_VERIFY=all routes
+  // single-token sequences here even then; PA_VERIFY=split keeps them apart.
   const bool fp8 = dtype == PA_FP8;
   const char* env = std::getenv("PA_VERIFY");
   if (!fp8 && env != nullptr && std::strcmp(env, "prefill") == 0) return vp;
-  const int32_t min_q = fp8 || (env != nullptr && std::strcmp(env, "all") == 0) ? 1 : 2;
+  const bool all = env != nullptr && std::strcmp(env, "all") == 0;
+  const bool split = env != nullptr && std::strcmp(env, "split") == 0;
+  const int32_t min_q = fp8 || all || (max_query_len >= 2 && !split) ? 1 : 2;
   const bool shape_ok = fp8 ? verify_fp8_supported(head_dim, G) : decode_mfma_supported(dtype, head_dim, G);
   if (!shape_ok || num_seqs < 1 || num_seqs > kMaxVerifySeqs || max_query_len < min_q || max_seq_len <= 0 ||
       num_tokens >= (1 << 26))

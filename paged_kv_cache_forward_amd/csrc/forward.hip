@@ -61,7 +61,12 @@ static pa_status shape_of(int32_t num_seqs, int32_t num_tokens, int32_t num_q_he
                                   fs->use_mfma_prefill);
     return PA_OK;
   }
-  fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
+  // When the multi-token decode launch also takes the single-token
+  // sequences, no single-token decode runs (and needs no workspace).
+  if (fs->vplan.on && fs->vplan.min_q <= 1)
+    fs->plan = DecodePlan{};
+  else
+    fs->plan = make_decode_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len);
   fs->any_prefill = max_query_len > 1 && !(fs->vplan.on && max_query_len <= fs->vplan.max_q);
   fs->use_mfma_prefill = fs->any_prefill && prefill_mfma_supported(c->dtype, c->head_dim, fs->group);
   fs->pplan = make_prefill_plan(num_tokens, num_q_heads, c->head_dim, max_seq_len, max_query_len,

@@ -104,9 +104,12 @@ def test_bit_identical_invariances(name, mode, monkeypatch):
     counts, so where a sequence is cut depends on its position in the batch:
     there a reordered batch is held to the oracle tolerance instead of bits."""
     if mode == "partition":
+        # single-token rows to the partitioned decode kernel, also in batches with longer rows
         monkeypatch.setenv("PA_DECODE", "partition")
+        monkeypatch.setenv("PA_VERIFY", "split")
     else:
         monkeypatch.delenv("PA_DECODE", raising=False)
+        monkeypatch.delenv("PA_VERIFY", raising=False)
     wl = workloads.mini(name)
     base = _device_run(wl)
     ref_bits = base.host(base.out)
@@ -201,9 +204,18 @@ def test_multi_token_decode_against_the_prefill_route(monkeypatch):
 
 
 def test_single_token_rows_through_the_multi_token_kernel(monkeypatch):
-    """PA_VERIFY=all sends single-token sequences through the multi-token decode kernel too."""
+    """PA_VERIFY=all sends single-token sequences through the multi-token decode kernel even in
+    batches of single-token sequences only (by default those keep the single-token decode)."""
     monkeypatch.setenv("PA_VERIFY", "all")
     for name in ("decode_bf16", "decode_gqa8", "mixed_bf16", "shared_bf16") + VERIFY_MINIS:
+        check_parity(workloads.mini(name), pools=False)
+
+
+def test_single_token_rows_kept_apart(monkeypatch):
+    """PA_VERIFY=split keeps the single-token sequences of a batch that also holds longer ones in
+    the single-token decode launch (by default the multi-token launch takes them)."""
+    monkeypatch.setenv("PA_VERIFY", "split")
+    for name in ("mixed_bf16", "mixed_gqa8", "verify_bf16", "verify_gqa8", "verify_mha"):
         check_parity(workloads.mini(name), pools=False)
 
 
