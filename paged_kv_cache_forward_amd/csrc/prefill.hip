@@ -392,6 +392,11 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
     const lds_u8* kl = k_lane + buf * SBUF;
     const lds_u8* vl = v_lane + buf * SBUF;
     const lds_u8* st8 = lds + buf * SBUF;
+    // Wave priority: raised over the two MFMA phases, lowered over the
+    // softmax, so of the two waves sharing a SIMD the one with products to
+    // issue goes first (measured on MI355X: 148.7 -> 147.0 us bf16, 212 -> 208
+    // us fp8, same box, alternating runs).
+    __builtin_amdgcn_s_setprio(2);
     f32x4_t s[RT][4];
     // bf16: the K fragments of 16-key block kt16 + 1 are read while block
     // kt16's MFMAs run (two register sets), so each block's LDS reads are in
@@ -439,7 +444,9 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
       if (F8 && kt16 == 1) __builtin_amdgcn_sched_barrier(0);   // bound how far fragment reads are hoisted
     }
     bf16x8_t pb[RT][2];
+    __builtin_amdgcn_s_setprio(0);
     softmax_tile(s, key0, pb);
+    __builtin_amdgcn_s_setprio(2);
     if constexpr (F8) {
       // P.V on the fp8 codes: the product takes each weight times its key's V
       // exponent (exact), the row sums (ones tile) the weights alone.  Keys
@@ -501,6 +508,7 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
       for (int rt = 0; rt < RT; ++rt)
         o[rt][C::DT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[rt][ks2], o[rt][C::DT], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Pipeline: tile kt+1 is copied into the other LDS stage while tile kt is
