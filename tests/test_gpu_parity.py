@@ -258,6 +258,11 @@ def test_prefill_waves_per_work_group(waves, split, monkeypatch):
     wl = workloads.independent("long_chunks", 41, Hq=32, Hkv=8, D=128, dtype="bf16",
                                cached=[0, 700, 1500], new=[300, 257, 129], pool_extra=4)
     check_parity(wl, pools=False)
+    # one and two query heads per KV head: 256 rows are 256 or 128 tokens per work-group
+    for seed, hq, hkv in ((42, 4, 4), (43, 8, 4)):
+        wl = workloads.independent(f"chunks_g{hq // hkv}", seed, Hq=hq, Hkv=hkv, D=128, dtype="bf16",
+                                   cached=[3, 0, 400, 1], new=[1, 300, 270, 2], pool_extra=4)
+        check_parity(wl, pools=False)
 
 
 def test_degenerate_batches():
