@@ -122,6 +122,8 @@ __device__ __forceinline__ s16x4_t lds_read_tr(const lds_u8* p) {
 struct PrefillArgs {
   AttnArgs a;
   int32_t tok;          // tokens per query tile (rows per work-group / G)
+  int32_t mtok;         // tokens per merge tile (divides tok)
+  int32_t mqtiles;      // merge tiles of the longest chunk
   int32_t qtiles;       // query tiles of the longest chunk
   int32_t piece_keys;   // keys per split piece (multiple of kKeys)
   int32_t pieces;       // pieces of the longest key range
@@ -570,19 +572,22 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
-  const int TOK = pk.tok;
-  const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.qtiles, a.num_seqs);
+  const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.mqtiles, a.num_seqs);
   const int q0 = a.qsl[it.i];
   const int n = a.qsl[it.i + 1] - q0;
   if (n < max(a.prefill_min_q, 2) || q0 < 0 || q0 + n > a.num_tokens) return;
-  const int tok0 = it.qt * TOK;
+  const int tok0 = it.qt * pk.mtok;   // this merge tile's tokens
   if (tok0 >= n) return;
+  // The prefill tile holding these tokens decided whether its rows went to
+  // partials, and how many pieces it wrote.
+  const int ptok0 = tok0 / pk.tok * pk.tok;
   const int L = min(a.seq_lens[it.i], a.bt_stride * kBlock);
   const int c = a.cached_lens[it.i];
-  const int tok_last = min(tok0 + TOK, n) - 1;
-  const int kv_end = a.causal ? min(L, c + tok_last + 1) : L;
+  const int ptok_last = min(ptok0 + pk.tok, n) - 1;
+  const int kv_end = a.causal ? min(L, c + ptok_last + 1) : L;
   if (kv_end <= pk.piece_keys || pk.pieces <= 1) return;   // written by the prefill kernel itself
   const int np = min((kv_end + pk.piece_keys - 1) / pk.piece_keys, pk.pieces);
+  const int tok_last = min(tok0 + pk.mtok, n) - 1;
   const int rows = (tok_last - tok0 + 1) * G;   // rows are token-major: the first `rows` are valid
   for (int idx = threadIdx.x; idx < rows * 8; idx += kMergeThreads) {
     const int r = idx >> 3, sl = idx & 7;
@@ -702,7 +707,11 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
     return fail(PA_ERR_UNSUPPORTED, "pa_forward: prefill grid of %lld work-groups", (long long)wgs);
   if (pp.pieces > 1 && (p_o == nullptr || p_ml == nullptr))
     return fail(PA_ERR_ARG, "pa_forward: prefill split needs workspace");
-  PrefillArgs k{a, TOK, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
+  // The merge works on tiles of at most 128 rows, whatever the prefill tile:
+  // with 256-row prefill tiles that doubles its work-groups.
+  const int MTOK = TOK * G > 128 && TOK % 2 == 0 ? TOK / 2 : TOK;
+  const int mqtiles = (max_query_len + MTOK - 1) / MTOK;
+  PrefillArgs k{a, TOK, MTOK, mqtiles, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
   if (fp8 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: fp8 prefill head_dim %d", a.head_dim);
   int mark = trace_begin(s);
   const dim3 grid((unsigned)wgs), block(64 * nw);
@@ -716,7 +725,7 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   pa_status st = launch_status("pa_forward (prefill)");
   if (st != PA_OK || pp.pieces <= 1) return st;
   mark = trace_begin(s);
-  const dim3 mgrid((unsigned)tiles);
+  const dim3 mgrid((unsigned)((int64_t)mqtiles * a.num_kv_heads * a.num_seqs));
   if (a.head_dim == 128) hipLaunchKernelGGL((prefill_merge_kernel<128>), mgrid, dim3(kMergeThreads), 0, s, k);
   else hipLaunchKernelGGL((prefill_merge_kernel<64>), mgrid, dim3(kMergeThreads), 0, s, k);
   trace_end(s, mark, "prefill_merge");
