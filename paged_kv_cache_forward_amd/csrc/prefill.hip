@@ -11,12 +11,14 @@
 // table like any other cached token.  Prefill is compute-bound (same page as
 // above, bullet on disaggregation), so both contractions run on MFMA.
 //
-// Work-group: 4 waves owning 128 query rows of one KV head g, a row being a
-// (token, query head) pair: row r -> token r / G, head g*G + r % G, so the G
-// heads sharing g share every K/V tile; each wave owns 32 rows (two 16-row
-// MFMA tiles).  Launch order: KV head fastest (every work-group of one KV head
-// runs on one XCD and shares that XCD's L2 for the K/V it re-reads), then the
-// query tile, latest tiles (most keys) first, then the sequence.
+// Work-group: 4 waves owning 128 query rows of one KV head g (or 8 waves and
+// 256 rows, chosen on the host), a row being a (token, query head) pair:
+// row r -> token r / G, head g*G + r % G, so the G heads sharing g share
+// every K/V tile; each wave owns 32 rows (two 16-row MFMA tiles).  Launch
+// order: KV head fastest (every work-group of one KV head runs on one XCD and
+// shares that XCD's L2 for the K/V it re-reads), then the query tile, latest
+// tiles (most keys) first, then the sequence (last in the batch first), then
+// the key piece (highest first).
 //
 // K/V tiles of 64 keys (four 16-token cache blocks) are copied global -> LDS
 // by the buffer unit, one tile ahead, into a double-buffered LDS stage (no
