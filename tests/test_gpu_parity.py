@@ -265,6 +265,25 @@ def test_prefill_waves_per_work_group(waves, split, monkeypatch):
         check_parity(wl, pools=False)
 
 
+@pytest.mark.parametrize("route", ["default", "split"])
+def test_two_query_heads_per_kv_head(route, monkeypatch):
+    """G = 2 on every decode path: single-token decode, multi-token decode (which takes the
+    single-token rows by default and leaves them to the single-token decode under split),
+    chunks, and an fp8 cache -- ragged lengths, a length-1 context, a partial last block."""
+    if route == "split":
+        monkeypatch.setenv("PA_VERIFY", "split")
+    else:
+        monkeypatch.delenv("PA_VERIFY", raising=False)
+    cached = [0, 15, 16, 33, 200, 517, 1029, 3]
+    check_parity(workloads.independent("g2_decode", 51, Hq=16, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[1] * len(cached), pool_extra=3))
+    check_parity(workloads.independent("g2_mixed", 52, Hq=16, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[1, 3, 1, 16, 1, 40, 2, 1], pool_extra=3))
+    check_parity(workloads.independent("g2_fp8", 53, Hq=16, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[1, 5, 1, 1, 30, 1, 1, 2], pool_extra=3,
+                                       cache_dtype="fp8"))
+
+
 def test_degenerate_batches():
     ensure_library()
     # sequences with no query rows between others, a length-1 context, and a 1-token chunk
