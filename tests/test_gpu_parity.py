@@ -284,6 +284,27 @@ def test_two_query_heads_per_kv_head(route, monkeypatch):
                                        cache_dtype="fp8"))
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5])
+def test_softmax_scales(scale, monkeypatch):
+    """Scales other than 1/sqrt(D): a negative one (the prefill folds it into Q by exact sign
+    flips), zero (uniform weights: the mean of the visible V rows) and a sharp one, on the
+    single-token, multi-token and prefill paths and an fp8 cache."""
+    monkeypatch.delenv("PA_VERIFY", raising=False)
+    cached = [0, 40, 300, 1100]
+    check_parity(workloads.independent("scale_decode", 61, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[1, 1, 1, 1], scale=scale, pool_extra=2),
+                 pools=False)
+    check_parity(workloads.independent("scale_mixed", 62, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[70, 1, 5, 200], scale=scale, pool_extra=2),
+                 pools=False)
+    check_parity(workloads.independent("scale_fp8", 63, Hq=32, Hkv=8, D=128, dtype="bf16",
+                                       cached=cached, new=[1, 3, 90, 1], scale=scale, pool_extra=2,
+                                       cache_dtype="fp8"), pools=False)
+    check_parity(workloads.independent("scale_f32", 64, Hq=4, Hkv=2, D=64, dtype="f32",
+                                       cached=cached, new=[1, 1, 1, 1], scale=scale, pool_extra=2),
+                 pools=False)
+
+
 def test_degenerate_batches():
     ensure_library()
     # sequences with no query rows between others, a length-1 context, and a 1-token chunk
