@@ -305,6 +305,23 @@ def test_softmax_scales(scale, monkeypatch):
                  pools=False)
 
 
+def test_over_1024_sequences(monkeypatch):
+    """Past the balanced launches' 1024 sequences the partitioned decode takes the single-token
+    rows and the chunked-prefill kernel the multi-token ones (the multi-token decode is off)."""
+    monkeypatch.delenv("PA_DECODE", raising=False)
+    monkeypatch.delenv("PA_VERIFY", raising=False)
+    rng = np.random.default_rng(71)
+    S = 1100
+    cached = rng.integers(0, 300, size=S)
+    check_parity(workloads.independent("s1100_decode", 72, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                       cached=cached, new=np.ones(S, dtype=np.int64), pool_extra=4),
+                 pools=False)
+    new = np.ones(S, dtype=np.int64)
+    new[::97] = rng.integers(2, 40, size=len(new[::97]))
+    check_parity(workloads.independent("s1100_mixed", 73, Hq=8, Hkv=2, D=128, dtype="bf16",
+                                       cached=cached, new=new, pool_extra=4), pools=False)
+
+
 def test_degenerate_batches():
     ensure_library()
     # sequences with no query rows between others, a length-1 context, and a 1-token chunk
