@@ -612,22 +612,20 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
 }
 
-// Merge of the balanced decode's parts: one work-group of four waves per
-// (sequence, KV head), for all G query heads of that head.  A part's G x D
-// partial block is contiguous, so reading a part is one coalesced load of 2G
-// floats per lane (lane = head * 64/G + chunk).  Wave w folds parts w, w+4,
-// ... in order with the log-sum-exp rule (four parts' loads in flight), then
-// wave 0 combines the four waves in order through LDS.
+// Merge of the balanced decode's parts: one wave per (sequence, KV head), for
+// all G query heads of that head.  A part's G x D partial block is
+// contiguous, so reading a part is one coalesced load of 2G floats per lane
+// (lane = head * 64/G + chunk).  The wave folds the parts in order with the
+// log-sum-exp rule, eight parts' loads in flight per round trip (a sequence
+// has a few parts: one memory round trip), and writes the output.
 template <int G>
-__global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
+__global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
   constexpr int LPH = 64 / G;          // lanes per head
   constexpr int DPL = kD / LPH;        // dims per lane: 2 G
-  constexpr int NWV = 4, U = 4;
-  __shared__ float s_m[NWV][G], s_l[NWV][G];
-  __shared__ float4 s_num[NWV][DPL / 4][64];
+  constexpr int U = 8;
   const AttnArgs& a = k.a;
   const int i = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane / LPH, c = lane % LPH;
+  const int lane = threadIdx.x, h = lane / LPH, c = lane % LPH;
   const int q0 = a.qsl[i];
   if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
   if (min(a.seq_lens[i], a.bt_stride * kBlock) <= 0) return;
@@ -639,13 +637,13 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
   float num[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) num[e] = 0.0f;
-  for (int p0 = w; p0 < P; p0 += NWV * U) {
+  for (int p0 = 0; p0 < P; p0 += U) {
     float2 ml[U];
     float4 x[U][DPL / 4];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (p0 + u * NWV < P) {
-        const size_t e = (slot0 + p0 + u * NWV) * G + h;
+      if (p0 + u < P) {
+        const size_t e = (slot0 + p0 + u) * G + h;
         ml[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
         const float4* src = reinterpret_cast<const float4*>(k.p_acc + e * kD + c * DPL);
 #pragma unroll
@@ -654,7 +652,7 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (p0 + u * NWV >= P) break;
+      if (p0 + u >= P) break;
       const float Mn = fmaxf(Mx, ml[u].x);
       const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(ml[u].x - Mn);
       den = fmaf(den, sa, ml[u].y * sb);
@@ -668,39 +666,10 @@ __global__ __launch_bounds__(256) void merge_balanced_kernel(BalancedArgs k) {
       Mx = Mn;
     }
   }
-  if (c == 0) {
-    s_m[w][h] = Mx;    // -inf for a wave without parts: weight 0 below
-    s_l[w][h] = den;
-  }
-#pragma unroll
-  for (int v = 0; v < DPL / 4; ++v)
-    s_num[w][v][lane] = make_float4(num[4 * v], num[4 * v + 1], num[4 * v + 2], num[4 * v + 3]);
-  __syncthreads();
-  if (w != 0) return;
-  float Mt = s_m[0][h];
-#pragma unroll
-  for (int ww = 1; ww < NWV; ++ww) Mt = fmaxf(Mt, s_m[ww][h]);
-  float dt = 0.0f;
-  float o[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-#pragma unroll
-  for (int ww = 0; ww < NWV; ++ww) {
-    const float f = fast_exp2(s_m[ww][h] - Mt);
-    dt = fmaf(f, s_l[ww][h], dt);
-#pragma unroll
-    for (int v = 0; v < DPL / 4; ++v) {
-      const float4 y = s_num[ww][v][lane];
-      o[4 * v + 0] = fmaf(f, y.x, o[4 * v + 0]);
-      o[4 * v + 1] = fmaf(f, y.y, o[4 * v + 1]);
-      o[4 * v + 2] = fmaf(f, y.z, o[4 * v + 2]);
-      o[4 * v + 3] = fmaf(f, y.w, o[4 * v + 3]);
-    }
-  }
-  const float inv = 1.0f / dt;
+  const float inv = 1.0f / den;
   uint32_t wd[DPL / 2];
 #pragma unroll
-  for (int e = 0; e < DPL / 2; ++e) wd[e] = pack_bf16x2(o[2 * e] * inv, o[2 * e + 1] * inv);
+  for (int e = 0; e < DPL / 2; ++e) wd[e] = pack_bf16x2(num[2 * e] * inv, num[2 * e + 1] * inv);
   uint8_t* op = (uint8_t*)a.out + ((size_t)q0 * a.num_q_heads + g * G + h) * kRowBytes + c * DPL * 2;
   if constexpr (DPL == 2) {
     *reinterpret_cast<uint32_t*>(op) = wd[0];
@@ -741,7 +710,7 @@ pa_status launch_balanced_g(const BalancedArgs& k, int depth, hipStream_t s) {
   pa_status st = launch_status("pa_forward (decode, balanced)");
   if (st != PA_OK) return st;
   mark = trace_begin(s);
-  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(256), 0, s, k);
+  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(64), 0, s, k);
   trace_end(s, mark, "merge");
   return launch_status("pa_forward (decode merge, balanced)");
 }
