@@ -531,9 +531,9 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
     const u32x4_t rv = rsrc_words(vc + off, kTileBytes);
     uint4* dst = stage(sI);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+    for (int ks = 0; ks < 4; ++ks) lds_copy16_nt(rk, dst + ks * 64, koff + ks * 64);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) lds_copy16(rv, dst + 256 + e * 64, voff + e * kRowBytes);
+    for (int e = 0; e < 4; ++e) lds_copy16_nt(rv, dst + 256 + e * 64, voff + e * kRowBytes);
   };
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, n - 1), s0);

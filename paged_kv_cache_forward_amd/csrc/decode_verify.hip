@@ -271,9 +271,9 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       const u32x4_t rk = rsrc_words(kc + off, TILE);
       const u32x4_t rv = rsrc_words(vc + off, TILE);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) lds_copy16(rk, dst + p * 64, j * kD + r * 16 + p * 64);
+      for (int p = 0; p < 2; ++p) lds_copy16_nt(rk, dst + p * 64, j * kD + r * 16 + p * 64);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) lds_copy16(rv, dst + 128 + p * 64, (p * 64 + lane) * kBlock);
+      for (int p = 0; p < 2; ++p) lds_copy16_nt(rv, dst + 128 + p * 64, (p * 64 + lane) * kBlock);
       const size_t xoff = (size_t)bid * Hkv * kBlock;
       const u32x4_t rkx = rsrc_words(kx + xoff, kBlock);
       const u32x4_t rvx = rsrc_words(vx + xoff, kBlock);
@@ -289,9 +289,9 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       const u32x4_t rk = rsrc_words(kc + off, bytes);
       const u32x4_t rv = rsrc_words(vc + off, bytes);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) lds_copy16(rk, dst + ks * 64, koff + ks * 64);
+      for (int ks = 0; ks < 4; ++ks) lds_copy16_nt(rk, dst + ks * 64, koff + ks * 64);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) lds_copy16(rv, dst + 256 + p * 64, voff + p * 64);
+      for (int p = 0; p < 4; ++p) lds_copy16_nt(rv, dst + 256 + p * 64, voff + p * 64);
     }
   };
 #pragma unroll

@@ -155,6 +155,18 @@ __device__ __forceinline__ void lds_copy16(u32x4_t rsrc, const void* lds, int vo
                : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// As lds_copy16, with the non-temporal (nt) cache policy: the lines are
+// fetched as a stream that the caches need not keep.  For data read once per
+// launch (a decode's K/V tiles).  Measured on MI355X, batched decode (64
+// sequences, 528 MB of K/V per launch): 99 -> 90.5 us; long context 0.74 ->
+// 0.79 of HBM peak.  Where other sequences re-read the same blocks from the
+// L2 (a shared prefix) it costs ~2%.
+__device__ __forceinline__ void lds_copy16_nt(u32x4_t rsrc, const void* lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
 // As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
 __device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
