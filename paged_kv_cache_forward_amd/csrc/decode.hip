@@ -453,10 +453,12 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
                 !(kind != nullptr && std::strcmp(kind, "partition") == 0);
   if (pl.balanced) {
     // 1024 single-wave work-groups in all: one per SIMD, every one resident
-    // at once (LDS and registers allow four per CU at depth 3), never more
-    // than the tiles there can be.  Measured on MI355X: HBM-bound batches
-    // gain nothing from more waves or deeper rings.  PA_DECODE_TOTAL_WAVES
-    // and PA_DECODE_DEPTH override.
+    // at once, never more than the tiles there can be; two tiles in flight.
+    // Measured on MI355X with the non-temporal tile copies (same box, two
+    // runs each, us of decode): batched decode 87.5-88.2 at depth 2 against
+    // 89.1-89.5 at depth 3 and 90.0-90.1 at depth 4; long context equal;
+    // a shared prefix 245-246 against 255-256.  768, 1280 or 1536 waves are
+    // slower.  PA_DECODE_TOTAL_WAVES and PA_DECODE_DEPTH override.
     int64_t target = 1024;
     if (const char* tw = std::getenv("PA_DECODE_TOTAL_WAVES")) {
       const int v = std::atoi(tw);
@@ -465,7 +467,7 @@ DecodePlan make_decode_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
     const int64_t max_tiles = (int64_t)num_seqs * (whole / kBlock);
     const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(target / num_kv_heads, max_tiles));
     pl.waves_per_head = (int32_t)wg;
-    pl.depth = 3;
+    pl.depth = 2;
     if (const char* dp = std::getenv("PA_DECODE_DEPTH")) {
       const int v = std::atoi(dp);
       if (v >= 2 && v <= 4) pl.depth = v;
