@@ -284,7 +284,7 @@ def cpu_baseline(wl, min_s=10.0, max_s=30.0):
 
 def allocator_rate(pa, wl, reps=3):
     """Host block allocator: replay the workload's allocation trace through the C ABI (ctypes included)."""
-    from paged_kv_cache_forward_amd.replay import _drive
+    from workloads import drive as _drive
     best = None
     for _ in range(reps):
         alloc = pa.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
@@ -463,7 +463,7 @@ def main():
     import torch
     import workloads
     import paged_kv_cache_forward_amd as pa
-    from paged_kv_cache_forward_amd.replay import DeviceRun
+    from workloads.device import DeviceRun
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

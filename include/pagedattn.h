@@ -148,8 +148,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs,
 /*
  * pa_forward_workspace_size — bytes of device scratch pa_forward needs for the
  * same host arguments (0 when the call needs none).  Depends only on its
- * arguments and the tuning variables PA_DECODE, PA_DECODE_TOTAL_WAVES,
- * PA_SPLIT and PA_PREFILL_SPLIT (see pa_forward).
+ * arguments and on the tuning variables that choose the route or the split
+ * (see pa_forward): PA_DECODE, PA_DECODE_TOTAL_WAVES, PA_SPLIT, PA_VERIFY,
+ * PA_VERIFY_TOTAL_WAVES and PA_PREFILL_SPLIT.
  */
 size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
                                  int32_t max_seq_len, int32_t max_query_len,
@@ -211,7 +212,7 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_DECODE=valu          force the vector decode kernel (partitioned)
  *   PA_DECODE_TOTAL_WAVES=<1..65536>  balanced decode: waves in all (default
  *            1024, one per SIMD), divided evenly among the KV heads
- *   PA_DECODE_DEPTH=2|3|4   balanced decode: K/V tiles in flight per wave (default 3)
+ *   PA_DECODE_DEPTH=2|3|4   balanced decode: K/V tiles in flight per wave (default 2)
  *   PA_SPLIT=auto (default) | off | <tokens>   partitioned decode: partition
  *            size (a multiple of 16, <= 8192); auto aims at ~4096 (sequence,
  *            KV head, partition) work-groups with partitions of 128..2048 tokens
@@ -220,10 +221,15 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_VERIFY=all           send single-token sequences through the multi-token
  *            decode path too (one launch for both kinds)
  *   PA_VERIFY_TOTAL_WAVES=<1..65536>  multi-token decode: waves in all (default 1024)
- *   PA_VERIFY_DEPTH=2|3|4   multi-token decode: K/V tiles in flight per wave
- *            (default 3, or 2 when four work-groups would not fit a CU's LDS)
+ *   PA_VERIFY_DEPTH=2..5    multi-token decode: K/V tiles in flight per wave
+ *            (bf16: default 3, or 2 when four work-groups would not fit a
+ *            CU's LDS; 4 and 5 both run 4.  fp8 cache: default 3; 5 runs 5,
+ *            any other value 3)
  *   PA_PREFILL_ROWS=32 (default) | 64   chunked prefill: (token, head) rows per
  *            wave (64: head_dim 128 only)
+ *   PA_PREFILL_WAVES=4|8    chunked prefill (bf16, head_dim 128, 32 rows per
+ *            wave): waves per work-group (default 8 when fewer than half of
+ *            num_seqs * max_query_len are query tokens, else 4)
  *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
  *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
  *            max(1024, a quarter of the longest sequence)

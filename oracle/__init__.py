@@ -36,9 +36,13 @@ Modules:
   cache      -- cache write through a slot mapping; whole-block copies
   attention  -- paged attention over a varlen super-batch; split/merge pieces
 
-Parity status: every function is pinned by ``tests/test_oracle_*.py`` (closed
-forms, the worked allocation example printed on [SLAVA], invariances, and a
-float64 library attention routine); none is "parity unpinned".
+Parity status: every function is pinned by ``tests/test_oracle_*.py``:
+``numerics.to_f64`` by torch's own bfloat16/float32 conversions over every
+bf16 bit pattern and by values the formats fix; the rest by closed forms, the
+worked allocation example printed on [SLAVA], invariances, and a float64
+library attention routine fed through torch's conversions.  Planted mistakes
+in each module fail a pin (``tests/test_oracle_mutations.py``).  None is
+"parity unpinned".
 """
 
 from .numerics import to_f64

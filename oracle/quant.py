@@ -18,6 +18,10 @@ with quantisation.  They fix no format.  Readings taken here:
     one to E4M3.
   * Rounding: to the nearest E4M3 value, ties to an even mantissa (the
     usual IEEE rule).  Because |x * 2^-e| <= 448 nothing saturates.
+  * Non-finite inputs: E4M3 FN has no infinity, so a NaN or an infinite
+    element is stored as the NaN code (0x7f, with the element's sign bit:
+    0xff when it is set), and the row's scale is taken from its finite
+    elements only (a row with none takes e = 0).
   * Dequantised value: decode(code) * 2^e, exact in float64.
   * Pool layout: num_blocks * num_kv_heads * (16 * D + 16) bytes in two
     planes.  First the codes, ``[num_blocks][num_kv_heads][16 * D]``: per
@@ -87,11 +91,17 @@ def row_exponent(amax):
 
 
 def quantize_rows(x):
-    """Rows of values (last axis = one row) -> (uint8 codes, uint8 biased exponent per row)."""
+    """Rows of values (last axis = one row) -> (uint8 codes, uint8 biased exponent per row).
+
+    NaN and infinite elements become the NaN code with their sign bit; the
+    scale ignores them.
+    """
     x = np.asarray(x, dtype=np.float64)
-    e = row_exponent(np.max(np.abs(x), axis=-1))
-    codes = encode_e4m3(np.ldexp(x, -e[..., None]))
-    return codes, (e + SCALE_BIAS).astype(np.uint8)
+    finite = np.isfinite(x)
+    e = row_exponent(np.max(np.where(finite, np.abs(x), 0.0), axis=-1))
+    codes = encode_e4m3(np.ldexp(np.where(finite, x, 0.0), -e[..., None]))
+    nan_codes = np.where(np.signbit(x), 0xFF, 0x7F).astype(np.uint8)
+    return np.where(finite, codes, nan_codes), (e + SCALE_BIAS).astype(np.uint8)
 
 
 def dequantize_rows(codes, exp_codes):

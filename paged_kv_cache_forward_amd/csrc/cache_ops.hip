@@ -79,16 +79,19 @@ __device__ __forceinline__ int fp8_row_exponent(float amax) {
   return min(max(e, -126), 127);
 }
 
-// E4M3 (OCP, FN) code of x * 2^-e, which lies in [-448, 448]: nearest value,
-// ties to an even mantissa; the sign of zero is kept.  Below 2^-6 the code
-// counts steps of 2^-9 (eight steps are the smallest normal, code 0x08);
-// above, mantissa (f - 1) * 8 of y = f * 2^E, a carry moving to the next binade.
+// E4M3 (OCP, FN) code of x * 2^-e, which lies in [-448, 448] for a finite x:
+// nearest value, ties to an even mantissa; the sign of zero is kept.  Below
+// 2^-6 the code counts steps of 2^-9 (eight steps are the smallest normal,
+// code 0x08); above, mantissa (f - 1) * 8 of y = f * 2^E, a carry moving to
+// the next binade.  E4M3 FN has no infinity: a NaN or infinite x is stored as
+// the NaN code 0x7f with x's sign bit.
 __device__ __forceinline__ uint32_t fp8_code(float x, int e) {
   const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  if (!__builtin_isfinite(x)) return sign | 0x7fu;
   const float a = fabsf(ldexpf(x, -e));
-  if (a < 0x1p-6f) return sign | (uint32_t)rintf(a * 512.0f);
+  if (a < 0x1p-6f) return sign | (uint32_t)(int)rintf(a * 512.0f);
   int E = (int)(__float_as_uint(a) >> 23) - 127;
-  uint32_t q = (uint32_t)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
+  uint32_t q = (uint32_t)(int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
   if (q == 8u) {
     q = 0u;
     ++E;
@@ -116,7 +119,10 @@ __global__ __launch_bounds__(256) void write_kv_fp8_kernel(const uint32_t* __res
   const bool is_v = blockIdx.y != 0;
   const uint32_t w = (is_v ? v : k)[rw * (D / 2) + lane];   // dims 2 lane, 2 lane + 1 (bf16)
   const float x0 = bf16_lo(w), x1 = bf16_hi(w);
-  const int e = fp8_row_exponent(wave_max(fmaxf(fabsf(x0), fabsf(x1))));
+  // The scale comes from the row's finite elements only.
+  const float a0 = __builtin_isfinite(x0) ? fabsf(x0) : 0.0f;
+  const float a1 = __builtin_isfinite(x1) ? fabsf(x1) : 0.0f;
+  const int e = fp8_row_exponent(wave_max(fmaxf(a0, a1)));
   const uint32_t c0 = fp8_code(x0, e), c1 = fp8_code(x1, e);
   const int64_t blk = slot / kBlock;
   const int row = (int)(slot - blk * kBlock);

@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 def _run(name):
     ensure_library()
-    from paged_kv_cache_forward_amd.replay import DeviceRun
+    from workloads.device import DeviceRun
     import torch
     run = DeviceRun(workloads.mini(name))
     torch.cuda.synchronize()

@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 def _device_run(wl, **kw):
     ensure_library()
-    from paged_kv_cache_forward_amd.replay import DeviceRun
+    from workloads.device import DeviceRun
     run = DeviceRun(wl, **kw)
     run.step()
     import torch
@@ -380,7 +380,7 @@ def test_copy_blocks_bit_exact():
 def test_error_paths(monkeypatch):
     pa = ensure_library()
     import torch
-    from paged_kv_cache_forward_amd.replay import DeviceRun
+    from workloads.device import DeviceRun
     wl = workloads.mini("decode_bf16")
     run = DeviceRun(wl)
     run.step_writes()
@@ -423,7 +423,8 @@ FP8_MINIS = ("decode_fp8", "verify_fp8", "fp8_gqa8", "fp8_mha_noncausal", "mixed
 
 def test_fp8_write_edge_rows():
     """Quantised write, bit for bit against the oracle: zero rows, -0, bf16 subnormals, the
-    largest bf16 values, exact rounding ties, padding and out-of-pool slots."""
+    largest bf16 values, exact rounding ties, NaN and infinite elements, padding and
+    out-of-pool slots."""
     pa = ensure_library()
     import torch
     from helpers import _write_fp8
@@ -434,13 +435,16 @@ def test_fp8_write_edge_rows():
             np.concatenate([[448.0], 1 + np.arange(1, D) / 16.0 * 0.0625]),        # amax 448: ties at 1/16 steps
             np.concatenate([[1.0], np.full(D - 1, 1 + 1 / 16)]),
             np.concatenate([[2.0 ** -120], np.full(D - 1, 3 * 2.0 ** -130)]),
-            rng.standard_normal(D) * 1e-3, rng.standard_normal(D) * 1e3]
+            rng.standard_normal(D) * 1e-3, rng.standard_normal(D) * 1e3,
+            # non-finite elements: the NaN code with their sign, the scale from the finite ones
+            np.concatenate([[np.nan, np.inf, -np.inf], rng.standard_normal(D - 3) * 5.0]),
+            np.full(D, np.inf)]
     T = len(rows)
     x = np.stack(rows)[:, None, :].repeat(Hkv, axis=1)
     x[:, 1] *= -0.75
     k = workloads.bf16_bits(x.astype(np.float32))
     v = workloads.bf16_bits((x[:, :, ::-1] * 0.5).astype(np.float32))
-    slots = np.array([3, -1, 17, 79, 40, NB * B + 2, 65, 0, 50], dtype=np.int64)
+    slots = np.array([3, -1, 17, 79, 40, NB * B + 2, 65, 0, 50, 22, 33], dtype=np.int64)
     kp = oracle.fp8_pool(NB, Hkv, D)
     vp = oracle.fp8_pool(NB, Hkv, D)
     keep = slots < NB * B

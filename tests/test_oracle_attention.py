@@ -99,6 +99,14 @@ def test_matches_library_sdpa(case):
         r += len(Q)
 
 
+def widen_by_torch(x, dtype):
+    """Stored rows -> float64 through torch's own dtype conversions (not the oracle's widening)."""
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float64).numpy()
+    t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
 @pytest.mark.parametrize("name", ["decode_f32", "mixed_bf16", "shared_bf16", "noncausal_bf16"])
 def test_workload_matches_library_sdpa(name):
     wl = workloads.mini(name)
@@ -106,8 +114,8 @@ def test_workload_matches_library_sdpa(name):
     rows = logical_rows(wl)
     qsl = wl.query_start_loc
     for i, (K, V) in enumerate(rows):
-        Q = oracle.to_f64(wl.q[qsl[i]:qsl[i + 1]], wl.dtype)
-        want = sdpa_f64(Q, oracle.to_f64(K, wl.dtype), oracle.to_f64(V, wl.dtype),
+        Q = widen_by_torch(wl.q[qsl[i]:qsl[i + 1]], wl.dtype)
+        want = sdpa_f64(Q, widen_by_torch(K, wl.dtype), widen_by_torch(V, wl.dtype),
                         int(wl.cached_lens[i]), wl.scale, wl.causal)
         assert np.max(np.abs(run.out[qsl[i]:qsl[i + 1]] - want)) <= 1e-12
 

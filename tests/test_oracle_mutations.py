@@ -47,6 +47,8 @@ MUTATIONS = [
     ("scale-not-minimal", "quant.py", "e = np.where(safe <= np.ldexp(E4M3_MAX, e - 1), e - 1, e)", "e = e + 1", ["test_oracle_quant.py"]),
     ("v-not-transposed", "quant.py", "return rows * D + d if kind == \"k\" else d * block_size + rows", "return rows * D + d", ["test_oracle_quant.py"]),
     ("scale-bias", "quant.py", "e = np.asarray(exp_codes, dtype=np.int64) - SCALE_BIAS", "e = np.asarray(exp_codes, dtype=np.int64) - SCALE_BIAS - 1", ["test_oracle_quant.py"]),
+    ("bf16-shift", "numerics.py", "x.astype(np.uint32) << np.uint32(16)", "x.astype(np.uint32) << np.uint32(15)", ["test_oracle_numerics.py", "test_oracle_attention.py"]),
+    ("bf16-low-half", "numerics.py", "x.astype(np.uint32) << np.uint32(16)", "x.astype(np.uint32)", ["test_oracle_numerics.py", "test_oracle_attention.py"]),
     ("v-from-k", "cache.py", "v_cache[blocks, :, rows, :] = np.asarray(v)[keep]", "v_cache[blocks, :, rows, :] = np.asarray(k)[keep]", ["test_oracle_cache.py"]),
 ]
 

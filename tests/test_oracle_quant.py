@@ -89,6 +89,21 @@ def test_row_exponent_closed_forms():
     assert np.all(amax > np.ldexp(448.0, e - 1))                 # smallest such e
 
 
+def test_non_finite_elements():
+    """NaN and infinities are stored as the NaN code with their sign; the scale comes from the finite
+    elements.  Row [NaN, +inf, -inf, 1, -3]: amax 3 -> e = -7 (448 * 2^-8 = 1.75 < 3 <= 3.5 = 448 * 2^-7),
+    so 1 * 2^7 = 128 -> 0x70 and -3 * 2^7 = -384 = -1.5 * 2^8 -> 0xFC; -NaN (sign set) -> 0xFF."""
+    row = np.array([[np.nan, np.inf, -np.inf, 1.0, -3.0, -np.nan]])
+    codes, exps = oracle.quantize_rows(row)
+    assert list(codes[0]) == [0x7F, 0x7F, 0xFF, 0x70, 0xFC, 0xFF]
+    assert list(exps) == [127 - 7]
+    back = oracle.dequantize_rows(codes, exps)[0]
+    assert np.isnan(back[:3]).all() and np.isnan(back[5]) and list(back[3:5]) == [1.0, -3.0]
+    # a row with no finite element takes e = 0
+    codes, exps = oracle.quantize_rows(np.array([[np.inf, np.nan]]))
+    assert list(codes[0]) == [0x7F, 0x7F] and list(exps) == [127]
+
+
 def test_quantisation_error_bound():
     """Relative error <= 2^-4 in the normal range (half a 3-bit ulp), absolute <= 2^-10 * 2^e below it."""
     rng = np.random.default_rng(2)

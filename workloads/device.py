@@ -1,42 +1,22 @@
-"""Run one engine step of a workload through the library on a GPU.
+"""GPU-side harness: run one engine step of a workload through the library.
 
-Replays the workload's allocator trace on the library's host allocator, puts
-the pools, queries and metadata in device memory (torch tensors), stores the
-cached tokens with ``pa_write_kv``, and then performs the step itself:
-``pa_copy_blocks`` for copy-on-write pairs, ``pa_write_kv`` for the step's
-new tokens, ``pa_forward`` for attention.  Every step of the path runs in the
-HIP library; this module only marshals.
+Test and benchmark infrastructure (tests, smoke and bench.py use it; the
+library never imports it).  Replays the workload's allocator trace on the
+library's host allocator (``workloads.drive``), puts the pools, queries and
+metadata in device memory (torch tensors), stores the cached tokens with
+``pa_write_kv``, and then performs the step itself: ``pa_copy_blocks`` for
+copy-on-write pairs, ``pa_write_kv`` for the step's new tokens, ``pa_forward``
+for attention.  Every step of the path runs in the HIP library; this module
+only marshals.
 """
 
 import numpy as np
 
 import paged_kv_cache_forward_amd as pa
 
+from . import drive
+
 BF16_NAN_BITS = 0x7FC0
-
-
-def _drive(wl, alloc):
-    """Replay wl.trace on ``alloc``: ids per handle, slots of cached and new rows, step copy pairs."""
-    ids = {}
-    ctx_slots = np.full(len(wl.ctx_k), -1, dtype=np.int64)
-    new_slots = np.full(len(wl.k_new), -1, dtype=np.int64)
-    cow = []
-    for op in wl.trace:
-        if op[0] == "create":
-            ids[op[1]] = alloc.create()
-        elif op[0] == "fork":
-            ids[op[1]] = alloc.fork(ids[op[2]], op[3])
-        else:
-            _, s, n, row0 = op
-            slots, pairs = alloc.append(ids[s], n)
-            if op[0] == "append_ctx":
-                if pairs:
-                    raise RuntimeError("cached-token append produced copy-on-write pairs")
-                ctx_slots[row0:row0 + n] = slots
-            else:
-                new_slots[row0:row0 + n] = slots
-                cow.extend(pairs)
-    return ids, ctx_slots, new_slots, cow
 
 
 class DeviceRun:
@@ -55,7 +35,7 @@ class DeviceRun:
         self.tdtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
         order = wl.free_order if free_order is None else free_order
         self.alloc = pa.BlockAllocator(wl.num_blocks, wl.block_size, order)
-        self.ids, self.ctx_slots, self.new_slots, self.cow = _drive(wl, self.alloc)
+        self.ids, self.ctx_slots, self.new_slots, self.cow = drive(wl, self.alloc)
 
         if wl.cache == "fp8":
             shape = pa.fp8_pool_shape(wl.pool_blocks, wl.num_kv_heads, wl.head_dim)
