@@ -9,21 +9,32 @@ Inputs are resident in HBM before the timed region.  Steps rotate over enough
 identical copies of the K/V pools that no step finds its K/V in the 256 MB
 last-level cache, as successive layers of a model would not.
 
-Default workload: 64 decode sequences with contexts U[128, 4096], 32 query /
-8 KV heads, head_dim 128, bf16, 16-token blocks scattered over a 20000-block
-pool.  Prints one JSON line on stdout; progress goes to stderr.
+Headline workloads: `batched_decode` (64 decode sequences with contexts
+U[128, 4096], 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
+scattered over a 20000-block pool) gives `value`; `long_context_decode` (8
+sequences of 32K-128K tokens, 64/8 heads, split-KV) is reported beside it in
+`headline_configs`.  Prints one JSON line on stdout; progress goes to stderr.
 
-Two timed regions of --steps steps each follow --warmup untimed steps: the
-first (no instrumentation) gives `value` and `ms_per_step`; the second runs
-with the library's per-kernel HIP-event tracing on and gives the kernel
-durations behind `roofline`.  Side legs: the prefill chunks of the mixed
-super-batch (MFMA utilisation), a speculative-decoding step (64 sequences
-verifying 2..8 tokens each) through the multi-token decode kernel and, for
-comparison, through the chunked-prefill kernel, the default decode step on a
-quantised fp8 cache (`fp8_decode`), a step launched call by call vs replayed from
-a HIP graph (`graph`, tiny and batched decode), the host allocator's replay
-rate, and the CPU oracle (`cpu_baseline`).  `--copy-probe` instead runs only
-the known-size copy used to calibrate rocprofv3's HBM byte counters.
+Before any timing, untimed steps run until the GPU has been busy for a few
+hundred milliseconds (`settle_ms`), so that the clocks have left their idle
+state, as in a serving loop; then --warmup untimed steps, then timed regions
+of --steps steps each: the first (HIP events around the K steps only) gives
+`value` and `ms_per_step`; the second records an event after every step
+(median, p10, p90 per step); the third repeats one pool copy every step (the
+"hot" median: K/V partly served from the caches); the fourth runs with the
+library's per-kernel HIP-event tracing on and gives the kernel durations behind
+`roofline`.  After the first, a probe kernel reads the shader clock
+(`pa_trace_clock`).  Side legs: the prefill chunks of the mixed super-batch
+(MFMA utilisation), a speculative-decoding step (64 sequences verifying 2..8
+tokens each) through the multi-token decode kernel and, for comparison,
+through the chunked-prefill kernel, the default decode step on a quantised fp8
+cache (`fp8_decode`), every other configuration as a whole step (`configs`,
+with its allocator accounting), a step launched call by call vs replayed from
+a HIP graph (`graph`), the host allocator's replay rate, and the CPU oracle
+(`cpu_baseline`, every configuration, in a child process that never touches
+the GPU: a process pool over (sequence, KV head) items, one BLAS thread each).
+`--copy-probe` instead runs only the known-size copy used to calibrate
+rocprofv3's HBM byte counters.
 """
 
 import argparse
@@ -118,13 +129,92 @@ def prefill_flops(wl):
     return int(f)
 
 
-def run_steps(run, steps, stream, with_writes=True):
-    """Enqueue `steps` steps, rotating pool copies; returns nothing (the caller brackets and synchronises)."""
+def run_steps(run, steps, stream, with_writes=True, rotate=True, events=None):
+    """Enqueue `steps` steps, rotating pool copies (or always the first with rotate=False); with
+    `events` (steps + 1 of them) one is recorded before the first step and after each step."""
+    if events is not None:
+        events[0].record(stream)
     for k in range(steps):
-        run.use(k)
+        run.use(k if rotate else 0)
         if with_writes:
             run.step_writes(stream)
         run.forward(stream)
+        if events is not None:
+            events[k + 1].record(stream)
+
+
+SETTLE_MS = 300.0
+
+
+def settle(run, stream, with_writes=True, min_ms=SETTLE_MS):
+    """Untimed steps until the GPU has been busy for at least `min_ms` (wall clock, synchronised
+    every few steps): the clocks leave their idle state before anything is timed."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        run_steps(run, 8, stream, with_writes)
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
+def step_distribution(run, steps, stream, with_writes=True, rotate=True):
+    """Per-step times (us) from events recorded after every step: median, p10, p90."""
+    import torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    run_steps(run, steps, stream, with_writes, rotate, events=evs)
+    torch.cuda.synchronize()
+    us = np.array([evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(steps)])
+    p10, p50, p90 = np.percentile(us, [10, 50, 90])
+    return {"median": round(float(p50), 2), "p10": round(float(p10), 2), "p90": round(float(p90), 2)}
+
+
+def read_mclk_mhz():
+    """Current memory clock from the driver's DPM table in sysfs (the level marked '*'), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_mclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.strip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def clocks(pa, stream):
+    """Shader clock the GPU runs at right now (probe kernel) and the memory clock (sysfs)."""
+    try:
+        sclk = round(pa.pa_trace_clock(stream), 1)
+    except Exception as e:                     # instrumentation only: never fail the bench on it
+        log(f"clock probe failed: {e}")
+        sclk = None
+    return {"sclk_mhz": sclk, "mclk_mhz": read_mclk_mhz()}
+
+
+def alloc_accounting(wl, run):
+    """The host allocator's view of the batch after the step's allocations ("Was ändert
+    PagedAttention an der KV-Speicherzuweisung für LLMs?", sections "Ungenutzten Platz in Blöcken
+    berechnen" and "Gemeinsame Nutzung ..."): blocks, slots, tokens and the unused share of the
+    allocated slots, per sequence (logical) and per physical block (a shared block counted once)."""
+    st = run.alloc.stats()
+    filled = {}
+    for i, t in enumerate(run.tables):
+        L = int(wl.seq_lens[i])
+        for p, b in enumerate(t):
+            n = min(wl.block_size, L - p * wl.block_size)
+            if n > 0:
+                filled[b] = max(filled.get(b, 0), n)
+    tokens_physical = int(sum(filled.values()))
+    out = {k: int(v) for k, v in st.items()}
+    out["tokens_physical"] = tokens_physical
+    out["unused_frac_logical"] = round(1.0 - st["tokens_logical"] / max(st["slots_logical"], 1), 5)
+    out["unused_frac_physical"] = round(1.0 - tokens_physical / max(st["slots_physical"], 1), 5)
+    out["sharing_factor"] = round(st["tokens_logical"] / max(tokens_physical, 1), 3)
+    return out
 
 
 def timed_region(run, steps, stream, with_writes=True):
@@ -233,53 +323,116 @@ def measured_traffic(kernel, workload):
     return int(round(fetch + write))
 
 
-def cpu_baseline(wl, min_s=10.0, max_s=30.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload.
+# -- CPU oracle baseline -----------------------------------------------------------
+#
+# Runs in a child process started with subprocess (never an exec of this
+# process) that imports neither torch nor the library and never opens the GPU,
+# with one BLAS thread per process.  It generates each configuration from its
+# seed, builds the oracle's pools (not timed), then times whole passes of the
+# oracle over the batch with a fork-started pool of N = len(sched_getaffinity)
+# worker processes over (sequence, KV head) items, longest first.
 
-    The sample is the workload's decode sequences in batch order, cycled until
-    at least `min_s` seconds of oracle time have passed (checked after each
-    sequence); its rate is reported in the bench's own unit (KV GB/s).
-    """
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
+_CPU = {}
+
+
+def _cpu_noop(_):
+    return os.getpid()
+
+
+def _cpu_item(item):
+    """The oracle on sequence i's query rows of KV head g's query heads, that head's pool slice."""
     import oracle
+    i, g = item
+    wl, ref = _CPU["wl"], _CPU["ref"]
+    qsl = wl.query_start_loc
+    r0, r1 = int(qsl[i]), int(qsl[i + 1])
+    G = wl.num_q_heads // wl.num_kv_heads
+    out = oracle.ref_paged_attention(wl.q[r0:r1, g * G:(g + 1) * G], ref.k_cache[:, g:g + 1], ref.v_cache[:, g:g + 1],
+                                     [ref.tables[i]], wl.seq_lens[i:i + 1], np.array([0, r1 - r0]),
+                                     wl.cached_lens[i:i + 1], wl.scale, wl.causal, wl.block_size, wl.dtype)
+    return float(np.abs(out).sum())
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_child_main(spec):
+    """--cpu-baseline-child: time the oracle on each named configuration; one JSON line on stdout."""
+    import multiprocessing as mp
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import workloads
     from helpers import OracleRun
+    n_proc = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        threads = 1
-    log("cpu baseline: building the oracle's pools (not timed)")
-    ref = OracleRun(wl, compute_out=False)
-    qsl = wl.query_start_loc
-    e = elem_bytes(wl)
-    seqs = decode_rows(wl) or list(range(wl.num_seqs))
-    done_bytes, done_seqs, done_tokens, passes = 0, 0, 0, 0
-    t0 = time.perf_counter()
-    while True:
-        for i in seqs:
-            r0, r1 = int(qsl[i]), int(qsl[i + 1])
-            oracle.ref_paged_attention(wl.q[r0:r1], ref.k_cache, ref.v_cache, [ref.tables[i]],
-                                       wl.seq_lens[i:i + 1], np.array([0, r1 - r0]), wl.cached_lens[i:i + 1],
-                                       wl.scale, wl.causal, wl.block_size, wl.dtype)
-            done_seqs += 1
-            done_tokens += r1 - r0
-            done_bytes += int(wl.seq_lens[i]) * 2 * wl.num_kv_heads * wl.head_dim * e
-            if time.perf_counter() - t0 > max_s:
-                break
-        passes += 1
-        if time.perf_counter() - t0 >= min_s:
-            break
-    dt = time.perf_counter() - t0
-    return {
-        "value": round(done_bytes / dt / 1e9, 4),
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"ref_paged_attention (NumPy float64) over the {len(seqs)} decode sequences of {wl.name}, "
-                  f"{passes} pass(es): {done_seqs} sequence calls, {done_tokens} query tokens, "
-                  f"{done_bytes / 1e9:.2f} GB of K/V in {dt:.1f} s",
-        "tokens_per_s": round(done_tokens / dt, 3),
-    }
+        blas = None
+    res = {"cores": n_proc, "cpu_model": cpu_model(), "blas_threads_per_process": blas, "configs": {}}
+    for name in spec["names"]:
+        log(f"cpu baseline: {name}: generating it and building the oracle's pools (not timed)")
+        wl = workloads.named(name)
+        if wl.cache == "fp8":
+            continue
+        ref = OracleRun(wl, compute_out=False)
+        _CPU.update(wl=wl, ref=ref)
+        items = [(i, g) for i in range(wl.num_seqs) if wl.query_lens[i] > 0 for g in range(wl.num_kv_heads)]
+        items.sort(key=lambda ig: -int(wl.seq_lens[ig[0]]) * int(wl.query_lens[ig[0]]))
+        small = name in ("tiny_decode", "batched_decode")
+        want_runs = 3 if small else 1
+        min_s = spec.get("min_s", 0.0) if name == spec.get("headline") else 0.0
+        runs = []
+        with mp.get_context("fork").Pool(n_proc) as pool:
+            pool.map(_cpu_noop, range(4 * n_proc))        # workers started before timing
+            log(f"cpu baseline: {name}: {len(items)} (sequence, KV head) items on {n_proc} processes")
+            t_all = time.perf_counter()
+            while True:
+                t0 = time.perf_counter()
+                pool.map(_cpu_item, items, chunksize=1)
+                runs.append(time.perf_counter() - t0)
+                elapsed = time.perf_counter() - t_all
+                if (len(runs) >= want_runs and elapsed >= min_s) or elapsed > spec.get("max_s", 60.0):
+                    break
+        best = min(runs)
+        kvb = kv_bytes(wl)
+        entry = {"seconds_best": round(best, 4), "seconds_runs": [round(x, 4) for x in runs],
+                 "query_tokens": wl.num_tokens, "tokens_per_s": round(wl.num_tokens / best, 2),
+                 "kv_bytes": int(kvb), "kv_GBs": round(kvb / best / 1e9, 4), "items": len(items)}
+        pf = prefill_flops(wl)
+        if pf:
+            entry["prefill_GFLOPs"] = round(pf / best / 1e9, 3)
+        res["configs"][name] = entry
+        log(f"cpu baseline: {name}: best pass {best:.3f} s ({entry['kv_GBs']} GB/s of K/V)")
+        _CPU.clear()
+        del ref, wl
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baselines(names, headline, min_s=5.0, max_s=60.0, timeout=900):
+    """Run cpu_child_main in a child process (BLAS threads fixed at 1) and return its JSON, or an error."""
+    import subprocess
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS",
+              "NUMEXPR_NUM_THREADS"):
+        env[k] = "1"
+    spec = {"names": list(names), "headline": headline, "min_s": min_s, "max_s": max_s}
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-child", json.dumps(spec)],
+                           env=env, stdout=subprocess.PIPE, stderr=None, text=True, timeout=timeout)
+    except subprocess.TimeoutExpired:
+        return {"error": f"cpu baseline child timed out after {timeout} s"}
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    if r.returncode != 0 or not lines:
+        return {"error": f"cpu baseline child exited with {r.returncode}"}
+    return json.loads(lines[-1])
 
 
 def allocator_rate(pa, wl, reps=3):
@@ -371,21 +524,29 @@ def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
 def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
     """One workload's whole step (copies, writes, forward) and its decode kernel against the HBM roofline.
 
-    Pools rotate over >= 1 GB of copies as in the headline run; the step time
-    comes from events around untraced steps, per-kernel times from the
-    library's own events on the launch stream."""
+    Pools rotate over >= 1 GB of copies as in the headline run; after the settle
+    phase, the step time comes from events around untraced steps, its spread
+    from events after every step, per-kernel times from the library's own
+    events on the launch stream."""
     log(f"config leg: {name}")
     wl = workloads.named(name)
     kvb = kv_bytes(wl)
     run = DeviceRun(wl, fill="zero", copies=max(2, -(-(1 << 30) // max(kvb, 1))))
+    settle(run, stream)
     run_steps(run, 3, stream)
     ms_step, _ = timed_region(run, steps, stream)
+    clk = clocks(pa, stream)
+    dist = step_distribution(run, steps, stream)
+    hot = step_distribution(run, steps, stream, rotate=False)
     per = traced_region(pa, run, steps, stream)
     out = {"seqs": wl.num_seqs, "query_tokens": wl.num_tokens, "sum_context_tokens": int(wl.seq_lens.sum()),
-           "dtype": wl.dtype, "ms_per_step": round(ms_step, 5),
+           "dtype": wl.dtype, "ms_per_step": round(ms_step, 5), "step_us": dist, "step_us_hot": hot,
            "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
            "kv_GBs_step": round(kvb / (ms_step * 1e-3) / 1e9, 2),
-           "kernel_ms": {k: round(mean(v), 5) for k, v in per.items()}}
+           "step_frac": round(kvb / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "kernel_ms": {k: round(mean(v), 5) for k, v in per.items()},
+           "kernel_us_median": {k: round(float(np.median(v)) * 1e3, 2) for k, v in per.items()},
+           "clocks": clk, "allocator": alloc_accounting(wl, run)}
     dec = next((k for k in ("decode_mfma", "decode_valu", "decode_verify") if k in per), None)
     if dec is not None and decode_rows(wl):
         algo = decode_algorithmic_bytes(wl)
@@ -397,7 +558,8 @@ def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
         ach = algo / (dms * 1e-3) / 1e9
         out["decode_roofline"] = {"kernel": dec, "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                                  "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(dms, 5)}
+                                  "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(dms, 5),
+                                  "traffic": measured_traffic(dec, wl.name)}
         if logical != algo:
             out["decode_roofline"]["logical_bytes_per_launch"] = int(logical)
             out["decode_roofline"]["logical_GBs"] = round(logical / (dms * 1e-3) / 1e9, 2)
@@ -454,7 +616,11 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_baseline_child is not None:    # the GPU-free child of cpu_baselines()
+        cpu_child_main(json.loads(args.cpu_baseline_child))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library is the "
               "single-GPU hot path and this benchmark measures one GPU's share.", file=sys.stderr)
@@ -480,9 +646,14 @@ def main():
     copies = args.copies or max(2, -(-(1 << 30) // max(kvb, 1)))
     log(f"placing it on the GPU ({copies} pool copies)")
     run = DeviceRun(wl, fill="zero", copies=copies)
-    log(f"warm-up {args.warmup} steps, then two timed regions of {args.steps} steps")
+    log(f"settle ({SETTLE_MS:.0f} ms of untimed steps), warm-up {args.warmup} steps, then timed regions of "
+        f"{args.steps} steps")
+    settled = settle(run, stream)
     run_steps(run, args.warmup, stream)
     ms_step, wall_ms = timed_region(run, args.steps, stream)
+    clk = clocks(pa, stream)
+    dist = step_distribution(run, args.steps, stream)
+    hot = step_distribution(run, args.steps, stream, rotate=False)
     per = traced_region(pa, run, args.steps, stream)
     kern_ms = {k: round(mean(v), 5) for k, v in per.items()}
     dominant = max(per, key=lambda k: sum(per[k]))
@@ -520,6 +691,10 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(wall_ms, 5),
+        "step_us": dist,
+        "step_us_hot": hot,
+        "settle_steps": settled,
+        "clocks": clk,
         "kernel_ms": kern_ms,
         "dominant_kernel": dominant,
         "workspace_bytes": int(plan_ws),
@@ -540,6 +715,7 @@ def main():
         res["write_kv"] = {"tokens": wl.num_tokens, "ms": kern_ms["write_kv"],
                            "GBs": round(wb / (kern_ms["write_kv"] * 1e-3) / 1e9, 2)}
     res["allocator"] = allocator_rate(pa, wl)
+    res["allocator"]["accounting"] = alloc_accounting(wl, run)
     del run
     torch.cuda.empty_cache()
 
@@ -551,6 +727,7 @@ def main():
                                     cached=mix.cached_lens[sel], new=mix.query_lens[sel], pool_factor=1.25)
         prun = DeviceRun(pre, fill="zero", copies=2)
         psteps = max(5, args.steps // 5)
+        settle(prun, stream, with_writes=False, min_ms=100)
         run_steps(prun, 3, stream, with_writes=False)
         pper = traced_region(pa, prun, psteps, stream, with_writes=False)
         pms = mean(pper["prefill"])
@@ -573,6 +750,7 @@ def main():
             if route == "prefill":
                 os.environ["PA_VERIFY"] = "prefill"
             try:
+                settle(vrun, stream, with_writes=False, min_ms=100)
                 run_steps(vrun, 3, stream, with_writes=False)
                 vms, _ = timed_region(vrun, vsteps, stream, with_writes=False)
                 legs[route] = (vms, traced_region(pa, vrun, vsteps, stream, with_writes=False))
@@ -603,6 +781,7 @@ def main():
         fwl = workloads.batched_decode_fp8()
         frun = DeviceRun(fwl, fill="zero", copies=max(2, -(-(1 << 30) // kv_bytes(fwl))))
         fsteps = max(10, args.steps // 2)
+        settle(frun, stream, min_ms=100)
         run_steps(frun, 3, stream)
         fms, _ = timed_region(frun, fsteps, stream)
         fper = traced_region(pa, frun, fsteps, stream)
@@ -630,6 +809,7 @@ def main():
                                      cached=mix.cached_lens[sel], new=mix.query_lens[sel], pool_factor=1.25,
                                      cache_dtype="fp8")
         fprun = DeviceRun(fpre, fill="zero", copies=2)
+        settle(fprun, stream, with_writes=False, min_ms=100)
         run_steps(fprun, 3, stream, with_writes=False)
         fpper = traced_region(pa, fprun, max(5, args.steps // 5), stream, with_writes=False)
         fpms = mean(fpper["prefill"])
@@ -644,6 +824,15 @@ def main():
     if not args.no_configs:
         res["configs"] = {n: config_leg(pa, torch, workloads, DeviceRun, n, max(10, args.steps // 2), stream)
                           for n in ("tiny_decode", "long_context_decode", "mixed_superbatch", "shared_prefix_cow")}
+        # Both decode configurations lead: the batch `value` is quoted on, and the longest contexts.
+        lc = res["configs"]["long_context_decode"]
+        res["headline_configs"] = {
+            wl.name: {"kv_GBs_step": res["value"], "step_frac": res["hbm_frac"],
+                      "decode_kernel_frac": res["roofline"]["frac"], "step_us": dist},
+            "long_context_decode": {"kv_GBs_step": lc["kv_GBs_step"], "step_frac": lc["step_frac"],
+                                    "decode_kernel_frac": lc.get("decode_roofline", {}).get("frac"),
+                                    "step_us": lc["step_us"]},
+        }
 
     if not args.no_graph:
         log("graph leg: one step per launch vs replayed from a HIP graph (tiny and batched decode)")
@@ -651,7 +840,27 @@ def main():
                         for n in ("tiny_decode", "batched_decode")]
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl)
+        names = [wl.name] + ([n for n in ("tiny_decode", "long_context_decode", "mixed_superbatch",
+                                          "shared_prefix_cow") if n != wl.name] if not args.no_configs else [])
+        log(f"cpu baseline (oracle, child process): {', '.join(names)}")
+        cb = cpu_baselines(names, wl.name)
+        head = cb.get("configs", {}).get(wl.name)
+        if head is None:
+            res["cpu_baseline"] = {"value": None, "unit": "GB/s", "cores": cb.get("cores"), "kind": "oracle",
+                                   "sample": "not measured", "error": cb.get("error")}
+        else:
+            res["cpu_baseline"] = {
+                "value": head["kv_GBs"], "unit": "GB/s", "cores": cb["cores"], "kind": "oracle",
+                "sample": f"the whole {wl.name} batch ({wl.num_seqs} sequences, {wl.num_tokens} query tokens, "
+                          f"{head['kv_bytes'] / 1e9:.3f} GB of K/V), best of {len(head['seconds_runs'])} passes: "
+                          f"ref_paged_attention (NumPy float64) over {head['items']} (sequence, KV head) items on a "
+                          f"pool of {cb['cores']} processes, one BLAS thread each",
+                "tokens_per_s": head["tokens_per_s"], "seconds_best": head["seconds_best"],
+                "cpu_model": cb.get("cpu_model"), "blas_threads_per_process": cb.get("blas_threads_per_process"),
+            }
+            for n, e in cb["configs"].items():
+                if n in res.get("configs", {}):
+                    res["configs"][n]["cpu_baseline"] = e
     print(json.dumps(res), flush=True)
 
 

@@ -283,6 +283,14 @@ pa_status pa_trace_enable(int32_t on);
  * Errors: PA_ERR_ARG (n NULL, cap < 0, out NULL with cap > 0), PA_ERR_HIP. */
 pa_status pa_trace_read(pa_trace_record* out, int32_t cap, int32_t* n);
 
+/* Measures the shader clock the GPU runs at now: launches a short probe (256
+ * one-wave work-groups, about a millisecond, on `stream`), waits for it, and
+ * sets *mhz to the median over the waves of (shader-clock ticks / real-time
+ * ticks) * 100 MHz.  Meant right after timed work, to record the clock it ran
+ * at.  Allocates nothing.  Errors: PA_ERR_ARG (mhz NULL, or the stream is
+ * being captured), PA_ERR_HIP. */
+pa_status pa_trace_clock(void* stream, float* mhz);
+
 /* ------------------------------------------------------------------------ */
 /* Host block allocator (no GPU calls; one thread at a time per allocator)   */
 /* ------------------------------------------------------------------------ */

@@ -70,6 +70,7 @@ _SIGS = {
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_trace_enable": (_i32, [_i32]),
     "pa_trace_read": (_i32, [ctypes.POINTER(TraceRecord), _i32, _pi32]),
+    "pa_trace_clock": (_i32, [_vp, ctypes.POINTER(ctypes.c_float)]),
     "pa_alloc_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_vp)]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_seq_create": (_i32, [_vp, _pi32]),
@@ -264,6 +265,13 @@ def pa_trace_read(cap=4096):
     n = ctypes.c_int32()
     _check(_load().pa_trace_read(buf, cap, ctypes.byref(n)))
     return [(buf[k].kernel.decode(), float(buf[k].ms)) for k in range(n.value)]
+
+
+def pa_trace_clock(stream=None):
+    """The shader clock (MHz) a short probe kernel runs at now (waits for the stream)."""
+    mhz = ctypes.c_float()
+    _check(_load().pa_trace_clock(_stream(stream), ctypes.byref(mhz)))
+    return float(mhz.value)
 
 
 # -- host allocator -------------------------------------------------------------

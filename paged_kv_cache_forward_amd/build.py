@@ -3,7 +3,9 @@
 Each HIP source is compiled with hipcc for gfx950 only; the host-only
 allocator and status code are compiled with g++; everything is linked into
 ``paged_kv_cache_forward_amd/libpagedattn.so``.  Run ``python -m
-paged_kv_cache_forward_amd.build`` (or call ``build()``).
+paged_kv_cache_forward_amd.build`` (or call ``build()``).  ``--sanitize``
+(``build_sanitized()``) instead builds the host allocator with the tests' trace
+driver under AddressSanitizer and UndefinedBehaviorSanitizer (CPU only).
 """
 
 import os
@@ -62,5 +64,25 @@ def build(verbose=False, extra_hip_flags=()):
     return LIB
 
 
+# The host allocator under AddressSanitizer and UndefinedBehaviorSanitizer: the
+# host-only sources (no GPU code) linked with the trace driver of the tests into
+# one executable, built with g++.
+SANITIZED_DRIVER = os.path.join(OUT_DIR, "alloc_driver_sanitized")
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined", "-std=c++17", "-Wall", "-I" + INCLUDE, "-I" + CSRC]
+
+
+def build_sanitized():
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = [os.path.join(ROOT, "tests", "alloc_driver.cpp")] + [os.path.join(CSRC, s) for s in CXX_SOURCES]
+    tmp = SANITIZED_DRIVER + ".tmp"
+    _run(["g++", *SANITIZE_FLAGS, *srcs, "-o", tmp])
+    os.replace(tmp, SANITIZED_DRIVER)
+    return SANITIZED_DRIVER
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--sanitize" in sys.argv[1:]:
+        print(build_sanitized())
+    else:
+        print(build(verbose=True))

@@ -639,15 +639,24 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
   for (int e = 0; e < DPL; ++e) num[e] = 0.0f;
   for (int p0 = 0; p0 < P; p0 += U) {
     float2 ml[U];
-    float4 x[U][DPL / 4];
+    float x[U][DPL];   // this lane's DPL dims of part p0 + u (2 floats at G = 1, else whole float4s)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (p0 + u < P) {
         const size_t e = (slot0 + p0 + u) * G + h;
         ml[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
-        const float4* src = reinterpret_cast<const float4*>(k.p_acc + e * kD + c * DPL);
+        const float* src = k.p_acc + e * kD + c * DPL;
+        if constexpr (DPL % 4 == 0) {
 #pragma unroll
-        for (int v = 0; v < DPL / 4; ++v) x[u][v] = src[v];
+          for (int v = 0; v < DPL / 4; ++v) {
+            const float4 t = reinterpret_cast<const float4*>(src)[v];
+            x[u][4 * v] = t.x; x[u][4 * v + 1] = t.y; x[u][4 * v + 2] = t.z; x[u][4 * v + 3] = t.w;
+          }
+        } else {
+          static_assert(DPL == 2, "dims per lane");
+          const float2 t = *reinterpret_cast<const float2*>(src);
+          x[u][0] = t.x; x[u][1] = t.y;
+        }
       }
     }
 #pragma unroll
@@ -657,12 +666,7 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
       const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(ml[u].x - Mn);
       den = fmaf(den, sa, ml[u].y * sb);
 #pragma unroll
-      for (int v = 0; v < DPL / 4; ++v) {
-        num[4 * v + 0] = fmaf(num[4 * v + 0], sa, x[u][v].x * sb);
-        num[4 * v + 1] = fmaf(num[4 * v + 1], sa, x[u][v].y * sb);
-        num[4 * v + 2] = fmaf(num[4 * v + 2], sa, x[u][v].z * sb);
-        num[4 * v + 3] = fmaf(num[4 * v + 3], sa, x[u][v].w * sb);
-      }
+      for (int e = 0; e < DPL; ++e) num[e] = fmaf(num[e], sa, x[u][e] * sb);
       Mx = Mn;
     }
   }

@@ -119,26 +119,18 @@ extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens
   return fs.workspace_bytes();
 }
 
-extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
-                                const int32_t* query_start_loc, const int32_t* cached_lens, int32_t num_seqs,
-                                int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
-                                int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  ForwardShape fs;
-  pa_status st = shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward", &fs);
-  if (st != PA_OK) return st;
-  if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !cached_lens)
-    return fail(PA_ERR_ARG, "pa_forward: NULL device pointer");
-  if (block_table_stride <= 0) return fail(PA_ERR_ARG, "pa_forward: block_table_stride %d", block_table_stride);
-  if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "pa_forward: scale is not finite");
-  if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "pa_forward: causal must be 0 or 1");
+namespace pa {
+
+// The body of pa_forward: `workspace` holds at least fs.workspace_bytes()
+// (checked by the caller).
+static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* cached_lens,
+                              int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                              int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                              void* workspace, hipStream_t s) {
+  pa_status st;
   const size_t ws_need = fs.workspace_bytes();
-  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
-    return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", ws_need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  hipStream_t s = (hipStream_t)stream;
   if (check_mode()) {
     if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_forward: PA_CHECK=1 cannot run on a stream being captured");
     st = validate_metadata(block_tables, block_table_stride, seq_lens, query_start_loc, cached_lens, num_seqs,
@@ -204,4 +196,41 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   if (st != PA_OK) return st;
   if (fs.plan.max_parts > 1) st = launch_merge(a, c->dtype, fs.plan, p_acc, p_ml, s);
   return st;
+}
+
+// Host-argument checks of pa_forward.
+static pa_status check_forward_args(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, int32_t block_table_stride,
+                                    const int32_t* seq_lens, const int32_t* query_start_loc,
+                                    const int32_t* cached_lens, float scale, int32_t causal, const char* who) {
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc || !cached_lens)
+    return fail(PA_ERR_ARG, "%s: NULL device pointer", who);
+  if (block_table_stride <= 0) return fail(PA_ERR_ARG, "%s: block_table_stride %d", who, block_table_stride);
+  if (!std::isfinite(scale)) return fail(PA_ERR_ARG, "%s: scale is not finite", who);
+  if (causal != 0 && causal != 1) return fail(PA_ERR_ARG, "%s: causal must be 0 or 1", who);
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t block_table_stride, const int32_t* seq_lens,
+                                const int32_t* query_start_loc, const int32_t* cached_lens, int32_t num_seqs,
+                                int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  ForwardShape fs;
+  pa_status st = shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward", &fs);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
+  st = check_forward_args(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                          cached_lens, scale, causal, "pa_forward");
+  if (st != PA_OK) return st;
+  const size_t ws_need = fs.workspace_bytes();
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
+    return fail(PA_ERR_ARG, "pa_forward: workspace of %zu bytes needed, %zu given", ws_need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                      cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
+                      workspace, (hipStream_t)stream);
 }

@@ -1,4 +1,4 @@
-// Per-kernel timing (tracing) for libpagedattn: host code only.
+// Per-kernel timing (tracing) and a shader-clock probe for libpagedattn.
 //
 // While tracing is on, every device call brackets each kernel it launches with
 // a pair of HIP events recorded on the caller's stream; pa_trace_read waits for
@@ -6,6 +6,7 @@
 // pool and are reused, so steady-state tracing creates none.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -79,9 +80,52 @@ void trace_end(hipStream_t s, int mark, const char* kernel) {
   g_pending.push_back({kernel, start, stop});
 }
 
+// Shader-clock probe: each of kClockWaves one-wave work-groups spins on a
+// dependent FMA chain and reads the shader-clock counter (s_memtime) and the
+// 100 MHz real-time counter (s_memrealtime) before and after; the ratio of the
+// two deltas is the shader clock it ran at.  Results go to a device array the
+// library holds, so the probe allocates nothing.
+constexpr int kClockWaves = 256;
+__device__ unsigned long long g_clock_ticks[2 * kClockWaves];
+
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* ticks, int iters) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  float x = (float)threadIdx.x;
+  for (int i = 0; i < iters; ++i) x = fmaf(x, 1.0000001f, 0.5f);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    ticks[2 * blockIdx.x] = x == 12345.0f ? 0ull : t1 - t0;   // x stays live; never equal in practice
+    ticks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" pa_status pa_trace_clock(void* stream, float* mhz) {
+  if (mhz == nullptr) return fail(PA_ERR_ARG, "pa_trace_clock: mhz is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_trace_clock: the stream is being captured");
+  void* dev = nullptr;
+  hipError_t e = hipGetSymbolAddress(&dev, HIP_SYMBOL(g_clock_ticks));
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_trace_clock: hipGetSymbolAddress: %s", hipGetErrorString(e));
+  unsigned long long host[2 * kClockWaves];
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(kClockWaves), dim3(64), 0, s, (unsigned long long*)dev, 50000);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(host, dev, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_trace_clock: %s", hipGetErrorString(e));
+  std::vector<float> f;
+  for (int w = 0; w < kClockWaves; ++w)
+    if (host[2 * w + 1] > 0) f.push_back(100.0f * (float)host[2 * w] / (float)host[2 * w + 1]);
+  if (f.empty()) return fail(PA_ERR_HIP, "pa_trace_clock: the real-time counter did not advance");
+  std::sort(f.begin(), f.end());
+  *mhz = f[f.size() / 2];
+  return PA_OK;
+}
 
 extern "C" pa_status pa_trace_enable(int32_t on) {
   g_on.store(on != 0);

@@ -95,6 +95,33 @@ def logical_rows(wl):
     return out
 
 
+def oracle_from_rows(rows, q, query_lens, wl):
+    """Oracle output for sequences given by their logical K/V rows (``rows[i] = (K, V)``, stored
+    format, ``[L_i][Hkv][D]``) and query rows ``q`` (``query_lens[i]`` rows each, the last ones of
+    the sequence), with ``wl``'s heads, dtype, cache format, scale and mask.  The rows go into a
+    fresh oracle pool, each sequence in blocks of its own, through the oracle's cache write."""
+    B = wl.block_size
+    lens = np.array([len(k) for k, _ in rows], dtype=np.int64)
+    nb = int(sum(-(-L // B) for L in lens)) + 1
+    if wl.cache == "fp8":
+        kc = oracle.fp8_pool(nb, wl.num_kv_heads, wl.head_dim, B)
+        vc = oracle.fp8_pool(nb, wl.num_kv_heads, wl.head_dim, B)
+    else:
+        kc, vc = (np.zeros((nb, wl.num_kv_heads, B, wl.head_dim), dtype=rows[0][0].dtype) for _ in range(2))
+    tables, b0 = [], 0
+    write = _write_fp8 if wl.cache == "fp8" else oracle.ref_write_kv
+    for K, V in rows:
+        n = -(-len(K) // B)
+        tables.append(list(range(b0, b0 + n)))
+        slots = np.array([(b0 + t // B) * B + t % B for t in range(len(K))], dtype=np.int64)
+        write(kc, vc, K, V, slots, B)
+        b0 += n
+    query_lens = np.asarray(query_lens, dtype=np.int64)
+    qsl = np.concatenate([[0], np.cumsum(query_lens)])
+    return oracle.ref_paged_attention(q, kc, vc, tables, lens, qsl, lens - query_lens, wl.scale, wl.causal,
+                                      B, wl.cache)
+
+
 def compare(got, want, dtype):
     """Max-abs / mean-abs error and the pass/fail of the stated tolerance.
 

@@ -102,3 +102,4 @@ def test_workspace_size_of_the_balanced_decode(monkeypatch):
     monkeypatch.delenv("PA_DECODE_TOTAL_WAVES", raising=False)
     got = pa.lib.pa_forward_workspace_size(2000, 2000, 32, 200, 1, ctypes.byref(desc))
     assert got == 0
+

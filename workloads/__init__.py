@@ -235,6 +235,57 @@ def shared_prefix(name, seed, *, Hq, Hkv, D, dtype, num_seqs, prefix, suffix_max
         ctx_k=ctx_k, ctx_v=ctx_v, trace=trace, notes=info)
 
 
+def unshared(wl, name=None, seed_offset=1000):
+    """The same batch with every sequence holding private copies of its rows: no forks.
+
+    Each batch sequence gets the same logical rows (token by token: the same
+    cached K/V rows, then the same new rows) as in ``wl``, but stored by its
+    own create + append_ctx + append_new, so no block is shared and no
+    copy-on-write happens.  q, the new rows, lengths and batch order are
+    unchanged; the pool gets a fresh free-list order (seeded).  This only
+    rearranges the trace and duplicates input rows.
+    """
+    rows = {}
+    for op in wl.trace:
+        kind = op[0]
+        if kind == "create":
+            rows[op[1]] = []
+        elif kind == "fork":
+            rows[op[1]] = list(rows[op[2]][: op[3]])
+        elif kind == "append_ctx":
+            _, s, n, r0 = op
+            rows[s].extend(("ctx", r) for r in range(r0, r0 + n))
+        elif kind == "append_new":
+            _, s, n, r0 = op
+            rows[s].extend(("new", r) for r in range(r0, r0 + n))
+    ctx_idx, trace, new_ops = [], [], []
+    for i, h in enumerate(wl.batch):
+        lr = rows[h]
+        n = int(wl.query_lens[i])
+        cached = lr[:len(lr) - n]
+        if any(src != "ctx" for src, _ in cached) or any(src != "new" for src, _ in lr[len(lr) - n:]):
+            raise ValueError("a sequence's new rows must come after all of its cached rows")
+        trace.append(("create", i))
+        if cached:
+            trace.append(("append_ctx", i, len(cached), len(ctx_idx)))
+            ctx_idx.extend(r for _, r in cached)
+        if n:
+            new_ops.append(("append_new", i, n, int(lr[len(lr) - n][1])))
+    trace.extend(new_ops)
+    ctx_idx = np.asarray(ctx_idx, dtype=np.int64)
+    blocks = int(sum(math.ceil(int(L) / BLOCK_SIZE) for L in wl.seq_lens))
+    num_blocks = max(wl.num_blocks, blocks + 1)
+    rng = np.random.Generator(np.random.PCG64(wl.seed + seed_offset))
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    return Workload(
+        name=name or wl.name + "_unshared", seed=wl.seed, num_q_heads=wl.num_q_heads,
+        num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim, dtype=wl.dtype, scale=wl.scale,
+        causal=wl.causal, num_blocks=num_blocks, free_order=free_order, batch=list(range(wl.num_seqs)),
+        seq_lens=wl.seq_lens.copy(), cached_lens=wl.cached_lens.copy(), query_lens=wl.query_lens.copy(),
+        q=wl.q, k_new=wl.k_new, v_new=wl.v_new, ctx_k=wl.ctx_k[ctx_idx], ctx_v=wl.ctx_v[ctx_idx],
+        trace=trace, notes=dict(wl.notes, unshared_from=wl.name), cache_dtype=wl.cache_dtype)
+
+
 # -- the five named workloads ------------------------------------------------
 
 def _lengths(seed_offset_rng, lo, hi, n):
@@ -339,6 +390,12 @@ def mini(name):
         L = rng.integers(1500, 6000, size=3)
         return independent(name, 13, Hq=64, Hkv=8, D=128, dtype="bf16", cached=L - 1,
                            new=np.ones(3, dtype=np.int64), pool_extra=3)
+    if name == "decode_mha":
+        # one query head per KV head: the balanced decode and its merge at G = 1
+        rng = np.random.Generator(np.random.PCG64(31))
+        L = np.concatenate([[1, 16, 17, 48], rng.integers(2, 3000, size=4)])
+        return independent(name, 31, Hq=8, Hkv=8, D=128, dtype="bf16", cached=L - 1,
+                           new=np.ones(len(L), dtype=np.int64), pool_extra=4)
     if name == "decode_d64_bf16":
         rng = np.random.Generator(np.random.PCG64(14))
         L = rng.integers(1, 1200, size=5)
@@ -427,7 +484,7 @@ def mini(name):
     raise KeyError(name)
 
 
-MINI = ["decode_f32", "decode_bf16", "decode_gqa8", "decode_d64_bf16", "decode_d128_f32",
+MINI = ["decode_f32", "decode_bf16", "decode_gqa8", "decode_mha", "decode_d64_bf16", "decode_d128_f32",
         "mixed_bf16", "mixed_gqa8", "mixed_mha_d64", "prefill_f32", "noncausal_bf16",
         "shared_bf16", "verify_bf16", "verify_gqa8", "verify_mha", "decode_fp8", "verify_fp8", "fp8_gqa8",
         "fp8_mha_noncausal", "mixed_fp8", "prefill_fp8_gqa8_noncausal"]

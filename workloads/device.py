@@ -27,7 +27,8 @@ class DeviceRun:
     (the way successive layers of a model read different caches).
     """
 
-    def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None, copies=1):
+    def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None, copies=1,
+                 max_seq_len=None):
         import torch
         self.torch = torch
         self.wl = wl
@@ -61,9 +62,12 @@ class DeviceRun:
         self.cached_lens = torch.from_numpy(wl.cached_lens.astype(np.int32)).to(self.dev)
         self.qsl = torch.from_numpy(wl.query_start_loc.astype(np.int32)).to(self.dev)
         self.out = torch.full_like(self.q, float("nan"))
+        # host bound on the lengths passed to pa_forward (may exceed the workload's, e.g. to let
+        # a captured step be replayed after the sequences grow)
+        self.max_seq_len = wl.max_seq_len if max_seq_len is None else max_seq_len
         self.workspace = None
         ws = pa.pa_forward_workspace_size(wl.num_seqs, wl.num_tokens, wl.num_q_heads,
-                                          wl.max_seq_len, wl.max_query_len, self.k_cache)
+                                          self.max_seq_len, wl.max_query_len, self.k_cache)
         if ws:
             self.workspace = pa.new_workspace(ws, self.dev)
         self.fill_context()
@@ -113,7 +117,7 @@ class DeviceRun:
     def forward(self, stream=None):
         wl = self.wl
         pa.pa_forward(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
-                      self.qsl, self.cached_lens, wl.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
+                      self.qsl, self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
                       workspace=self.workspace, stream=stream)
 
     def step(self, stream=None):
