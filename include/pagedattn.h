@@ -245,6 +245,30 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_forward_noalloc — pa_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same arguments and results as pa_forward, without
+ * the workspace.  The split-KV scratch is instead a device array the library
+ * holds, PA_FORWARD_NOALLOC_MAX_SCRATCH bytes on each GPU it runs on, kept
+ * until the process ends; its address is looked up once per device, on the
+ * first call there.  The call allocates nothing.
+ *   - A batch whose pa_forward_workspace_size exceeds the limit returns
+ *     PA_ERR_UNSUPPORTED with nothing enqueued (use pa_forward).
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents (no call needs it cleared).  Calls that may overlap
+ *     on one GPU -- on different streams without ordering between them, or
+ *     from several threads -- race on it and give wrong results; order them.
+ * Other errors as pa_forward.
+ */
+#define PA_FORWARD_NOALLOC_MAX_SCRATCH ((size_t)64 << 20)
+pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t block_table_stride,
+                             const int32_t* seq_lens, const int32_t* query_start_loc,
+                             const int32_t* cached_lens, int32_t num_seqs, int32_t num_tokens,
+                             int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                             const pa_cache_desc* c, float scale, int32_t causal, void* stream);
+
+/*
  * HIP graphs.  pa_write_kv, pa_copy_blocks and pa_forward may be recorded into
  * a HIP graph (stream capture on `stream`), so that a whole serving step
  * replays as one launch ([ART] forward-pass paragraph: the step's kernels are

@@ -68,6 +68,8 @@ _SIGS = {
     "pa_forward_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  _pdesc, ctypes.c_float, _i32, _vp]),
     "pa_trace_enable": (_i32, [_i32]),
     "pa_trace_read": (_i32, [ctypes.POINTER(TraceRecord), _i32, _pi32]),
     "pa_trace_clock": (_i32, [_vp, ctypes.POINTER(ctypes.c_float)]),
@@ -250,6 +252,31 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
                           _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
                           int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
                           ws_ptr, ws_bytes, _stream(stream)))
+
+
+NOALLOC_MAX_SCRATCH = 64 << 20      # PA_FORWARD_NOALLOC_MAX_SCRATCH
+
+
+def pa_forward_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
+                       max_seq_len, max_query_len, scale, causal=True, stream=None):
+    """pa_forward without a workspace: the library's own per-GPU scratch array is used, and nothing
+    is allocated (here or in the library).  Batches needing more than NOALLOC_MAX_SCRATCH bytes of
+    scratch raise PA_ERR_UNSUPPORTED."""
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    T, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != _row_dtype(k_cache):
+        raise ValueError("out must match q, and q the cache dtype (bf16 for an fp8 cache)")
+    S = seq_lens.shape[0]
+    if query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes do not match num_seqs")
+    _check(_load().pa_forward_noalloc(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                      _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+                                      block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                                      _dev(query_start_loc, "query_start_loc", torch.int32),
+                                      _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
+                                      int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
+                                      _stream(stream)))
 
 
 # -- tracing ---------------------------------------------------------------------

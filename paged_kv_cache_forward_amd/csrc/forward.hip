@@ -10,6 +10,7 @@
 // kernel.  Grids are sized from the host scalars max_seq_len / max_query_len,
 // so nothing waits on the device.
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "device.h"
@@ -120,9 +121,51 @@ extern "C" size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens
 }
 
 namespace pa {
+namespace {
 
-// The body of pa_forward: `workspace` holds at least fs.workspace_bytes()
-// (checked by the caller).
+// Scratch of pa_forward_noalloc: one array per GPU, held for the life of the
+// process.  Host code never uses the array's name as an address: on each
+// device it takes the array's device address once, with that device current,
+// and passes that address to the kernels.
+constexpr size_t kNoallocScratchBytes = PA_FORWARD_NOALLOC_MAX_SCRATCH;
+__device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `s`.
+pa_status scratch_for_stream(hipStream_t s, void** out) {
+  hipDevice_t dev = 0;
+  if (s == nullptr) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return fail(PA_ERR_HIP, "pa_forward_noalloc: hipGetDevice failed");
+    dev = cur;
+  } else if (hipStreamGetDevice(s, &dev) != hipSuccess) {
+    return fail(PA_ERR_HIP, "pa_forward_noalloc: hipStreamGetDevice failed");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "pa_forward_noalloc: device %d", (int)dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return fail(PA_ERR_HIP, "pa_forward_noalloc: hipGetDevice failed");
+    if (prev != dev && hipSetDevice(dev) != hipSuccess)
+      return fail(PA_ERR_HIP, "pa_forward_noalloc: hipSetDevice(%d) failed", (int)dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != dev) (void)hipSetDevice(prev);
+    if (e != hipSuccess || p == nullptr)
+      return fail(PA_ERR_HIP, "pa_forward_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
+// The body of pa_forward and pa_forward_noalloc: `workspace` holds at least
+// fs.workspace_bytes() (checked by the callers).
 static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_tables, int32_t block_table_stride,
                               const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* cached_lens,
@@ -198,7 +241,7 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
   return st;
 }
 
-// Host-argument checks of pa_forward.
+// Host-argument checks shared by both entry points.
 static pa_status check_forward_args(void* out, const void* q, const void* k_cache, const void* v_cache,
                                     const int32_t* block_tables, int32_t block_table_stride,
                                     const int32_t* seq_lens, const int32_t* query_start_loc,
@@ -233,4 +276,33 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
                       cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
                       workspace, (hipStream_t)stream);
+}
+
+extern "C" pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t block_table_stride,
+                                        const int32_t* seq_lens, const int32_t* query_start_loc,
+                                        const int32_t* cached_lens, int32_t num_seqs, int32_t num_tokens,
+                                        int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                        const pa_cache_desc* c, float scale, int32_t causal, void* stream) {
+  ForwardShape fs;
+  pa_status st =
+      shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_noalloc", &fs);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
+  st = check_forward_args(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                          cached_lens, scale, causal, "pa_forward_noalloc");
+  if (st != PA_OK) return st;
+  const size_t ws_need = fs.workspace_bytes();
+  if (ws_need > kNoallocScratchBytes)
+    return fail(PA_ERR_UNSUPPORTED, "pa_forward_noalloc: this batch needs %zu bytes of scratch, more than the %zu "
+                "bytes the library holds per GPU (use pa_forward with a workspace)", ws_need, kNoallocScratchBytes);
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (ws_need > 0) {
+    st = scratch_for_stream(s, &ws);
+    if (st != PA_OK) return st;
+  }
+  return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                      cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
+                      ws, s);
 }

@@ -103,3 +103,22 @@ def test_workspace_size_of_the_balanced_decode(monkeypatch):
     got = pa.lib.pa_forward_workspace_size(2000, 2000, 32, 200, 1, ctypes.byref(desc))
     assert got == 0
 
+
+def test_noalloc_host_checks_without_a_gpu():
+    """pa_forward_noalloc checks its host arguments, and refuses a batch whose scratch exceeds the
+    library's per-GPU array, before any HIP call."""
+    import ctypes
+    pa = ensure_library()
+    desc = pa.CacheDesc(100, 8, 128, 16, pa.PA_BF16)
+    st = pa.lib.pa_forward_noalloc(None, None, None, None, None, 1, None, None, None, 4, 4, 32, 100, 1,
+                                   ctypes.byref(desc), 0.1, 1, None)
+    assert st == pa.PA_ERR_ARG and "NULL" in pa.lib.pa_last_error().decode()
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: the call returns before launching
+    S = 65536
+    assert pa.lib.pa_forward_workspace_size(S, S, 32, 8192, 1, ctypes.byref(desc)) > pa.NOALLOC_MAX_SCRATCH
+    st = pa.lib.pa_forward_noalloc(fake, fake, fake, fake, fake, 1, fake, fake, fake, S, S, 32, 8192, 1,
+                                   ctypes.byref(desc), 0.1, 1, None)
+    assert st == pa.PA_ERR_UNSUPPORTED and "scratch" in pa.lib.pa_last_error().decode()
+    # empty batches are a no-op, as for pa_forward
+    assert pa.lib.pa_forward_noalloc(None, None, None, None, None, 1, None, None, None, 0, 0, 32, 0, 0,
+                                     ctypes.byref(desc), 0.1, 1, None) == pa.PA_OK
