@@ -295,6 +295,7 @@ KERNEL_SOURCES = {
     "prefill": ("prefill.hip", "device.h"),
     "write_kv": ("cache_ops.hip", "device.h"),
     "decode_verify": ("decode_verify.hip", "device.h"),
+    "decode_shared": ("decode_shared.hip", "device.h"),
 }
 
 
@@ -521,6 +522,35 @@ def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
             "speedup": round(eager_us / graph_us, 3)}
 
 
+def shared_leg(pa, torch, DeviceRun, wl, steps, stream, uniq):
+    """The same step through pa_forward_shared (shared blocks read once per group of sequences, the
+    allocator's shared-block counts passed in), its decode kernel against HBM on the distinct bytes."""
+    log(f"config leg: {wl.name} through pa_forward_shared")
+    run = DeviceRun(wl, fill="zero", copies=max(2, -(-(1 << 30) // max(kv_bytes(wl), 1))), shared=True)
+    settle(run, stream)
+    run_steps(run, 3, stream)
+    ms_step, _ = timed_region(run, steps, stream)
+    dist = step_distribution(run, steps, stream)
+    per = traced_region(pa, run, steps, stream)
+    out = {"ms_per_step": round(ms_step, 5), "step_us": dist,
+           "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
+           "kv_GBs_step_unique": round(uniq / (ms_step * 1e-3) / 1e9, 2),
+           "kernel_ms": {k: round(mean(v), 5) for k, v in per.items()},
+           "kernel_us_median": {k: round(float(np.median(v)) * 1e3, 2) for k, v in per.items()},
+           "groups_shared_blocks_max": int(run.shared_blocks.max())}
+    if "decode_shared" in per:
+        algo = decode_algorithmic_bytes(wl) - kv_bytes(wl, decode_rows(wl)) + uniq
+        dms = mean(per["decode_shared"])
+        ach = algo / (dms * 1e-3) / 1e9
+        out["decode_roofline"] = {"kernel": "decode_shared", "bound": "hbm", "achieved": round(ach, 2),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                                  "algorithmic_bytes_per_launch": int(algo), "launch_ms": round(dms, 5),
+                                  "traffic": measured_traffic("decode_shared", wl.name)}
+    del run
+    torch.cuda.empty_cache()
+    return out
+
+
 def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
     """One workload's whole step (copies, writes, forward) and its decode kernel against the HBM roofline.
 
@@ -573,6 +603,7 @@ def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
         uniq = unique_kv_bytes(wl, run.tables)
         out["kv_unique_bytes"] = int(uniq)
         out["kv_GBs_step_unique"] = round(uniq / (ms_step * 1e-3) / 1e9, 2)
+        out["shared_decode"] = shared_leg(pa, torch, DeviceRun, wl, steps, stream, uniq)
     if name == "long_context_decode":
         # bulk cache write: the first 262144 context tokens stored again (same slots, same bytes)
         n = min(len(wl.ctx_k), 1 << 18)

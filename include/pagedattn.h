@@ -269,6 +269,47 @@ pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, cons
                              const pa_cache_desc* c, float scale, int32_t causal, void* stream);
 
 /*
+ * pa_forward_shared — pa_forward for a batch whose sequences share prefix
+ * blocks, reading each shared block once for all of them.
+ *
+ * [SLAVA] section "Gemeinsame Nutzung erfordert mehr als Speicherzuweisung"
+ * and [AIU] FAQ (sharing question): requests that fork from one prompt point
+ * at the same physical blocks.  The result is pa_forward's (the same
+ * definition, tolerances and supported shapes); only the work changes.
+ *
+ *   shared_blocks  device int32 [num_seqs]: shared_blocks[i] = the number of
+ *                  leading block-table entries sequence i has in common with
+ *                  sequence i - 1 (shared_blocks[0] is ignored); fewer than
+ *                  the true count is allowed (less is shared), more is not.
+ *                  pa_alloc_shared_blocks computes it on the host.
+ *   other arguments as pa_forward; workspace of at least
+ *   pa_forward_shared_workspace_size(...) bytes.
+ *
+ * A batch of single-token sequences (max_query_len == 1), bf16, head_dim 128,
+ * up to 512 sequences, runs the shared-prefix decode: consecutive batch
+ * entries are taken in fixed groups of P = 32 / (num_q_heads / num_kv_heads)
+ * (4 at eight query heads per KV head, 32 at one); a group's leading blocks
+ * that every member shares (and sees whole) are streamed once, with every
+ * member's query heads as the columns of the matrix-core products; each
+ * sequence's remaining blocks are its own; a log-sum-exp merge combines the
+ * two parts per sequence.  Every other batch runs pa_forward's paths, and
+ * shared_blocks is not read.  Results are deterministic; they are not bit
+ * for bit pa_forward's (another order of accumulation).  Check mode
+ * (PA_CHECK=1) also validates shared_blocks against the tables.
+ * PA_SHARED_TOTAL_WAVES=<1..65536> sets the waves in all (default 1024).
+ * Errors as pa_forward (PA_ERR_ARG also for a NULL shared_blocks).
+ */
+size_t pa_forward_shared_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                        int32_t max_seq_len, int32_t max_query_len, const pa_cache_desc* c);
+pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t block_table_stride,
+                            const int32_t* seq_lens, const int32_t* query_start_loc,
+                            const int32_t* cached_lens, const int32_t* shared_blocks, int32_t num_seqs,
+                            int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                            const pa_cache_desc* c, float scale, int32_t causal, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * HIP graphs.  pa_write_kv, pa_copy_blocks and pa_forward may be recorded into
  * a HIP graph (stream capture on `stream`), so that a whole serving step
  * replays as one launch ([ART] forward-pass paragraph: the step's kernels are
@@ -377,6 +418,15 @@ pa_status pa_seq_free(pa_alloc* a, int32_t seq);
 pa_status pa_seq_block_table(const pa_alloc* a, int32_t seq, int32_t* out, int32_t cap,
                              int32_t* n_blocks, int32_t* len);
 pa_status pa_alloc_stats(const pa_alloc* a, pa_alloc_stats_t* s);
+
+/* Blocks each sequence shares with the one before it in a batch: for
+ * seq_ids[0..n-1] (host int32, batch order), out[i] (host int32) = the number
+ * of leading block-table entries sequence seq_ids[i] has in common with
+ * seq_ids[i-1] (the length of their common prefix of block ids), out[0] = 0.
+ * The argument pa_forward_shared takes ([SLAVA] section "Gemeinsame Nutzung
+ * ...": forked requests point at the same blocks).  Errors: PA_ERR_ARG (NULL
+ * arguments, n < 0, unknown sequence). */
+pa_status pa_alloc_shared_blocks(const pa_alloc* a, const int32_t* seq_ids, int32_t n, int32_t* out);
 
 /* Refcount of one block, or -1 for an id outside the pool. */
 int32_t pa_block_refcount(const pa_alloc* a, int32_t block);

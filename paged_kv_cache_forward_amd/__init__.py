@@ -70,6 +70,9 @@ _SIGS = {
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _pdesc, ctypes.c_float, _i32, _vp]),
+    "pa_forward_shared_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
+    "pa_forward_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                 _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_trace_enable": (_i32, [_i32]),
     "pa_trace_read": (_i32, [ctypes.POINTER(TraceRecord), _i32, _pi32]),
     "pa_trace_clock": (_i32, [_vp, ctypes.POINTER(ctypes.c_float)]),
@@ -82,6 +85,7 @@ _SIGS = {
     "pa_seq_block_table": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
     "pa_alloc_stats": (_i32, [_vp, ctypes.POINTER(AllocStats)]),
     "pa_block_refcount": (_i32, [_vp, _i32]),
+    "pa_alloc_shared_blocks": (_i32, [_vp, _pi32, _i32, _pi32]),
     "pa_alloc_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
     "pa_prefix_register": (_i32, [_vp, _i32, _pi32, _i32]),
     "pa_prefix_lookup": (_i32, [_vp, _pi32, _i32, _pi32, _pi32]),
@@ -254,6 +258,41 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
                           ws_ptr, ws_bytes, _stream(stream)))
 
 
+def pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):
+    desc = cache_desc(k_cache)
+    return int(_load().pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len,
+                                                        max_query_len, ctypes.byref(desc)))
+
+
+def pa_forward_shared(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
+                      shared_blocks, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+    """pa_forward for a batch whose sequences share prefix blocks: ``shared_blocks`` (int32 device
+    tensor [num_seqs]) gives the leading blocks each sequence has in common with the previous one
+    (``BlockAllocator.shared_blocks``)."""
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    T, Hq, D = q.shape
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != _row_dtype(k_cache):
+        raise ValueError("out must match q, and q the cache dtype (bf16 for an fp8 cache)")
+    S = seq_lens.shape[0]
+    if (query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S
+            or shared_blocks.shape != (S,)):
+        raise ValueError("metadata shapes do not match num_seqs")
+    need = pa_forward_shared_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().pa_forward_shared(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                     _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+                                     block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                                     _dev(query_start_loc, "query_start_loc", torch.int32),
+                                     _dev(cached_lens, "cached_lens", torch.int32),
+                                     _dev(shared_blocks, "shared_blocks", torch.int32), S, T, Hq, int(max_seq_len),
+                                     int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
+                                     ws_ptr, ws_bytes, _stream(stream)))
+
+
 NOALLOC_MAX_SCRATCH = 64 << 20      # PA_FORWARD_NOALLOC_MAX_SCRATCH
 
 
@@ -361,6 +400,13 @@ class BlockAllocator:
         st = AllocStats()
         _check(_load().pa_alloc_stats(self._h, ctypes.byref(st)))
         return {name: getattr(st, name) for name, _ in AllocStats._fields_}
+
+    def shared_blocks(self, seq_ids):
+        """Leading blocks each of ``seq_ids`` (batch order) shares with the one before it (int32 array)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+        out = np.zeros(max(len(ids), 1), dtype=np.int32)
+        _check(_load().pa_alloc_shared_blocks(self._h, ids.ctypes.data_as(_pi32), len(ids), out.ctypes.data_as(_pi32)))
+        return out[:len(ids)]
 
     def refcount(self, block):
         return int(_load().pa_block_refcount(self._h, block))

@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
-HIP_SOURCES = ["cache_ops.hip", "decode.hip", "decode_mfma.hip", "decode_verify.hip", "prefill.hip",
-               "forward.hip", "trace.hip"]
+HIP_SOURCES = ["cache_ops.hip", "decode.hip", "decode_mfma.hip", "decode_verify.hip", "decode_shared.hip",
+               "prefill.hip", "forward.hip", "trace.hip"]
 CXX_SOURCES = ["alloc.cpp", "status.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -276,6 +276,26 @@ extern "C" pa_status pa_alloc_stats(const pa_alloc* a, pa_alloc_stats_t* st) {
   return PA_OK;
 }
 
+extern "C" pa_status pa_alloc_shared_blocks(const pa_alloc* a, const int32_t* seq_ids, int32_t n, int32_t* out) {
+  if (a == nullptr || (n > 0 && (seq_ids == nullptr || out == nullptr)))
+    return pa::fail(PA_ERR_ARG, "pa_alloc_shared_blocks: NULL argument");
+  if (n < 0) return pa::fail(PA_ERR_ARG, "pa_alloc_shared_blocks: n %d < 0", n);
+  for (int32_t i = 0; i < n; ++i)
+    if (a->find(seq_ids[i]) == nullptr)
+      return pa::fail(PA_ERR_ARG, "pa_alloc_shared_blocks: unknown sequence %d", seq_ids[i]);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t k = 0;
+    if (i > 0) {
+      const auto& t0 = a->find(seq_ids[i - 1])->table;
+      const auto& t1 = a->find(seq_ids[i])->table;
+      const size_t m = std::min(t0.size(), t1.size());
+      while ((size_t)k < m && t0[k] == t1[k]) ++k;
+    }
+    out[i] = k;
+  }
+  return PA_OK;
+}
+
 extern "C" int32_t pa_block_refcount(const pa_alloc* a, int32_t block) {
   if (a == nullptr || block < 0 || block >= a->num_blocks) return -1;
   return a->refcount[block];

@@ -62,8 +62,6 @@ constexpr int kMaxVerifySeqs = 1024;              // per-sequence tables kept in
 constexpr int kMaxColGroups = 4;
 constexpr int kMaxVerifyTokens = 16;
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 struct VerifyArgs {
   AttnArgs a;
@@ -90,10 +88,6 @@ __device__ __forceinline__ bool verify_item(const VerifyArgs& k, int i, int& q0,
   n = a.qsl[i + 1] - q0;
   len = min(a.seq_lens[i], a.bt_stride * kBlock);
   return n >= k.min_q && n <= k.max_q && q0 >= 0 && q0 + n <= a.num_tokens && len >= n;
-}
-
-__device__ __forceinline__ s16x4_t lds_read_tr(const void* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p);
 }
 
 // Wait until at most OPS * t vector memory operations (t tiles' copies) are outstanding.

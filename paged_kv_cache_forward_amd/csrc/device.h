@@ -11,7 +11,9 @@
 namespace pa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 16;          // tokens per cache block
@@ -183,6 +185,16 @@ __device__ __forceinline__ void wait_tiles(int t) {
   else PA_VM_WAIT(24);
 }
 typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+// ds_read_b64_tr_b16: each lane reads 8 bytes (four bf16) at its own LDS
+// address; within every group of 16 lanes the 4 x 16 block so read (lane l
+// holding row l / 4, columns 4 (l % 4) .. +3) is handed back transposed, lane
+// m of the group receiving column m's four values (rows 0..3).  With the four
+// lanes of a row pointing at one key's 16 dims, lane m gets four keys of dim m:
+// the A operand of a 16x16x16 MFMA whose k dimension is the keys.
+__device__ __forceinline__ s16x4_t lds_read_tr(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(lds_void_t*)p);
+}
 
 // Balanced split of a stream of `total` tiles over Wg ranks: rank r takes
 // tiles [stream_start(r), stream_start(r + 1)).

@@ -9,6 +9,7 @@
 // step) to the multi-token decode kernel; longer ones to the chunked-prefill
 // kernel.  Grids are sized from the host scalars max_seq_len / max_query_len,
 // so nothing waits on the device.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <vector>
@@ -103,6 +104,30 @@ static pa_status validate_metadata(const int32_t* block_tables, int32_t stride, 
       const int32_t b = BT[(size_t)i * stride + j];
       if (b < 0 || b >= num_blocks) return fail(PA_ERR_RANGE, "pa_forward: sequence %d block %lld = %d outside the pool", i, (long long)j, b);
     }
+  }
+  return PA_OK;
+}
+
+// Check mode for pa_forward_shared: sequence i's first shared_blocks[i] table
+// entries equal sequence i - 1's, within both sequences' blocks.
+static pa_status validate_shared(const int32_t* block_tables, int32_t stride, const int32_t* seq_lens,
+                                 const int32_t* shared_blocks, int32_t num_seqs, hipStream_t s) {
+  std::vector<int32_t> L(num_seqs), SB(num_seqs), BT((size_t)num_seqs * stride);
+  bool ok = hipMemcpyAsync(L.data(), seq_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(SB.data(), shared_blocks, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(BT.data(), block_tables, sizeof(int32_t) * BT.size(), hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) return fail(PA_ERR_HIP, "pa_forward_shared: check-mode copy failed");
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (SB[i] < 0) return fail(PA_ERR_RANGE, "pa_forward_shared: shared_blocks[%d] = %d < 0", i, SB[i]);
+    if (i == 0 || SB[i] == 0) continue;
+    const int64_t nb = std::min(((int64_t)L[i] + kBlock - 1) / kBlock, ((int64_t)L[i - 1] + kBlock - 1) / kBlock);
+    if (SB[i] > nb)
+      return fail(PA_ERR_RANGE, "pa_forward_shared: shared_blocks[%d] = %d exceeds the sequences' blocks (%lld)", i,
+                  SB[i], (long long)nb);
+    for (int32_t b = 0; b < SB[i]; ++b)
+      if (BT[(size_t)i * stride + b] != BT[(size_t)(i - 1) * stride + b])
+        return fail(PA_ERR_RANGE, "pa_forward_shared: sequence %d block %d differs from sequence %d's", i, b, i - 1);
   }
   return PA_OK;
 }
@@ -305,4 +330,76 @@ extern "C" pa_status pa_forward_noalloc(void* out, const void* q, const void* k_
   return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
                       cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
                       ws, s);
+}
+
+static SharedPlan shared_plan_of(int32_t num_seqs, int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                 const pa_cache_desc* c) {
+  return make_shared_plan(num_seqs, num_q_heads, c->num_kv_heads, c->head_dim, c->dtype, max_seq_len, max_query_len);
+}
+
+extern "C" size_t pa_forward_shared_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                                   int32_t max_seq_len, int32_t max_query_len,
+                                                   const pa_cache_desc* c) {
+  ForwardShape fs;
+  if (shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_shared_workspace_size",
+               &fs) != PA_OK)
+    return 0;
+  const SharedPlan sp = shared_plan_of(num_seqs, num_q_heads, max_seq_len, max_query_len, c);
+  return sp.on ? sp.workspace_bytes() : fs.workspace_bytes();
+}
+
+extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t block_table_stride,
+                                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                                       const int32_t* cached_lens, const int32_t* shared_blocks, int32_t num_seqs,
+                                       int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                       int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  ForwardShape fs;
+  pa_status st =
+      shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_shared", &fs);
+  if (st != PA_OK) return st;
+  if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
+  st = check_forward_args(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                          cached_lens, scale, causal, "pa_forward_shared");
+  if (st != PA_OK) return st;
+  if (shared_blocks == nullptr) return fail(PA_ERR_ARG, "pa_forward_shared: shared_blocks is NULL");
+  const SharedPlan sp = shared_plan_of(num_seqs, num_q_heads, max_seq_len, max_query_len, c);
+  const size_t ws_need = sp.on ? sp.workspace_bytes() : fs.workspace_bytes();
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
+    return fail(PA_ERR_ARG, "pa_forward_shared: workspace of %zu bytes needed, %zu given", ws_need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (!sp.on)   // not a batch of single-token bf16 head_dim-128 sequences: pa_forward's paths
+    return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                        cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale,
+                        causal, workspace, s);
+  if (check_mode()) {
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_forward_shared: PA_CHECK=1 cannot run on a stream being captured");
+    st = validate_metadata(block_tables, block_table_stride, seq_lens, query_start_loc, cached_lens, num_seqs,
+                           num_tokens, max_seq_len, max_query_len, c->num_blocks, s);
+    if (st != PA_OK) return st;
+    st = validate_shared(block_tables, block_table_stride, seq_lens, shared_blocks, num_seqs, s);
+    if (st != PA_OK) return st;
+  }
+  AttnArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.bt_stride = block_table_stride;
+  a.seq_lens = seq_lens;
+  a.qsl = query_start_loc;
+  a.cached_lens = cached_lens;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = c->num_kv_heads;
+  a.num_blocks = c->num_blocks;
+  a.head_dim = c->head_dim;
+  a.scale_log2 = scale * kLog2e;
+  a.causal = causal;
+  a.prefill_min_q = 2;
+  return launch_decode_shared(a, sp, shared_blocks, workspace, s);
 }

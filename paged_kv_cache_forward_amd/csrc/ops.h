@@ -117,6 +117,27 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
 pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,
                                int32_t* part_table, hipStream_t s);
 
+// Plan for the shared-prefix decode (pa_forward_shared): single-token
+// sequences only, bf16, head_dim 128, at most 512 sequences.  Workspace
+// (offsets 256-byte aligned):
+//   [group prefix F per sequence: int32 [num_seqs]]
+//   [item (first rank, parts): int2 [2 num_seqs]]
+//   [partial acc: fp32 [Hkv][2 num_seqs + waves_per_head][col_groups][8][64][4]]
+//   [partial (max, sum): fp32 [Hkv][2 num_seqs + waves_per_head][16 col_groups][2]]
+struct SharedPlan {
+  bool on;
+  int32_t col_groups;      // 2 or 4 groups of 16 MFMA columns
+  int32_t waves_per_head;
+  int32_t depth;           // K/V tiles in flight per wave (2 or 3)
+  size_t prefix_bytes, info_bytes, acc_bytes, ml_bytes;
+  size_t workspace_bytes() const { return prefix_bytes + info_bytes + acc_bytes + ml_bytes; }
+};
+
+SharedPlan make_shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t dtype, int32_t max_seq_len, int32_t max_query_len);
+pa_status launch_decode_shared(const AttnArgs& a, const SharedPlan& sp, const int32_t* shared_blocks,
+                               void* workspace, hipStream_t s);
+
 // Split-KV plan for the chunked-prefill kernel: the key range of every
 // (sequence, query tile, KV head) work-group is cut into pieces of piece_keys
 // keys (a multiple of 64); work-groups whose range spans more than one piece

@@ -186,3 +186,40 @@ def test_prefix_errors():
     with pytest.raises(pa.PagedAttnError):
         a.prefix_lookup([1, 2, 3], -1)
     assert a.prefix_lookup([]) == (1, 0)
+
+
+def _lcp(a, b):
+    k = 0
+    while k < min(len(a), len(b)) and a[k] == b[k]:
+        k += 1
+    return k
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_blocks_is_the_common_table_prefix(seed):
+    """pa_alloc_shared_blocks = the length of the common prefix of consecutive block tables (computed
+    here from the tables alone), on random fork/append/free traces."""
+    pa = ensure_library()
+    rng = np.random.default_rng(300 + seed)
+    nb = 200
+    a = pa.BlockAllocator(nb, 16, rng.permutation(nb))
+    live = [a.create()]
+    a.append(live[0], int(rng.integers(1, 200)))
+    for _ in range(120):
+        op = int(rng.integers(0, 4))
+        try:
+            if op == 0:
+                p = live[int(rng.integers(0, len(live)))]
+                live.append(a.fork(p, int(rng.integers(0, a.length(p) + 1))))
+            elif op in (1, 2):
+                a.append(live[int(rng.integers(0, len(live)))], int(rng.integers(0, 30)))
+            elif len(live) > 1:
+                a.free_seq(live.pop(int(rng.integers(0, len(live)))))
+        except pa.OutOfBlocks:
+            pass
+        order = [live[k] for k in rng.permutation(len(live))]
+        got = a.shared_blocks(order)
+        tabs = [a.block_table(s) for s in order]
+        assert list(got) == [0] + [_lcp(x, y) for x, y in zip(tabs, tabs[1:])]
+    with pytest.raises(pa.PagedAttnError):
+        a.shared_blocks([10 ** 6])

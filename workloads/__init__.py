@@ -286,6 +286,56 @@ def unshared(wl, name=None, seed_offset=1000):
         trace=trace, notes=dict(wl.notes, unshared_from=wl.name), cache_dtype=wl.cache_dtype)
 
 
+def fork_tree(name, seed, *, Hq, Hkv, D, dtype, root, forks, suffix_max, num_blocks=None, pool_extra=4):
+    """Sequences forked from each other, one decode token each, in batch order.
+
+    ``root`` tokens are stored for sequence 0; sequence i >= 1 forks
+    ``forks[i-1] = (parent, k)`` (parent < i, k <= the parent's length at that
+    point: the parent's first k tokens are shared); then every sequence whose
+    length is a whole number of blocks adds a private suffix of
+    U{0..suffix_max} cached tokens (the others may share their last, partial
+    block, which a cached append must not write into), and finally one new
+    token each (a sequence whose next token lands inside a shared block copies
+    it first).
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    S = len(forks) + 1
+    trace = [("create", 0), ("append_ctx", 0, root, 0)]
+    lens = [root]
+    row = root
+    for i, (p, k) in enumerate(forks, start=1):
+        if not (0 <= p < i and 0 <= k <= lens[p]):
+            raise ValueError(f"fork {i}: parent {p}, {k} tokens")
+        trace.append(("fork", i, p, k))
+        lens.append(k)
+    suffix = rng.integers(0, suffix_max + 1, size=S)
+    suffix[[L % BLOCK_SIZE != 0 for L in lens]] = 0
+    for i in range(S):
+        if suffix[i]:
+            trace.append(("append_ctx", i, int(suffix[i]), row))
+            row += int(suffix[i])
+            lens[i] += int(suffix[i])
+    for i in range(S):
+        trace.append(("append_new", i, 1, i))
+    cached = np.asarray(lens, dtype=np.int64)
+    new = np.ones(S, dtype=np.int64)
+    blocks = int(sum(math.ceil((c + 1) / BLOCK_SIZE) for c in cached))
+    if num_blocks is None:
+        num_blocks = blocks + pool_extra
+    free_order = rng.permutation(num_blocks).astype(np.int32)
+    q = _normal(rng, (S, Hq, D), dtype)
+    k_new = _normal(rng, (S, Hkv, D), dtype)
+    v_new = _normal(rng, (S, Hkv, D), dtype)
+    ctx_k = _normal(rng, (row, Hkv, D), dtype)
+    ctx_v = _normal(rng, (row, Hkv, D), dtype)
+    return Workload(
+        name=name, seed=seed, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, dtype=dtype,
+        scale=1.0 / math.sqrt(D), causal=True, num_blocks=num_blocks, free_order=free_order,
+        batch=list(range(S)), seq_lens=(cached + new).astype(np.int32), cached_lens=cached.astype(np.int32),
+        query_lens=new.astype(np.int32), q=q, k_new=k_new, v_new=v_new, ctx_k=ctx_k, ctx_v=ctx_v,
+        trace=trace, notes={"forks": list(forks), "suffix": suffix.tolist()})
+
+
 # -- the five named workloads ------------------------------------------------
 
 def _lengths(seed_offset_rng, lo, hi, n):

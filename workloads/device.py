@@ -28,7 +28,7 @@ class DeviceRun:
     """
 
     def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None, copies=1,
-                 max_seq_len=None):
+                 max_seq_len=None, shared=False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -65,9 +65,14 @@ class DeviceRun:
         # host bound on the lengths passed to pa_forward (may exceed the workload's, e.g. to let
         # a captured step be replayed after the sequences grow)
         self.max_seq_len = wl.max_seq_len if max_seq_len is None else max_seq_len
+        # shared: attention through pa_forward_shared, with the blocks each batch sequence shares
+        # with the one before it as the host allocator reports them
+        self.shared = shared
+        self.shared_blocks = self.alloc.shared_blocks([self.ids[h] for h in wl.batch])
+        self.shared_blocks_d = torch.from_numpy(self.shared_blocks).to(self.dev)
         self.workspace = None
-        ws = pa.pa_forward_workspace_size(wl.num_seqs, wl.num_tokens, wl.num_q_heads,
-                                          self.max_seq_len, wl.max_query_len, self.k_cache)
+        size = pa.pa_forward_shared_workspace_size if shared else pa.pa_forward_workspace_size
+        ws = size(wl.num_seqs, wl.num_tokens, wl.num_q_heads, self.max_seq_len, wl.max_query_len, self.k_cache)
         if ws:
             self.workspace = pa.new_workspace(ws, self.dev)
         self.fill_context()
@@ -116,6 +121,11 @@ class DeviceRun:
 
     def forward(self, stream=None):
         wl = self.wl
+        if self.shared:
+            pa.pa_forward_shared(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
+                                 self.qsl, self.cached_lens, self.shared_blocks_d, self.max_seq_len,
+                                 wl.max_query_len, wl.scale, wl.causal, workspace=self.workspace, stream=stream)
+            return
         pa.pa_forward(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
                       self.qsl, self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
                       workspace=self.workspace, stream=stream)
