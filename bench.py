@@ -2,9 +2,11 @@
 
 A step is the whole device-side hot path on one synthetic batch whose host
 allocation has already produced its block tables and slot mapping: the
-copy-on-write block copies (pa_copy_blocks, when the step has any), the cache
-write of the step's new tokens (pa_write_kv), then attention (pa_forward:
-decode + split-KV merge, and chunked prefill when the batch has chunks).
+copy-on-write block copies (pa_copy_blocks, when the step has any), then the
+cache write of the step's new tokens and attention in one call
+(pa_write_kv_forward: a decode-only batch fuses the write into the decode;
+otherwise pa_write_kv, then decode + split-KV merge, and chunked prefill when
+the batch has chunks).
 Inputs are resident in HBM before the timed region.  Steps rotate over enough
 identical copies of the K/V pools that no step finds its K/V in the 256 MB
 last-level cache, as successive layers of a model would not.
@@ -137,8 +139,9 @@ def run_steps(run, steps, stream, with_writes=True, rotate=True, events=None):
     for k in range(steps):
         run.use(k if rotate else 0)
         if with_writes:
-            run.step_writes(stream)
-        run.forward(stream)
+            run.step(stream)
+        else:
+            run.forward(stream)
         if events is not None:
             events[k + 1].record(stream)
 
@@ -230,6 +233,18 @@ def timed_region(run, steps, stream, with_writes=True):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     return start.elapsed_time(end) / steps, wall_ms
+
+
+def unfused_step(run, steps, stream):
+    """The same step as two calls (pa_write_kv, then pa_forward): its median per-step time in us,
+    for a single-token batch (where pa_write_kv_forward fuses the write), else None."""
+    if run.wl.max_query_len != 1 or run.shared:
+        return None
+    run.fused = False
+    try:
+        return step_distribution(run, steps, stream)
+    finally:
+        run.fused = True
 
 
 def traced_region(pa, run, steps, stream, with_writes=True):
@@ -479,7 +494,7 @@ def mean(xs):
 
 
 def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
-    """One serving step (pa_copy_blocks + pa_write_kv + pa_forward) per launch vs replayed from a HIP graph.
+    """One serving step (pa_copy_blocks + pa_write_kv_forward) per launch vs replayed from a HIP graph.
 
     Both are timed back to back over `steps` steps on a side stream with HIP
     events; the replay's output bits must equal the eager step's.
@@ -568,6 +583,7 @@ def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
     clk = clocks(pa, stream)
     dist = step_distribution(run, steps, stream)
     hot = step_distribution(run, steps, stream, rotate=False)
+    unfused = unfused_step(run, steps, stream)
     per = traced_region(pa, run, steps, stream)
     out = {"seqs": wl.num_seqs, "query_tokens": wl.num_tokens, "sum_context_tokens": int(wl.seq_lens.sum()),
            "dtype": wl.dtype, "ms_per_step": round(ms_step, 5), "step_us": dist, "step_us_hot": hot,
@@ -577,6 +593,8 @@ def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
            "kernel_ms": {k: round(mean(v), 5) for k, v in per.items()},
            "kernel_us_median": {k: round(float(np.median(v)) * 1e3, 2) for k, v in per.items()},
            "clocks": clk, "allocator": alloc_accounting(wl, run)}
+    if unfused is not None:
+        out["step_us_unfused"] = unfused
     dec = next((k for k in ("decode_mfma", "decode_valu", "decode_verify") if k in per), None)
     if dec is not None and decode_rows(wl):
         algo = decode_algorithmic_bytes(wl)
@@ -685,6 +703,7 @@ def main():
     clk = clocks(pa, stream)
     dist = step_distribution(run, args.steps, stream)
     hot = step_distribution(run, args.steps, stream, rotate=False)
+    unfused = unfused_step(run, args.steps, stream)
     per = traced_region(pa, run, args.steps, stream)
     kern_ms = {k: round(mean(v), 5) for k, v in per.items()}
     dominant = max(per, key=lambda k: sum(per[k]))
@@ -717,13 +736,14 @@ def main():
             "sum_context_tokens": int(wl.seq_lens.sum()),
             "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
             "block_size": wl.block_size, "pool_blocks": wl.num_blocks, "pool_copies": copies,
-            "step": "pa_copy_blocks (if any) + pa_write_kv(new tokens) + pa_forward",
+            "step": "pa_copy_blocks (if any) + pa_write_kv_forward(new tokens, attention)",
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(wl.num_tokens / (ms_step * 1e-3), 1),
         "wall_ms_per_step": round(wall_ms, 5),
         "step_us": dist,
         "step_us_hot": hot,
+        "step_us_unfused": unfused,
         "settle_steps": settled,
         "clocks": clk,
         "kernel_ms": kern_ms,

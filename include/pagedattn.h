@@ -269,6 +269,35 @@ pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, cons
                              const pa_cache_desc* c, float scale, int32_t causal, void* stream);
 
 /*
+ * pa_write_kv_forward — pa_write_kv followed by pa_forward, in one call.
+ *
+ * [SLAVA] lead paragraph and [ART] forward-pass paragraph: a step stores its
+ * new tokens' keys and values in their slots, then attends over the cache.
+ * Arguments: pa_write_kv's (k, v, slot_mapping; num_tokens is the batch's)
+ * and pa_forward's; the results -- the cache bytes and `out` -- are those of
+ * the two calls in that order, bit for bit.
+ *
+ * A batch of single-token sequences (max_query_len == 1) with a bf16 or fp32
+ * cache whose decode runs the balanced split-KV kernel or the vector kernel
+ * (the defaults) takes a fused path: the decode reads each new token's row
+ * from k / v instead of the cache and stores it into the cache itself, so no
+ * separate write launch runs.  Every other batch runs the two calls.
+ * Precondition of the fused path: each sequence's new token goes to its own
+ * position seq_lens[i] - 1 as its block table maps it (slot_mapping[
+ * query_start_loc[i]] = table[i][(L-1)/16]*16 + (L-1)%16), no two sequences
+ * name the same slot, and that block is not read by another sequence of the
+ * batch (the allocator's copy-on-write gives this).  Check mode (PA_CHECK=1)
+ * validates the slots.  Errors as pa_write_kv and pa_forward.
+ */
+pa_status pa_write_kv_forward(const void* k, const void* v, const int64_t* slot_mapping, void* out,
+                              const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+                              int32_t block_table_stride, const int32_t* seq_lens,
+                              const int32_t* query_start_loc, const int32_t* cached_lens, int32_t num_seqs,
+                              int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                              int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_forward_shared — pa_forward for a batch whose sequences share prefix
  * blocks, reading each shared block once for all of them.
  *
@@ -310,7 +339,8 @@ pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const
                             size_t workspace_bytes, void* stream);
 
 /*
- * HIP graphs.  pa_write_kv, pa_copy_blocks and pa_forward may be recorded into
+ * HIP graphs.  pa_write_kv, pa_copy_blocks, pa_forward and pa_write_kv_forward
+ * (and pa_forward_noalloc, pa_forward_shared) may be recorded into
  * a HIP graph (stream capture on `stream`), so that a whole serving step
  * replays as one launch ([ART] forward-pass paragraph: the step's kernels are
  * replayed from a captured graph to save launch overhead).  On the fast path

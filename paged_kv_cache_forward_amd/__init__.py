@@ -8,7 +8,7 @@ into the library raises ImportError (the module itself imports without it so
 that ``paged_kv_cache_forward_amd.build`` can create it).
 
 Functions carry the C names: ``pa_write_kv``, ``pa_copy_blocks``,
-``pa_forward_workspace_size``, ``pa_forward``; ``BlockAllocator`` wraps the
+``pa_forward_workspace_size``, ``pa_forward``, ``pa_write_kv_forward``, ...; ``BlockAllocator`` wraps the
 ``pa_alloc_*`` / ``pa_seq_*`` calls.
 """
 
@@ -68,6 +68,8 @@ _SIGS = {
     "pa_forward_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_write_kv_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
+                                   _i32, _i32, _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _pdesc, ctypes.c_float, _i32, _vp]),
     "pa_forward_shared_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
@@ -256,6 +258,39 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
                           _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
                           int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
                           ws_ptr, ws_bytes, _stream(stream)))
+
+
+def pa_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                        cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+    """``pa_write_kv`` then ``pa_forward`` in one call (a single-token batch fuses the write into the
+    decode); the workspace is ``pa_forward``'s."""
+    torch = _torch()
+    desc = cache_desc(k_cache)
+    T, Hq, D = q.shape
+    if k.dtype != _row_dtype(k_cache) or v.dtype != k.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k, v and the caches must share one dtype (bf16 rows for an fp8 cache)")
+    if v_cache.shape != k_cache.shape or v.shape != k.shape or k.dim() != 3 or k.shape[0] != T:
+        raise ValueError("k/v must be [T][num_kv_heads][head_dim] with q's T")
+    if k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or slot_mapping.shape != (T,):
+        raise ValueError("k/v must be [T][num_kv_heads][head_dim] and slot_mapping [T]")
+    if out.shape != q.shape or out.dtype != q.dtype or q.dtype != _row_dtype(k_cache):
+        raise ValueError("out must match q, and q the cache dtype (bf16 for an fp8 cache)")
+    S = seq_lens.shape[0]
+    if query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S:
+        raise ValueError("metadata shapes do not match num_seqs")
+    need = pa_forward_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
+    if workspace is None and need > 0:
+        workspace = new_workspace(need, q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().pa_write_kv_forward(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int64),
+                                   _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+                                   _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
+                                   block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
+                                   _dev(query_start_loc, "query_start_loc", torch.int32),
+                                   _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
+                                   int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
+                                   ws_ptr, ws_bytes, _stream(stream)))
 
 
 def pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):

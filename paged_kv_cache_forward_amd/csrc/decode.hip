@@ -205,9 +205,13 @@ __device__ __forceinline__ void fold_tile(const uint4 (&kq)[Tile<T, D>::CPL], ui
 // next one's loads are in flight.  The prefetch is issued unconditionally
 // (its index clamped to the last block) so the compiler's wait counts only
 // ever wait for the buffer being folded, never for the one in flight.
+//
+// With `fw` (a fused cache write; [t0, t1) ends at the sequence's last token,
+// the step's new one), the row of token t1 - 1 is taken from the step's new
+// K/V rows instead of the cache and stored into the cache at its place.
 template <typename T, int D, int G>
 __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, int row, int t0, int t1,
-                                             RowState<G, Tile<T, D>::E>& st) {
+                                             RowState<G, Tile<T, D>::E>& st, bool fw = false) {
   using TL = Tile<T, D>;
   constexpr int CPL = TL::CPL;
   const int lane = threadIdx.x;
@@ -226,6 +230,13 @@ __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, in
   const uint8_t* vc = (const uint8_t*)a.v_cache + (size_t)g * tile_bytes;
   const size_t block_stride = (size_t)a.num_kv_heads * tile_bytes;
 
+  uint4 kn = make_uint4(0u, 0u, 0u, 0u), vn = kn;
+  if (fw) {   // the new token's K/V chunk of this lane's column
+    const size_t nrow = ((size_t)row * a.num_kv_heads + g) * TL::ROW_BYTES + col * 16;
+    kn = ld16((const uint8_t*)a.k_new + nrow);
+    vn = ld16((const uint8_t*)a.v_new + nrow);
+  }
+
   const int b_first = t0 / kBlock;
   const int nbt = (t1 - 1) / kBlock - b_first + 1;
   for (int bb = 0; bb < nbt; bb += 64) {
@@ -237,12 +248,32 @@ __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, in
       const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, j) * block_stride;
       load_tile<T, D>(tile_rsrc(kc + off, tile_bytes), tile_rsrc(vc + off, tile_bytes), lane_off, kq, vq);
     };
+    // Fused write: in the block holding token t1 - 1, the lanes of its row
+    // take the new chunks and store them into the cache.
+    auto patch = [&](int j, uint4 (&kq)[CPL], uint4 (&vq)[CPL]) {
+      const int tok0 = tok_base + j * kBlock;
+      if (!fw || tok0 + kBlock < t1) return;   // wave-uniform
+      const int rho = t1 - 1 - tok0;
+      if (rg != rho % TL::R) return;
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        if (u == rho / TL::R) {
+          kq[u] = kn;
+          vq[u] = vn;
+        }
+      }
+      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, j) * block_stride + rho * TL::ROW_BYTES + col * 16;
+      st16((uint8_t*)a.k_cache + (size_t)g * tile_bytes + off, kn);
+      st16((uint8_t*)a.v_cache + (size_t)g * tile_bytes + off, vn);
+    };
     issue(0, ka, va);
     for (int j = 0; j < nb; j += 2) {
       issue(min(j + 1, nb - 1), kb, vb);
+      patch(j, ka, va);
       fold_tile<T, D, G>(ka, va, qv, tok_base + j * kBlock, t1, rg, a.scale_log2, st);
       if (j + 1 >= nb) break;
       issue(min(j + 2, nb - 1), ka, va);
+      patch(j + 1, kb, vb);
       fold_tile<T, D, G>(kb, vb, qv, tok_base + (j + 1) * kBlock, t1, rg, a.scale_log2, st);
     }
   }
@@ -296,7 +327,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeKernelArgs k) {
     if (t0 >= L) return;
     const int t1 = min(t0 + k.part_tokens, L);
     st.init();
-    attend_range<T, D, G>(a, i, g, q0, t0, t1, st);
+    attend_range<T, D, G>(a, i, g, q0, t0, t1, st, a.k_new != nullptr && t1 == L);
     combine_row_groups<T, D, G>(st);
     if (k.max_parts == 1 || L <= k.part_tokens) {
       write_final<T, D, G>(a, q0, g, st);

@@ -402,7 +402,13 @@ __device__ __forceinline__ void finish_segment(const BalancedArgs& k, int i, int
 // query rows of the next segment's sequence are copied to LDS one segment
 // ahead, so a sequence boundary only flushes the fold state: nothing issued
 // there is waited on by the next fold.
-template <int G, int NS>
+//
+// FW (a fused cache write, k_new / v_new set): the step's new token is not in
+// the cache yet.  Its K and V rows are copied to LDS with the query rows, and
+// the lanes of its row in the sequence's last tile take them instead of the
+// cache's; merge_balanced_kernel then stores the rows into the cache.  A
+// separate instantiation, so that the plain kernel's registers are untouched.
+template <int G, int NS, bool FW>
 __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   static_assert(16 % G == 0, "query heads per KV head must divide 16");
   static_assert(NS >= 2 && NS <= 4, "tiles in flight");
@@ -415,6 +421,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   __shared__ int s_raw[2][64];                   // lookup windows: block-table entry (copied), sequence, logical block
   __shared__ int s_sj[2][2][64];
   __shared__ __attribute__((aligned(16))) uint4 s_q[4 * 4 * G];    // next segment's query rows: [ks][r][h]
+  __shared__ __attribute__((aligned(16))) uint4 s_new[2][32];      // fused write: new K row, then V row, by segment parity
   __shared__ __attribute__((aligned(16))) uint4 s_t0[512];         // tile stages: K [ks][lane], V [e][lane]
   __shared__ __attribute__((aligned(16))) uint4 s_t1[512];
   __shared__ __attribute__((aligned(16))) uint4 s_t2[512];
@@ -507,15 +514,25 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   const int j = lane & 15, r = lane >> 4;
   const int hq0 = g * G;
   // Query rows of sequence `seq` -> s_q, lane r * G + h copying dims 32 ks + 8 r .. +8 of head h.
-  auto copy_q = [&](int seq) {
+  // With a fused cache write (k_new set), also the sequence's new K and V rows
+  // -> s_new[par] when this range folds its last tile.
+  constexpr bool fused = FW;
+  auto copy_q = [&](int seq, int par) {
     const int q0 = __builtin_amdgcn_readfirstlane(s_meta[seq] >> 5);
     const u32x4_t rq = rsrc_words((const uint8_t*)a.q + ((size_t)q0 * a.num_q_heads + hq0) * kRowBytes, G * kRowBytes);
     if (lane < 4 * G) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) lds_copy16(rq, s_q + ks * 4 * G, (lane % G) * kRowBytes + (lane / G) * 16 + ks * 64);
     }
+    if (fused && __builtin_amdgcn_readfirstlane(s_cum[seq + 1]) <= tb + n && lane < 32) {
+      // lanes 0..15: the K row's 16-byte chunks; lanes 16..31: the V row's
+      const uint8_t* src = (const uint8_t*)(lane < 16 ? a.k_new : a.v_new) +
+                           ((size_t)q0 * Hkv + g) * kRowBytes + (lane & 15) * 16;
+      lds_copy16_global(src, &s_new[par][0]);
+    }
   };
-  copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]));
+  copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]), 0);
+  int seg = -1;             // this range's segment count - 1: s_new[seg & 1] holds the current one's rows
   int q_tile = -(NS - 1);   // tile whose issue followed the last query copy
 
   const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * kTileBytes;
@@ -561,6 +578,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
           finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
         }
         cur = seq;
+        ++seg;
         const int meta = s_meta[seq];
         cur_end = (s_cum[seq + 1] - s_cum[seq] - 1) * kBlock + (meta & 31) + 1;   // sequence length
         cur_j0 = jt;
@@ -581,7 +599,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
         int nx = seq + 1;                      // next sequence with tiles, if this range reaches it
         while (nx < S && s_cum[nx + 1] == s_cum[nx]) ++nx;
         if (nx < S && s_cum[nx] < tb + n) {
-          copy_q(nx);
+          copy_q(nx, (seg + 1) & 1);
           q_tile = u;
         }
         st.m = kNegBig;
@@ -605,6 +623,23 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
       for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) vq[e] = __builtin_bit_cast(uint4, src[256 + e * 64 + lane]);
+      if (fused && (jt + 1) * kBlock >= cur_end) {
+        // The sequence's last tile: row rho = (L - 1) % 16 is the new token.
+        // Its lanes take the new row (copied to s_new with the query rows)
+        // instead of the cache's; the merge kernel stores it into the cache.
+        const int rho = (cur_end - 1) & (kBlock - 1);
+        const uint4* nr = s_new[seg & 1];
+        if (j == rho) {   // K piece ks: lane (r, j) holds bytes 64 ks + 16 r of row j
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kq[ks] = nr[ks * 4 + r];
+        }
+        if (r == (rho >> 2)) {   // V piece e: lane (r, j) holds bytes 16 j of row 4 r + e
+          const uint4 nv = nr[16 + j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e == (rho & 3)) vq[e] = nv;
+        }
+      }
       fold<G>(kq, vq, qf, jt * kBlock, cur_end, r, a.scale_log2, st);
     }
   }
@@ -628,7 +663,18 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
   const int lane = threadIdx.x, h = lane / LPH, c = lane % LPH;
   const int q0 = a.qsl[i];
   if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
-  if (min(a.seq_lens[i], a.bt_stride * kBlock) <= 0) return;
+  const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
+  if (L <= 0) return;
+  if (a.k_new != nullptr && lane < 32) {
+    // Fused cache write: the new token's K (lanes 0..15) and V (16..31) row
+    // into its slot, position L - 1.  The decode kernel, which ran before,
+    // took this row from k_new / v_new, not from the cache.
+    const int bid = clamp_block(a.block_tables[(size_t)i * a.bt_stride + (L - 1) / kBlock], a.num_blocks);
+    const size_t src = ((size_t)q0 * a.num_kv_heads + g) * kRowBytes + (lane & 15) * 16;
+    const size_t dst = ((size_t)bid * a.num_kv_heads + g) * kTileBytes + ((L - 1) % kBlock) * kRowBytes + (lane & 15) * 16;
+    const uint4 x = ld16((const uint8_t*)(lane < 16 ? a.k_new : a.v_new) + src);
+    st16((uint8_t*)(lane < 16 ? a.k_cache : a.v_cache) + dst, x);
+  }
   const int2 si = k.seqinfo[i];          // written by this call's decode kernel
   const int P = si.y;
   if (P <= 1) return;                    // written out by the decode kernel
@@ -707,9 +753,16 @@ pa_status launch_balanced_g(const BalancedArgs& k, int depth, hipStream_t s) {
   const int W = k.waves_per_head * k.a.num_kv_heads;
   const size_t lds = balanced_lds_bytes(k.a.num_seqs);
   int mark = trace_begin(s);
-  if (depth == 4) hipLaunchKernelGGL((decode_balanced_kernel<G, 4>), dim3(W), dim3(64), lds, s, k);
-  else if (depth == 3) hipLaunchKernelGGL((decode_balanced_kernel<G, 3>), dim3(W), dim3(64), lds, s, k);
-  else hipLaunchKernelGGL((decode_balanced_kernel<G, 2>), dim3(W), dim3(64), lds, s, k);
+  // the fused cache write is its own instantiation: the plain kernel keeps its registers
+  if (k.a.k_new != nullptr) {
+    if (depth == 4) hipLaunchKernelGGL((decode_balanced_kernel<G, 4, true>), dim3(W), dim3(64), lds, s, k);
+    else if (depth == 3) hipLaunchKernelGGL((decode_balanced_kernel<G, 3, true>), dim3(W), dim3(64), lds, s, k);
+    else hipLaunchKernelGGL((decode_balanced_kernel<G, 2, true>), dim3(W), dim3(64), lds, s, k);
+  } else {
+    if (depth == 4) hipLaunchKernelGGL((decode_balanced_kernel<G, 4, false>), dim3(W), dim3(64), lds, s, k);
+    else if (depth == 3) hipLaunchKernelGGL((decode_balanced_kernel<G, 3, false>), dim3(W), dim3(64), lds, s, k);
+    else hipLaunchKernelGGL((decode_balanced_kernel<G, 2, false>), dim3(W), dim3(64), lds, s, k);
+  }
   trace_end(s, mark, "decode_mfma");
   pa_status st = launch_status("pa_forward (decode, balanced)");
   if (st != PA_OK) return st;

@@ -169,6 +169,16 @@ __device__ __forceinline__ void lds_copy16_nt(u32x4_t rsrc, const void* lds, int
                : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// As lds_copy16, from a per-lane global address instead of a buffer
+// resource (no bounds check: `src` must be valid for 16 bytes in every
+// active lane).  For a few scattered rows, where building resources would
+// cost scalar registers.
+__device__ __forceinline__ void lds_copy16_global(const void* src, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(src)
+               : "memory", "m0");
+}
 // As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
 __device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"

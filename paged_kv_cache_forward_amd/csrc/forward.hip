@@ -108,6 +108,37 @@ static pa_status validate_metadata(const int32_t* block_tables, int32_t stride, 
   return PA_OK;
 }
 
+// Check mode for the fused write: every single-token sequence's new token is
+// stored at its position L - 1 as its block table gives it.
+static pa_status validate_fused_slots(const int32_t* block_tables, int32_t stride, const int32_t* seq_lens,
+                                      const int32_t* qsl, const int64_t* slots, int32_t num_seqs,
+                                      int32_t num_tokens, hipStream_t s) {
+  std::vector<int32_t> L(num_seqs), Q(num_seqs + 1), BT((size_t)num_seqs * stride);
+  std::vector<int64_t> SL(num_tokens);
+  bool ok = hipMemcpyAsync(L.data(), seq_lens, sizeof(int32_t) * num_seqs, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(Q.data(), qsl, sizeof(int32_t) * (num_seqs + 1), hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(BT.data(), block_tables, sizeof(int32_t) * BT.size(), hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipMemcpyAsync(SL.data(), slots, sizeof(int64_t) * num_tokens, hipMemcpyDeviceToHost, s) == hipSuccess;
+  ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  if (!ok) return fail(PA_ERR_HIP, "pa_write_kv_forward: check-mode copy failed");
+  std::vector<int64_t> seen;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    if (Q[i] < 0 || Q[i + 1] - Q[i] != 1 || Q[i] >= num_tokens || L[i] < 1 || (L[i] - 1) / kBlock >= stride)
+      continue;                                       // the metadata check reports these
+    const int64_t p = (int64_t)L[i] - 1;
+    const int64_t want = (int64_t)BT[(size_t)i * stride + p / kBlock] * kBlock + p % kBlock;
+    if (SL[Q[i]] != want)
+      return fail(PA_ERR_RANGE, "pa_write_kv_forward: sequence %d's new token has slot %lld, its position %lld is "
+                  "slot %lld", i, (long long)SL[Q[i]], (long long)p, (long long)want);
+    seen.push_back(want);
+  }
+  std::sort(seen.begin(), seen.end());
+  for (size_t j = 1; j < seen.size(); ++j)
+    if (seen[j] == seen[j - 1])
+      return fail(PA_ERR_RANGE, "pa_write_kv_forward: two sequences write slot %lld", (long long)seen[j]);
+  return PA_OK;
+}
+
 // Check mode for pa_forward_shared: sequence i's first shared_blocks[i] table
 // entries equal sequence i - 1's, within both sequences' blocks.
 static pa_status validate_shared(const int32_t* block_tables, int32_t stride, const int32_t* seq_lens,
@@ -196,7 +227,8 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
                               const int32_t* seq_lens, const int32_t* query_start_loc, const int32_t* cached_lens,
                               int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
                               int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
-                              void* workspace, hipStream_t s) {
+                              void* workspace, hipStream_t s, const void* k_new = nullptr,
+                              const void* v_new = nullptr) {
   pa_status st;
   const size_t ws_need = fs.workspace_bytes();
   if (check_mode()) {
@@ -225,6 +257,8 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
   a.scale_log2 = scale * kLog2e;
   a.causal = causal;
   a.prefill_min_q = fs.vplan.on ? fs.vplan.max_q + 1 : 2;
+  a.k_new = k_new;
+  a.v_new = v_new;
 
   int32_t* p_info = nullptr;
   float* p_acc = nullptr;
@@ -402,4 +436,49 @@ extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_c
   a.causal = causal;
   a.prefill_min_q = 2;
   return launch_decode_shared(a, sp, shared_blocks, workspace, s);
+}
+
+extern "C" pa_status pa_write_kv_forward(const void* k, const void* v, const int64_t* slot_mapping, void* out,
+                                         const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                         int32_t block_table_stride, const int32_t* seq_lens,
+                                         const int32_t* query_start_loc, const int32_t* cached_lens,
+                                         int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                         int32_t max_seq_len, int32_t max_query_len, const pa_cache_desc* c,
+                                         float scale, int32_t causal, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  ForwardShape fs;
+  pa_status st =
+      shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_write_kv_forward", &fs);
+  if (st != PA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // A batch of single-token sequences whose decode runs the balanced matrix-core
+  // kernel or the vector kernel takes the fused write; anything else writes first.
+  const bool fuse = num_seqs > 0 && num_tokens > 0 && max_seq_len > 0 && max_query_len == 1 &&
+                    c->dtype != PA_FP8 && !fs.vplan.on && (fs.plan.balanced || !fs.plan.mfma);
+  if (!fuse) {
+    st = pa_write_kv(k, v, k_cache, v_cache, slot_mapping, num_tokens, c, stream);
+    if (st != PA_OK) return st;
+    return pa_forward(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                      cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
+                      workspace, workspace_bytes, stream);
+  }
+  st = check_forward_args(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                          cached_lens, scale, causal, "pa_write_kv_forward");
+  if (st != PA_OK) return st;
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_ARG, "pa_write_kv_forward: NULL device pointer");
+  if ((c->head_dim * elem_bytes(c->dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_kv_forward: head_dim %d", c->head_dim);
+  const size_t ws_need = fs.workspace_bytes();
+  if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
+    return fail(PA_ERR_ARG, "pa_write_kv_forward: workspace of %zu bytes needed, %zu given", ws_need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (check_mode()) {
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_write_kv_forward: PA_CHECK=1 cannot run on a stream being captured");
+    st = validate_fused_slots(block_tables, block_table_stride, seq_lens, query_start_loc, slot_mapping, num_seqs,
+                              num_tokens, s);
+    if (st != PA_OK) return st;
+  }
+  return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                      cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale, causal,
+                      workspace, s, k, v);
 }

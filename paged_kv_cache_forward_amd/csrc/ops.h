@@ -45,6 +45,13 @@ struct AttnArgs {
   float scale_log2;            // softmax scale * log2(e): scores are kept in base-2 units
   int32_t causal;
   int32_t prefill_min_q;       // the prefill kernel takes sequences with at least this many query tokens
+  // Fused cache write (pa_write_kv_forward on a batch of single-token
+  // sequences; both NULL otherwise): the step's new K and V rows,
+  // [num_tokens][num_kv_heads][head_dim].  The decode kernel that folds a
+  // sequence's last block takes the new token's row (position L - 1) from
+  // these and stores it into the cache there.
+  const void* k_new;
+  const void* v_new;
 };
 
 // Plan for the decode path (sequences with one query token).

@@ -1,4 +1,4 @@
-"""HIP-graph capture of a serving step (pa_copy_blocks + pa_write_kv + pa_forward).
+"""HIP-graph capture of a serving step (pa_copy_blocks + pa_write_kv_forward).
 
 "Внутреннее устройство vLLM" (artificials.ru), forward-pass paragraph: the
 step's kernels are captured once and replayed as a graph.  The step is

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Each case replays one seeded workload twice -- on the library (C++ allocator,
-device pools, pa_copy_blocks / pa_write_kv / pa_forward) and on the oracle
+device pools, pa_copy_blocks / pa_write_kv_forward) and on the oracle
 (RefAllocator, NumPy pools, fp64 attention) -- and compares:
   * slots, block tables and copy pairs: bit-exact;
   * the whole K and V pools after the writes: bit-exact (NaN-poisoned

@@ -122,3 +122,27 @@ def test_noalloc_host_checks_without_a_gpu():
     # empty batches are a no-op, as for pa_forward
     assert pa.lib.pa_forward_noalloc(None, None, None, None, None, 1, None, None, None, 0, 0, 32, 0, 0,
                                      ctypes.byref(desc), 0.1, 1, None) == pa.PA_OK
+
+
+def test_write_kv_forward_host_checks_without_a_gpu():
+    """pa_write_kv_forward checks its host arguments (NULL pointers, a short workspace) before any HIP
+    call, and an empty batch is a no-op."""
+    import ctypes
+    pa = ensure_library()
+    desc = pa.CacheDesc(100, 8, 128, 16, pa.PA_BF16)
+    fn = pa.lib.pa_write_kv_forward
+    st = fn(None, None, None, None, None, None, None, None, 1, None, None, None, 4, 4, 32, 100, 1,
+            ctypes.byref(desc), 0.1, 1, None, 0, None)
+    assert st == pa.PA_ERR_ARG and "NULL" in pa.lib.pa_last_error().decode()
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: the call returns before launching
+    S = 64
+    assert pa.lib.pa_forward_workspace_size(S, S, 32, 8192, 1, ctypes.byref(desc)) > 0
+    st = fn(fake, fake, fake, fake, fake, fake, fake, fake, 1, fake, fake, fake, S, S, 32, 8192, 1,
+            ctypes.byref(desc), 0.1, 1, fake, 16, None)
+    assert st == pa.PA_ERR_ARG and "workspace" in pa.lib.pa_last_error().decode()
+    st = fn(None, fake, fake, fake, fake, fake, fake, fake, 1, fake, fake, fake, S, S, 32, 8192, 1,
+            ctypes.byref(desc), 0.1, 1, None, 0, None)
+    assert st == pa.PA_ERR_ARG and "NULL" in pa.lib.pa_last_error().decode()
+    assert fn(None, None, None, None, None, None, None, None, 1, None, None, None, 0, 0, 32, 0, 0,
+              ctypes.byref(desc), 0.1, 1, None, 0, None) == pa.PA_OK
+

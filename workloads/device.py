@@ -5,8 +5,8 @@ library never imports it).  Replays the workload's allocator trace on the
 library's host allocator (``workloads.drive``), puts the pools, queries and
 metadata in device memory (torch tensors), stores the cached tokens with
 ``pa_write_kv``, and then performs the step itself: ``pa_copy_blocks`` for
-copy-on-write pairs, ``pa_write_kv`` for the step's new tokens, ``pa_forward``
-for attention.  Every step of the path runs in the HIP library; this module
+copy-on-write pairs, then ``pa_write_kv_forward`` (the new tokens' K/V and
+attention; or ``pa_write_kv`` and ``pa_forward`` separately).  Every step of the path runs in the HIP library; this module
 only marshals.
 """
 
@@ -28,7 +28,7 @@ class DeviceRun:
     """
 
     def __init__(self, wl, device="cuda:0", fill="nan", free_order=None, table_stride=None, copies=1,
-                 max_seq_len=None, shared=False):
+                 max_seq_len=None, shared=False, fused=True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -68,6 +68,7 @@ class DeviceRun:
         # shared: attention through pa_forward_shared, with the blocks each batch sequence shares
         # with the one before it as the host allocator reports them
         self.shared = shared
+        self.fused = fused
         self.shared_blocks = self.alloc.shared_blocks([self.ids[h] for h in wl.batch])
         self.shared_blocks_d = torch.from_numpy(self.shared_blocks).to(self.dev)
         self.workspace = None
@@ -131,8 +132,20 @@ class DeviceRun:
                       workspace=self.workspace, stream=stream)
 
     def step(self, stream=None):
-        self.step_writes(stream)
-        self.forward(stream)
+        """One engine step.  With ``fused`` (the default) the new tokens' write and attention are one
+        ``pa_write_kv_forward`` call (the library fuses the write into a single-token batch's decode);
+        otherwise ``pa_write_kv`` then ``pa_forward`` (or ``pa_forward_shared``)."""
+        if self.shared or not self.fused:
+            self.step_writes(stream)
+            self.forward(stream)
+            return
+        wl = self.wl
+        if self.pairs_d.shape[0]:
+            pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d, stream=stream)
+        pa.pa_write_kv_forward(self.k_new, self.v_new, self.new_slots_d, self.out, self.q, self.k_cache,
+                               self.v_cache, self.block_tables, self.seq_lens, self.qsl, self.cached_lens,
+                               self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
+                               workspace=self.workspace, stream=stream)
 
     # -- host copies for checking -------------------------------------------
     def host(self, t):
