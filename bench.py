@@ -493,14 +493,20 @@ def mean(xs):
     return float(np.mean(xs)) if xs else None
 
 
-def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
-    """One serving step (pa_copy_blocks + pa_write_kv_forward) per launch vs replayed from a HIP graph.
+GRAPH_LAYERS = 8
 
-    Both are timed back to back over `steps` steps on a side stream with HIP
-    events; the replay's output bits must equal the eager step's.
+
+def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
+    """Serving steps (pa_copy_blocks + pa_write_kv_forward) issued one call at a time vs replayed
+    from HIP graphs.
+
+    Three ways, timed back to back on a side stream with HIP events: eager
+    steps; a graph of one step, replayed; a graph of GRAPH_LAYERS steps over as
+    many pool copies (a model's layers, each with its own cache), replayed --
+    per step.  Every replay's output bits must equal the eager step's.
     """
     wl = workloads.named(name)
-    run = DeviceRun(wl, fill="zero")
+    run = DeviceRun(wl, fill="zero", copies=GRAPH_LAYERS)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -508,16 +514,28 @@ def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
             run.step()
     torch.cuda.synchronize()
     want = run.host(run.out).copy()
+
+    def layers():
+        for k in range(GRAPH_LAYERS):
+            run.use(k)
+            run.step()
+        run.use(0)
+
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         run.step()
+    graph_l = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_l, stream=side):
+        layers()
     torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    if not np.array_equal(run.host(run.out), want):
-        raise RuntimeError(f"graph replay of {name} differs from the eager step")
+    for g in (graph, graph_l):
+        run.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not np.array_equal(run.host(run.out), want):
+            raise RuntimeError(f"graph replay of {name} differs from the eager step")
 
-    def timed(fn):
+    def timed(fn, per=1):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(side):
             for _ in range(5):
@@ -527,14 +545,19 @@ def graph_leg(pa, torch, workloads, DeviceRun, name, steps):
                 fn()
             b.record(side)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / steps
+        return a.elapsed_time(b) * 1e3 / (steps * per)
 
     eager_us = timed(run.step)
     graph_us = timed(graph.replay)
-    del graph, run
+    eager_l_us = timed(layers, GRAPH_LAYERS)
+    graph_l_us = timed(graph_l.replay, GRAPH_LAYERS)
+    del graph, graph_l, run
     torch.cuda.empty_cache()
     return {"workload": name, "eager_us_per_step": round(eager_us, 2), "graph_us_per_step": round(graph_us, 2),
-            "speedup": round(eager_us / graph_us, 3)}
+            "speedup": round(eager_us / graph_us, 3),
+            "layers_per_graph": GRAPH_LAYERS, "eager_layers_us_per_step": round(eager_l_us, 2),
+            "graph_layers_us_per_step": round(graph_l_us, 2),
+            "speedup_layers": round(eager_l_us / graph_l_us, 3)}
 
 
 def shared_leg(pa, torch, DeviceRun, wl, steps, stream, uniq):

@@ -260,10 +260,8 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
                           ws_ptr, ws_bytes, _stream(stream)))
 
 
-def pa_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                        cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
-    """``pa_write_kv`` then ``pa_forward`` in one call (a single-token batch fuses the write into the
-    decode); the workspace is ``pa_forward``'s."""
+def _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                           cached_lens, max_seq_len, max_query_len, scale, causal, workspace, stream):
     torch = _torch()
     desc = cache_desc(k_cache)
     T, Hq, D = q.shape
@@ -283,14 +281,50 @@ def pa_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tabl
         workspace = new_workspace(need, q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_load().pa_write_kv_forward(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int64),
-                                   _dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
-                                   _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
-                                   block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
-                                   _dev(query_start_loc, "query_start_loc", torch.int32),
-                                   _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
-                                   int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
-                                   ws_ptr, ws_bytes, _stream(stream)))
+    # the descriptor and the workspace stay referenced by the tuple for as long as it is used
+    return (_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int64), _dev(out, "out"),
+            _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+            _dev(seq_lens, "seq_lens", torch.int32), _dev(query_start_loc, "query_start_loc", torch.int32),
+            _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len), int(max_query_len),
+            ctypes.byref(desc), float(scale), int(bool(causal)), ws_ptr, ws_bytes, _stream(stream)), (desc, workspace)
+
+
+def pa_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                        cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+    """``pa_write_kv`` then ``pa_forward`` in one call (a single-token batch fuses the write into the
+    decode); the workspace is ``pa_forward``'s."""
+    args, _keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
+                                         query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
+                                         workspace, stream)
+    _check(_load().pa_write_kv_forward(*args))
+
+
+class BoundCall:
+    """One library call with its arguments marshalled once: calling it issues the same call again.
+
+    For a serving loop whose tensors stay where they are between steps (their
+    contents may change): the per-call cost is the C call alone.  The tensors
+    and the stream must outlive the object; it keeps the workspace and the
+    cache descriptor alive itself."""
+
+    def __init__(self, name, args, keep):
+        self._fn = getattr(_load(), name)
+        self._args = args
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+
+
+def bind_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+                          cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None,
+                          stream=None):
+    """``pa_write_kv_forward`` with these arguments as a ``BoundCall`` (nothing is enqueued here)."""
+    args, keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
+                                        query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
+                                        workspace, stream)
+    return BoundCall("pa_write_kv_forward", args, keep)
 
 
 def pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):

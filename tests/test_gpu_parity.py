@@ -83,7 +83,8 @@ def test_long_context_full_size():
 
 
 def _permuted_batch(wl, perm):
-    """Same trace and values, super-batch order permuted."""
+    """Same trace and values, super-batch order permuted: query rows, new K/V rows and the
+    trace's new-row indices move with their sequences."""
     import copy
     w2 = copy.copy(wl)
     qsl = wl.query_start_loc
@@ -92,6 +93,14 @@ def _permuted_batch(wl, perm):
     w2.cached_lens = wl.cached_lens[perm]
     w2.query_lens = wl.query_lens[perm]
     w2.q = np.concatenate([wl.q[qsl[p]:qsl[p + 1]] for p in perm])
+    w2.k_new = np.concatenate([wl.k_new[qsl[p]:qsl[p + 1]] for p in perm])
+    w2.v_new = np.concatenate([wl.v_new[qsl[p]:qsl[p + 1]] for p in perm])
+    start, pos = {}, 0
+    for p in perm:
+        start[int(qsl[p])] = pos
+        pos += int(qsl[p + 1] - qsl[p])
+    w2.trace = [("append_new", op[1], op[2], start[int(op[3])]) if op[0] == "append_new" else op
+                for op in wl.trace]
     return w2, qsl
 
 

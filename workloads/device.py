@@ -69,6 +69,7 @@ class DeviceRun:
         # with the one before it as the host allocator reports them
         self.shared = shared
         self.fused = fused
+        self._bound = {}
         self.shared_blocks = self.alloc.shared_blocks([self.ids[h] for h in wl.batch])
         self.shared_blocks_d = torch.from_numpy(self.shared_blocks).to(self.dev)
         self.workspace = None
@@ -142,10 +143,17 @@ class DeviceRun:
         wl = self.wl
         if self.pairs_d.shape[0]:
             pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d, stream=stream)
-        pa.pa_write_kv_forward(self.k_new, self.v_new, self.new_slots_d, self.out, self.q, self.k_cache,
-                               self.v_cache, self.block_tables, self.seq_lens, self.qsl, self.cached_lens,
-                               self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
-                               workspace=self.workspace, stream=stream)
+        # the call's arguments are marshalled once per (pool copy, stream): the tensors stay in place
+        s = self.torch.cuda.current_stream() if stream is None else stream
+        key = (self.k_cache.data_ptr(), s.cuda_stream)
+        call = self._bound.get(key)
+        if call is None:
+            call = pa.bind_write_kv_forward(self.k_new, self.v_new, self.new_slots_d, self.out, self.q,
+                                            self.k_cache, self.v_cache, self.block_tables, self.seq_lens, self.qsl,
+                                            self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale,
+                                            wl.causal, workspace=self.workspace, stream=s)
+            self._bound[key] = call
+        call()
 
     # -- host copies for checking -------------------------------------------
     def host(self, t):
