@@ -688,6 +688,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--config-leg", default=None, metavar="WORKLOAD",
+                    help="run only this workload's configuration leg (as in `configs`) and print it")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.cpu_baseline_child is not None:    # the GPU-free child of cpu_baselines()
@@ -711,6 +713,11 @@ def main():
     if args.copy_probe:
         copy_probe(pa, torch, stream, args.steps)
         return
+    if args.config_leg:
+        # one configuration's leg alone (for a profiler run): its JSON object on stdout
+        print(json.dumps({args.config_leg: config_leg(pa, torch, workloads, DeviceRun, args.config_leg,
+                                                      args.steps, stream)}), flush=True)
+        return
 
     log(f"generating workload {args.workload}")
     wl = workloads.named(args.workload)
@@ -730,7 +737,7 @@ def main():
     per = traced_region(pa, run, args.steps, stream)
     kern_ms = {k: round(mean(v), 5) for k, v in per.items()}
     dominant = max(per, key=lambda k: sum(per[k]))
-    dec_kernel = "decode_mfma" if "decode_mfma" in per else "decode_valu"
+    dec_kernel = next(k for k in ("decode_mfma", "decode_verify", "decode_valu") if k in per)
 
     algo = decode_algorithmic_bytes(wl)
     dom_ms = mean(per[dec_kernel])

@@ -203,8 +203,9 @@ __device__ __forceinline__ void fold_tile(const uint4 (&kq)[Tile<T, D>::CPL], ui
 //
 // Blocks stream through two register buffers: while one block is folded the
 // next one's loads are in flight.  The prefetch is issued unconditionally
-// (its index clamped to the last block) so the compiler's wait counts only
-// ever wait for the buffer being folded, never for the one in flight.
+// (past the last block it reads an empty range: zeros, no memory traffic) so
+// the compiler's wait counts only ever wait for the buffer being folded,
+// never for the one in flight.
 //
 // With `fw` (a fused cache write; [t0, t1) ends at the sequence's last token,
 // the step's new one), the row of token t1 - 1 is taken from the step's new
@@ -244,9 +245,11 @@ __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, in
     const int my_bid = lane < nb ? clamp_block(bt_row[b_first + bb + lane], a.num_blocks) : 0;
     const int tok_base = (b_first + bb) * kBlock;
     uint4 ka[CPL], va[CPL], kb[CPL], vb[CPL];
+    // A prefetch past the last block (j >= nb) reads an empty range: zeros, no memory traffic.
     auto issue = [&](int j, uint4 (&kq)[CPL], uint4 (&vq)[CPL]) {
-      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, j) * block_stride;
-      load_tile<T, D>(tile_rsrc(kc + off, tile_bytes), tile_rsrc(vc + off, tile_bytes), lane_off, kq, vq);
+      const int bytes = j < nb ? tile_bytes : 0;
+      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, min(j, nb - 1)) * block_stride;
+      load_tile<T, D>(tile_rsrc(kc + off, bytes), tile_rsrc(vc + off, bytes), lane_off, kq, vq);
     };
     // Fused write: in the block holding token t1 - 1, the lanes of its row
     // take the new chunks and store them into the cache.
@@ -268,11 +271,11 @@ __device__ __forceinline__ void attend_range(const AttnArgs& a, int i, int g, in
     };
     issue(0, ka, va);
     for (int j = 0; j < nb; j += 2) {
-      issue(min(j + 1, nb - 1), kb, vb);
+      issue(j + 1, kb, vb);
       patch(j, ka, va);
       fold_tile<T, D, G>(ka, va, qv, tok_base + j * kBlock, t1, rg, a.scale_log2, st);
       if (j + 1 >= nb) break;
-      issue(min(j + 2, nb - 1), ka, va);
+      issue(j + 2, ka, va);
       patch(j + 1, kb, vb);
       fold_tile<T, D, G>(kb, vb, qv, tok_base + (j + 1) * kBlock, t1, rg, a.scale_log2, st);
     }

@@ -222,10 +222,12 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(MfmaDecodeArgs k) 
     const int entry = cb == 0 ? bt_first : bt_row[min(b_first + w + (cb + lane) * NW, a.bt_stride - 1)];
     const int my_bid = lane < nb ? clamp_block(entry, a.num_blocks) : 0;
     uint4 ka[4], va[4], kb[4], vb[4];
+    // A prefetch past the last block (jj >= nb) reads an empty range: zeros, no memory traffic.
     auto issue = [&](int jj, uint4 (&kq)[4], uint4 (&vq)[4]) {
-      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, jj) * block_stride;
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, kTileBytes);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, kTileBytes);
+      const int bytes = jj < nb ? kTileBytes : 0;
+      const size_t off = (size_t)__builtin_amdgcn_readlane(my_bid, min(jj, nb - 1)) * block_stride;
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kc + off, bytes);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vc + off, bytes);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kq[ks] = buf_ld16(rk, koff + ks * 64);
 #pragma unroll
@@ -237,10 +239,10 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(MfmaDecodeArgs k) 
     const int tok_base = (b_first + w + cb * NW) * kBlock;
     issue(0, ka, va);
     for (int jj = 0; jj < nb; jj += 2) {
-      issue(min(jj + 1, nb - 1), kb, vb);
+      issue(jj + 1, kb, vb);
       fold<G>(ka, va, qf, tok_base + jj * NW * kBlock, t1, r, a.scale_log2, st);
       if (jj + 1 >= nb) break;
-      issue(min(jj + 2, nb - 1), ka, va);
+      issue(jj + 2, ka, va);
       fold<G>(kb, vb, qf, tok_base + (jj + 1) * NW * kBlock, t1, r, a.scale_log2, st);
     }
   }
@@ -541,11 +543,16 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   const int koff = j * kRowBytes + r * 16;
   const int voff = 4 * r * kRowBytes + j * 16;
   auto stage = [&](int sI) -> uint4* { return sI == 0 ? s_t0 : sI == 1 ? s_t1 : sI == 2 ? s_t2 : s_t3; };
-  auto issue = [&](int u, int sI) {
+  // A prefetch past the range (uu >= n) still issues its eight copies, so
+  // that every wait counts the same operations, but through an empty range:
+  // they read nothing and write zeros into a stage no later fold reads.
+  auto issue = [&](int uu, int sI) {
+    const int u = min(uu, n - 1);
+    const int bytes = uu < n ? kTileBytes : 0;
     const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[(u >> 6) & 1][u & 63]), a.num_blocks);
     const size_t off = (size_t)bid * block_stride;
-    const u32x4_t rk = rsrc_words(kc + off, kTileBytes);
-    const u32x4_t rv = rsrc_words(vc + off, kTileBytes);
+    const u32x4_t rk = rsrc_words(kc + off, bytes);
+    const u32x4_t rv = rsrc_words(vc + off, bytes);
     uint4* dst = stage(sI);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) lds_copy16_nt(rk, dst + ks * 64, koff + ks * 64);
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
     for (int e = 0; e < 4; ++e) lds_copy16_nt(rv, dst + 256 + e * 64, voff + e * kRowBytes);
   };
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, n - 1), s0);
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0, s0);
 
   WaveState<G> st;
   bf16x8_t qf[4];
@@ -613,7 +620,7 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
       // stay after those reads and ahead of the reads of this tile's stage,
       // which wait for this tile's copies: NS - 1 tiles were issued after them.
       __builtin_amdgcn_sched_barrier(0);
-      issue(min(u + NS - 1, n - 1), (sI + NS - 1) % NS);
+      issue(u + NS - 1, (sI + NS - 1) % NS);
       __builtin_amdgcn_sched_barrier(0);
       wait_tiles(NS - 1);
       cur_jl = jt;

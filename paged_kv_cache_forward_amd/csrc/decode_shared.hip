@@ -235,12 +235,16 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
   // dims] sub-tile of dim block 2p + dsel.
   const int koff = j * kRowBytes + r * 16;
   const int voff = ((lane & 31) >> 1) * kRowBytes + (lane >> 5) * 32 + (lane & 1) * 16;
-  auto issue = [&](int u, int sI) {
+  // A prefetch past the range (uu >= cnt) still issues its eight copies, so
+  // that every wait counts the same operations, but through an empty range:
+  // they read nothing and write zeros into a stage no later fold reads.
+  auto issue = [&](int uu, int sI) {
+    const int u = min(uu, cnt - 1);
     const int w = (u >> 6) & 1, e = u & 63;
     const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[w][e]), a.num_blocks);
     const size_t off = (size_t)bid * block_stride;
     // Rows the item does not see (past a sequence's last token) read as zero.
-    const int bytes = __builtin_amdgcn_readfirstlane(s_sj[w][1][e] >> 16) * kRowBytes;
+    const int bytes = uu < cnt ? __builtin_amdgcn_readfirstlane(s_sj[w][1][e] >> 16) * kRowBytes : 0;
     const u32x4_t rk = rsrc_words(kc + off, bytes);
     const u32x4_t rv = rsrc_words(vc + off, bytes);
     uint4* dst = s_st[sI];
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
     for (int p = 0; p < 4; ++p) lds_copy16_nt(rv, dst + 256 + p * 64, voff + p * 64);
   };
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, cnt - 1), s0);
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0, s0);
 
   // Transposed-read address of this lane inside a [16 keys][16 dims] sub-tile:
   // row group r points at key rows 4r .. 4r+3, four lanes per row, four dims each.
@@ -384,7 +388,7 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
       // stay after those reads and ahead of the reads of this tile's stage,
       // which wait for this tile's copies: NS - 1 tiles were issued after them.
       __builtin_amdgcn_sched_barrier(0);
-      issue(min(u + NS - 1, cnt - 1), (sI + NS - 1) % NS);
+      issue(u + NS - 1, (sI + NS - 1) % NS);
       __builtin_amdgcn_sched_barrier(0);
       wait_copies(NS - 1);
       cur_jl = jt;

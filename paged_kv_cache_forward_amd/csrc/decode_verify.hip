@@ -139,7 +139,20 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   // [piece][lane], V codes [dim][16 keys], then 16 K and 16 V row exponents.
   __shared__ __attribute__((aligned(16))) uint4 s_st[NS][STAGE_U4];
   const int Hkv = a.num_kv_heads;
-  const int g = blockIdx.x % Hkv, rank = blockIdx.x / Hkv;
+  // Work-group -> (KV head, rank).  Work-groups go to the eight XCDs round
+  // robin (blockIdx % 8).  fp8: the row exponents of all KV heads of a block
+  // share one 128-byte line (16 bytes per head), so the KV heads of one rank
+  // -- the same blocks -- are put on one XCD, where the line is fetched once
+  // into that XCD's L2 instead of once per XCD.  Otherwise KV head fastest.
+  int g, rank;
+  if (F8 && k.waves_per_head % 8 == 0) {
+    const int y = blockIdx.x >> 3;
+    g = y % Hkv;
+    rank = (y / Hkv) * 8 + (blockIdx.x & 7);
+  } else {
+    g = blockIdx.x % Hkv;
+    rank = blockIdx.x / Hkv;
+  }
   const int lane = threadIdx.x;
 
   // Tiles of every sequence this kernel handles (0 for the others), then
@@ -252,7 +265,12 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   // [16 keys][16 dims] sub-tile of dim block 2e + dsel.
   const int voff = ((lane & 31) >> 1) * kRowBytes + (lane >> 5) * 32 + (lane & 1) * 16;
   auto stage = [&](int sI) -> uint4* { return s_st[sI]; };
-  auto issue = [&](int u, int sI) {
+  // A prefetch past the range (uu >= cnt) still issues its copies, so that
+  // every wait counts the same operations, but through empty ranges: they
+  // read nothing and write zeros into a stage no later fold reads.
+  auto issue = [&](int uu, int sI) {
+    const int u = min(uu, cnt - 1);
+    const bool real = uu < cnt;
     const int w = (u >> 6) & 1, e = u & 63;
     const int bid = clamp_block(__builtin_amdgcn_readfirstlane(s_raw[w][e]), a.num_blocks);
     const size_t off = (size_t)bid * block_stride;
@@ -262,15 +280,15 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       // (stored transposed): piece p, lane l = dim 64 p + l, all 16 keys.  Then
       // lanes 0..3 copy the 16 K and the 16 V row exponents.  Keys past the
       // sequence are masked where they are used.
-      const u32x4_t rk = rsrc_words(kc + off, TILE);
-      const u32x4_t rv = rsrc_words(vc + off, TILE);
+      const u32x4_t rk = rsrc_words(kc + off, real ? TILE : 0);
+      const u32x4_t rv = rsrc_words(vc + off, real ? TILE : 0);
 #pragma unroll
       for (int p = 0; p < 2; ++p) lds_copy16_nt(rk, dst + p * 64, j * kD + r * 16 + p * 64);
 #pragma unroll
       for (int p = 0; p < 2; ++p) lds_copy16_nt(rv, dst + 128 + p * 64, (p * 64 + lane) * kBlock);
       const size_t xoff = (size_t)bid * Hkv * kBlock;
-      const u32x4_t rkx = rsrc_words(kx + xoff, kBlock);
-      const u32x4_t rvx = rsrc_words(vx + xoff, kBlock);
+      const u32x4_t rkx = rsrc_words(kx + xoff, real ? kBlock : 0);
+      const u32x4_t rvx = rsrc_words(vx + xoff, real ? kBlock : 0);
       if (lane < 4) {
         lds_copy4(rkx, dst + 256, 4 * lane);
         lds_copy4(rvx, (uint8_t*)(dst + 256) + 16, 4 * lane);
@@ -279,7 +297,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       const int seq = __builtin_amdgcn_readfirstlane(s_sj[w][0][e]);
       const int jt = __builtin_amdgcn_readfirstlane(s_sj[w][1][e]);
       // Rows past the sequence read as zero.
-      const int bytes = __builtin_amdgcn_readfirstlane(min(s_len[seq] - jt * kBlock, kBlock) * kRowBytes);
+      const int bytes = real ? __builtin_amdgcn_readfirstlane(min(s_len[seq] - jt * kBlock, kBlock) * kRowBytes) : 0;
       const u32x4_t rk = rsrc_words(kc + off, bytes);
       const u32x4_t rv = rsrc_words(vc + off, bytes);
 #pragma unroll
@@ -289,7 +307,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
     }
   };
 #pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) issue(min(s0, cnt - 1), s0);
+  for (int s0 = 0; s0 < NS - 1; ++s0) issue(s0, s0);
 
   // Transpose-read address of this lane inside a [16 keys][16 dims] sub-tile:
   // row group r points at key rows 4r .. 4r+3, four lanes per row, four dims each.
@@ -397,7 +415,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       // stay after those reads and ahead of the reads of this tile's stage,
       // which wait for this tile's copies: NS - 1 tiles were issued after them.
       __builtin_amdgcn_sched_barrier(0);
-      issue(min(u + NS - 1, cnt - 1), (sI + NS - 1) % NS);
+      issue(u + NS - 1, (sI + NS - 1) % NS);
       __builtin_amdgcn_sched_barrier(0);
       wait_ops<OPS>(NS - 1);
       cur_jl = jt;

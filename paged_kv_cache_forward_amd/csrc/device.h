@@ -138,7 +138,7 @@ __device__ __forceinline__ u32x4_t rsrc_words(const uint8_t* base, int bytes) {
   u32x4_t w;
   w.x = __builtin_amdgcn_readfirstlane((unsigned)p);
   w.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32) & 0xffffu);
-  w.z = (unsigned)bytes;
+  w.z = __builtin_amdgcn_readfirstlane((unsigned)bytes);
   w.w = 0x00020000u;
   return w;
 }
