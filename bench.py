@@ -9,7 +9,8 @@ otherwise pa_write_kv, then decode + split-KV merge, and chunked prefill when
 the batch has chunks).
 Inputs are resident in HBM before the timed region.  Steps rotate over enough
 identical copies of the K/V pools that no step finds its K/V in the 256 MB
-last-level cache, as successive layers of a model would not.
+last-level cache, as successive layers of a model would not (at most 128
+copies: a tiny batch's K/V stays cache-resident, as in a model of 128 layers).
 
 Headline workloads: `batched_decode` (64 decode sequences with contexts
 U[128, 4096], 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks
@@ -146,13 +147,31 @@ def run_steps(run, steps, stream, with_writes=True, rotate=True, events=None):
             events[k + 1].record(stream)
 
 
+MAX_POOL_COPIES = 128
+
+
+def pool_copies(kvb):
+    """Identical K/V pool copies that timed steps rotate over: enough for >= 1 GiB of K/V read
+    across the rotation (so a step's K/V is not served from the 256 MB last-level cache), at
+    least 2 and at most MAX_POOL_COPIES (a model's layer count: a tiny batch then stays
+    cache-resident, as it would in a model)."""
+    return min(MAX_POOL_COPIES, max(2, -(-(1 << 30) // max(int(kvb), 1))))
+
+
 SETTLE_MS = 300.0
 
 
-def settle(run, stream, with_writes=True, min_ms=SETTLE_MS):
-    """Untimed steps until the GPU has been busy for at least `min_ms` (wall clock, synchronised
-    every few steps): the clocks leave their idle state before anything is timed."""
+def _settle_set(ms):
+    global SETTLE_MS
+    SETTLE_MS = float(ms)
+
+
+def settle(run, stream, with_writes=True, min_ms=None):
+    """Untimed steps until the GPU has been busy for at least `min_ms` (default SETTLE_MS; wall
+    clock, synchronised every few steps): the clocks leave their idle state before anything is
+    timed."""
     import torch
+    min_ms = SETTLE_MS if min_ms is None else min_ms
     t0 = time.perf_counter()
     n = 0
     while (time.perf_counter() - t0) * 1e3 < min_ms:
@@ -318,10 +337,11 @@ def measured_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernel is unchanged since.
 
     The summary (profiles/<kernel>-<workload>-hbm_counters.txt) holds key=value
-    lines: FETCH_SIZE and WRITE_SIZE in KiB per dispatch, the scale factors that
-    a plain copy of known size gave for each counter, and the sha256 of the
-    kernel's sources when the counters were taken.  Returns None when there is
-    no summary or the sources have changed.
+    lines: the bytes one dispatch read and wrote past the L2, from the TCC
+    request counters by size (TCC_EA0_RDREQ_32B/64B/128B: requests of 32, 64
+    and 128 bytes; TCC_EA0_WRREQ, TCC_EA0_WRREQ_64B: write requests of 32 and 64
+    bytes), and the sha256 of the kernel's sources when the counters were taken.
+    Returns None when there is no summary or the sources have changed.
     """
     path = os.path.join(PROFILES, f"{kernel}-{workload}-hbm_counters.txt")
     if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
@@ -334,9 +354,7 @@ def measured_traffic(kernel, workload):
                 kv[k.strip()] = v.strip()
     if kv.get("source_sha256") != source_digest(*KERNEL_SOURCES[kernel]):
         return None
-    fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"]) * 1024
-    write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"]) * 1024
-    return int(round(fetch + write))
+    return int(round(float(kv["read_bytes_per_dispatch"]) + float(kv["write_bytes_per_dispatch"])))
 
 
 # -- CPU oracle baseline -----------------------------------------------------------
@@ -564,7 +582,7 @@ def shared_leg(pa, torch, DeviceRun, wl, steps, stream, uniq):
     """The same step through pa_forward_shared (shared blocks read once per group of sequences, the
     allocator's shared-block counts passed in), its decode kernel against HBM on the distinct bytes."""
     log(f"config leg: {wl.name} through pa_forward_shared")
-    run = DeviceRun(wl, fill="zero", copies=max(2, -(-(1 << 30) // max(kv_bytes(wl), 1))), shared=True)
+    run = DeviceRun(wl, fill="zero", copies=pool_copies(kv_bytes(wl)), shared=True)
     settle(run, stream)
     run_steps(run, 3, stream)
     ms_step, _ = timed_region(run, steps, stream)
@@ -592,14 +610,14 @@ def shared_leg(pa, torch, DeviceRun, wl, steps, stream, uniq):
 def config_leg(pa, torch, workloads, DeviceRun, name, steps, stream):
     """One workload's whole step (copies, writes, forward) and its decode kernel against the HBM roofline.
 
-    Pools rotate over >= 1 GB of copies as in the headline run; after the settle
+    Pools rotate over copies as in the headline run (pool_copies); after the settle
     phase, the step time comes from events around untraced steps, its spread
     from events after every step, per-kernel times from the library's own
     events on the launch stream."""
     log(f"config leg: {name}")
     wl = workloads.named(name)
     kvb = kv_bytes(wl)
-    run = DeviceRun(wl, fill="zero", copies=max(2, -(-(1 << 30) // max(kvb, 1))))
+    run = DeviceRun(wl, fill="zero", copies=pool_copies(kvb))
     settle(run, stream)
     run_steps(run, 3, stream)
     ms_step, _ = timed_region(run, steps, stream)
@@ -677,7 +695,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="batched_decode")
-    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: enough for >= 1 GB of K/V)")
+    ap.add_argument("--copies", type=int, default=0, help="pool copies to rotate (0: pool_copies, >= 1 GiB of K/V, at most 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill MFMA-utilisation leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph step-replay leg")
@@ -688,6 +706,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pa_copy_blocks over 1 GiB (read) + 1 GiB (write): the known-size copy "
                          "that calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed busy time before timing (0 for a counter-collection run, where every "
+                         "dispatch is serialised)")
     ap.add_argument("--config-leg", default=None, metavar="WORKLOAD",
                     help="run only this workload's configuration leg (as in `configs`) and print it")
     ap.add_argument("--cpu-baseline-child", default=None, help=argparse.SUPPRESS)
@@ -695,6 +716,7 @@ def main():
     if args.cpu_baseline_child is not None:    # the GPU-free child of cpu_baselines()
         cpu_child_main(json.loads(args.cpu_baseline_child))
         return
+    _settle_set(args.settle_ms)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the library is the "
               "single-GPU hot path and this benchmark measures one GPU's share.", file=sys.stderr)
@@ -722,7 +744,7 @@ def main():
     log(f"generating workload {args.workload}")
     wl = workloads.named(args.workload)
     kvb = kv_bytes(wl)
-    copies = args.copies or max(2, -(-(1 << 30) // max(kvb, 1)))
+    copies = args.copies or pool_copies(kvb)
     log(f"placing it on the GPU ({copies} pool copies)")
     run = DeviceRun(wl, fill="zero", copies=copies)
     log(f"settle ({SETTLE_MS:.0f} ms of untimed steps), warm-up {args.warmup} steps, then timed regions of "
@@ -824,7 +846,7 @@ def main():
     if not args.no_verify:
         log("multi-token decode leg: 64 sequences verifying 2..8 tokens (forward only), two routes")
         vwl = workloads.spec_verify()
-        vrun = DeviceRun(vwl, fill="zero", copies=max(2, -(-(1 << 30) // kv_bytes(vwl))))
+        vrun = DeviceRun(vwl, fill="zero", copies=pool_copies(kv_bytes(vwl)))
         vsteps = max(10, args.steps // 2)
         legs = {}
         for route in ("verify", "prefill"):
@@ -860,7 +882,7 @@ def main():
     if not args.no_fp8:
         log("fp8 leg: the default batched decode on a quantised (E4M3 + row scales) cache, whole steps")
         fwl = workloads.batched_decode_fp8()
-        frun = DeviceRun(fwl, fill="zero", copies=max(2, -(-(1 << 30) // kv_bytes(fwl))))
+        frun = DeviceRun(fwl, fill="zero", copies=pool_copies(kv_bytes(fwl)))
         fsteps = max(10, args.steps // 2)
         settle(frun, stream, min_ms=100)
         run_steps(frun, 3, stream)
