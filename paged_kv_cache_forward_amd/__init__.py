@@ -193,7 +193,7 @@ def _row_dtype(k_cache):
     return torch.bfloat16 if k_cache.dtype == torch.uint8 else k_cache.dtype
 
 
-def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
+def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None, bind=False):
     torch = _torch()
     desc = cache_desc(k_cache)
     if k.dtype != _row_dtype(k_cache) or v.dtype != k.dtype or v_cache.dtype != k_cache.dtype:
@@ -203,19 +203,19 @@ def pa_write_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     T = k.shape[0]
     if k.dim() != 3 or k.shape[1:] != (desc.num_kv_heads, desc.head_dim) or slot_mapping.shape != (T,):
         raise ValueError("k/v must be [T][num_kv_heads][head_dim] and slot_mapping [T]")
-    _check(_load().pa_write_kv(_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    return _call("pa_write_kv", (_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                            _dev(slot_mapping, "slot_mapping", torch.int64), T, ctypes.byref(desc),
-                           _stream(stream)))
+                           _stream(stream)), (desc,), bind)
 
 
-def pa_copy_blocks(k_cache, v_cache, pairs, stream=None):
+def pa_copy_blocks(k_cache, v_cache, pairs, stream=None, bind=False):
     torch = _torch()
     desc = cache_desc(k_cache)
     if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be [n][2]")
-    _check(_load().pa_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    return _call("pa_copy_blocks", (_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                               _dev(pairs, "pairs", torch.int32), pairs.shape[0], ctypes.byref(desc),
-                              _stream(stream)))
+                              _stream(stream)), (desc,), bind)
 
 
 def pa_forward_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):
@@ -231,7 +231,7 @@ def new_workspace(nbytes, device):
 
 
 def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
-               max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+               max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None, bind=False):
     """Attention for the super-batch; ``out`` is written in place.
 
     ``workspace`` is a uint8 device tensor of at least
@@ -251,13 +251,13 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
         workspace = new_workspace(need, q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_load().pa_forward(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+    return _call("pa_forward", (_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
                           _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
                           _dev(seq_lens, "seq_lens", torch.int32),
                           _dev(query_start_loc, "query_start_loc", torch.int32),
                           _dev(cached_lens, "cached_lens", torch.int32), S, T, Hq, int(max_seq_len),
                           int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
-                          ws_ptr, ws_bytes, _stream(stream)))
+                          ws_ptr, ws_bytes, _stream(stream)), (desc, workspace), bind)
 
 
 def _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
@@ -291,17 +291,28 @@ def _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_t
 
 
 def pa_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                        cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+                        cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None,
+                        bind=False):
     """``pa_write_kv`` then ``pa_forward`` in one call (a single-token batch fuses the write into the
     decode); the workspace is ``pa_forward``'s."""
-    args, _keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
-                                         query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
-                                         workspace, stream)
-    _check(_load().pa_write_kv_forward(*args))
+    args, keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
+                                        query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
+                                        workspace, stream)
+    return _call("pa_write_kv_forward", args, keep, bind)
+
+
+def _call(name, args, keep, bind):
+    """Issue library call `name` with marshalled `args`, or with ``bind`` return it as a BoundCall."""
+    if bind:
+        return BoundCall(name, args, keep)
+    _check(getattr(_load(), name)(*args))
+    return None
 
 
 class BoundCall:
     """One library call with its arguments marshalled once: calling it issues the same call again.
+
+    The device calls take ``bind=True`` to return one instead of issuing the call.
 
     For a serving loop whose tensors stay where they are between steps (their
     contents may change): the per-call cost is the C call alone.  The tensors
@@ -317,16 +328,6 @@ class BoundCall:
         _check(self._fn(*self._args))
 
 
-def bind_write_kv_forward(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                          cached_lens, max_seq_len, max_query_len, scale, causal=True, workspace=None,
-                          stream=None):
-    """``pa_write_kv_forward`` with these arguments as a ``BoundCall`` (nothing is enqueued here)."""
-    args, keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
-                                        query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
-                                        workspace, stream)
-    return BoundCall("pa_write_kv_forward", args, keep)
-
-
 def pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, k_cache):
     desc = cache_desc(k_cache)
     return int(_load().pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_len,
@@ -334,7 +335,7 @@ def pa_forward_shared_workspace_size(num_seqs, num_tokens, num_q_heads, max_seq_
 
 
 def pa_forward_shared(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, cached_lens,
-                      shared_blocks, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None):
+                      shared_blocks, max_seq_len, max_query_len, scale, causal=True, workspace=None, stream=None, bind=False):
     """pa_forward for a batch whose sequences share prefix blocks: ``shared_blocks`` (int32 device
     tensor [num_seqs]) gives the leading blocks each sequence has in common with the previous one
     (``BlockAllocator.shared_blocks``)."""
@@ -352,14 +353,14 @@ def pa_forward_shared(out, q, k_cache, v_cache, block_tables, seq_lens, query_st
         workspace = new_workspace(need, q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_load().pa_forward_shared(_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
+    return _call("pa_forward_shared", (_dev(out, "out"), _dev(q, "q"), _dev(k_cache, "k_cache"),
                                      _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32),
                                      block_tables.shape[1], _dev(seq_lens, "seq_lens", torch.int32),
                                      _dev(query_start_loc, "query_start_loc", torch.int32),
                                      _dev(cached_lens, "cached_lens", torch.int32),
                                      _dev(shared_blocks, "shared_blocks", torch.int32), S, T, Hq, int(max_seq_len),
                                      int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
-                                     ws_ptr, ws_bytes, _stream(stream)))
+                                     ws_ptr, ws_bytes, _stream(stream)), (desc, workspace), bind)
 
 
 NOALLOC_MAX_SCRATCH = 64 << 20      # PA_FORWARD_NOALLOC_MAX_SCRATCH

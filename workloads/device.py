@@ -69,7 +69,7 @@ class DeviceRun:
         # with the one before it as the host allocator reports them
         self.shared = shared
         self.fused = fused
-        self._bound = {}
+        self._bound_calls = {}
         self.shared_blocks = self.alloc.shared_blocks([self.ids[h] for h in wl.batch])
         self.shared_blocks_d = torch.from_numpy(self.shared_blocks).to(self.dev)
         self.workspace = None
@@ -115,22 +115,37 @@ class DeviceRun:
             pa.pa_write_kv(k, v, self.k_cache, self.v_cache, s)
             del k, v, s
 
+    # Each library call's arguments are marshalled once per (call, pool copy, stream) and the
+    # bound call re-issued (pa.BoundCall): the tensors stay where they are between steps.
+    def _bound(self, what, stream, make):
+        s = self.torch.cuda.current_stream() if stream is None else stream
+        key = (what, self.k_cache.data_ptr(), s.cuda_stream)
+        call = self._bound_calls.get(key)
+        if call is None:
+            call = make(s)
+            self._bound_calls[key] = call
+        return call
+
     def step_writes(self, stream=None):
         """This step's cache updates: copy-on-write copies, then the new tokens' K/V."""
         if self.pairs_d.shape[0]:
-            pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d, stream=stream)
-        pa.pa_write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache, self.new_slots_d, stream=stream)
+            self._bound("copy", stream, lambda s: pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d,
+                                                                    stream=s, bind=True))()
+        self._bound("write", stream, lambda s: pa.pa_write_kv(self.k_new, self.v_new, self.k_cache, self.v_cache,
+                                                              self.new_slots_d, stream=s, bind=True))()
 
     def forward(self, stream=None):
         wl = self.wl
         if self.shared:
-            pa.pa_forward_shared(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
-                                 self.qsl, self.cached_lens, self.shared_blocks_d, self.max_seq_len,
-                                 wl.max_query_len, wl.scale, wl.causal, workspace=self.workspace, stream=stream)
+            self._bound("shared", stream, lambda s: pa.pa_forward_shared(
+                self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, self.qsl,
+                self.cached_lens, self.shared_blocks_d, self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
+                workspace=self.workspace, stream=s, bind=True))()
             return
-        pa.pa_forward(self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens,
-                      self.qsl, self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale, wl.causal,
-                      workspace=self.workspace, stream=stream)
+        self._bound("forward", stream, lambda s: pa.pa_forward(
+            self.out, self.q, self.k_cache, self.v_cache, self.block_tables, self.seq_lens, self.qsl,
+            self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale, wl.causal, workspace=self.workspace,
+            stream=s, bind=True))()
 
     def step(self, stream=None):
         """One engine step.  With ``fused`` (the default) the new tokens' write and attention are one
@@ -142,18 +157,12 @@ class DeviceRun:
             return
         wl = self.wl
         if self.pairs_d.shape[0]:
-            pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d, stream=stream)
-        # the call's arguments are marshalled once per (pool copy, stream): the tensors stay in place
-        s = self.torch.cuda.current_stream() if stream is None else stream
-        key = (self.k_cache.data_ptr(), s.cuda_stream)
-        call = self._bound.get(key)
-        if call is None:
-            call = pa.bind_write_kv_forward(self.k_new, self.v_new, self.new_slots_d, self.out, self.q,
-                                            self.k_cache, self.v_cache, self.block_tables, self.seq_lens, self.qsl,
-                                            self.cached_lens, self.max_seq_len, wl.max_query_len, wl.scale,
-                                            wl.causal, workspace=self.workspace, stream=s)
-            self._bound[key] = call
-        call()
+            self._bound("copy", stream, lambda s: pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d,
+                                                                    stream=s, bind=True))()
+        self._bound("fused", stream, lambda s: pa.pa_write_kv_forward(
+            self.k_new, self.v_new, self.new_slots_d, self.out, self.q, self.k_cache, self.v_cache,
+            self.block_tables, self.seq_lens, self.qsl, self.cached_lens, self.max_seq_len, wl.max_query_len,
+            wl.scale, wl.causal, workspace=self.workspace, stream=s, bind=True))()
 
     # -- host copies for checking -------------------------------------------
     def host(self, t):
