@@ -339,8 +339,33 @@ pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const
                             size_t workspace_bytes, void* stream);
 
 /*
+ * pa_write_kv_forward_shared — pa_write_kv followed by pa_forward_shared, in
+ * one call.
+ *
+ * As pa_write_kv_forward ([SLAVA] lead paragraph, [ART] forward-pass
+ * paragraph: the step's write comes before its attention) for the batches
+ * pa_forward_shared takes: when its shared-prefix decode runs the batch, the
+ * decode takes each new token's row from k / v and its merge stores the row
+ * into its slot; otherwise the two calls run.  The cache bytes are those of
+ * pa_write_kv, and the output that of pa_forward_shared, bit for bit.
+ * Preconditions: pa_write_kv_forward's (each new token at its sequence's
+ * position L - 1, no slot twice, that block read by no other sequence) and
+ * pa_forward_shared's (shared_blocks not above the true counts); check mode
+ * validates both.  Arguments: pa_write_kv_forward's plus shared_blocks;
+ * workspace as pa_forward_shared.  Errors as pa_write_kv and pa_forward_shared.
+ */
+pa_status pa_write_kv_forward_shared(const void* k, const void* v, const int64_t* slot_mapping, void* out,
+                                     const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     int32_t block_table_stride, const int32_t* seq_lens,
+                                     const int32_t* query_start_loc, const int32_t* cached_lens,
+                                     const int32_t* shared_blocks, int32_t num_seqs, int32_t num_tokens,
+                                     int32_t num_q_heads, int32_t max_seq_len, int32_t max_query_len,
+                                     const pa_cache_desc* c, float scale, int32_t causal, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * HIP graphs.  pa_write_kv, pa_copy_blocks, pa_forward and pa_write_kv_forward
- * (and pa_forward_noalloc, pa_forward_shared) may be recorded into
+ * (and pa_forward_noalloc, pa_forward_shared, pa_write_kv_forward_shared) may be recorded into
  * a HIP graph (stream capture on `stream`), so that a whole serving step
  * replays as one launch ([ART] forward-pass paragraph: the step's kernels are
  * replayed from a captured graph to save launch overhead).  On the fast path

@@ -70,6 +70,8 @@ _SIGS = {
                           _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_write_kv_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32,
                                    _i32, _i32, _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
+    "pa_write_kv_forward_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
+                                          _i32, _i32, _i32, _i32, _pdesc, ctypes.c_float, _i32, _vp, _sz, _vp]),
     "pa_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                   _pdesc, ctypes.c_float, _i32, _vp]),
     "pa_forward_shared_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _pdesc]),
@@ -261,7 +263,7 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
 
 
 def _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
-                           cached_lens, max_seq_len, max_query_len, scale, causal, workspace, stream):
+                           cached_lens, max_seq_len, max_query_len, scale, causal, workspace, stream, need=None):
     torch = _torch()
     desc = cache_desc(k_cache)
     T, Hq, D = q.shape
@@ -276,7 +278,8 @@ def _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_t
     S = seq_lens.shape[0]
     if query_start_loc.shape != (S + 1,) or cached_lens.shape != (S,) or block_tables.shape[0] != S:
         raise ValueError("metadata shapes do not match num_seqs")
-    need = pa_forward_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
+    if need is None:
+        need = pa_forward_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
     if workspace is None and need > 0:
         workspace = new_workspace(need, q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
@@ -361,6 +364,27 @@ def pa_forward_shared(out, q, k_cache, v_cache, block_tables, seq_lens, query_st
                                      _dev(shared_blocks, "shared_blocks", torch.int32), S, T, Hq, int(max_seq_len),
                                      int(max_query_len), ctypes.byref(desc), float(scale), int(bool(causal)),
                                      ws_ptr, ws_bytes, _stream(stream)), (desc, workspace), bind)
+
+
+def pa_write_kv_forward_shared(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
+                               query_start_loc, cached_lens, shared_blocks, max_seq_len, max_query_len, scale,
+                               causal=True, workspace=None, stream=None, bind=False):
+    """``pa_write_kv`` then ``pa_forward_shared`` in one call (fused when the shared-prefix decode
+    takes the batch); the workspace is ``pa_forward_shared``'s."""
+    torch = _torch()
+    S = seq_lens.shape[0]
+    if shared_blocks.shape != (S,):
+        raise ValueError("shared_blocks must be [num_seqs]")
+    T, Hq, _ = q.shape
+    if workspace is None:
+        need = pa_forward_shared_workspace_size(S, T, Hq, max_seq_len, max_query_len, k_cache)
+        workspace = new_workspace(need, q.device) if need > 0 else None
+    args, keep = _write_kv_forward_args(k, v, slot_mapping, out, q, k_cache, v_cache, block_tables, seq_lens,
+                                        query_start_loc, cached_lens, max_seq_len, max_query_len, scale, causal,
+                                        workspace, stream, need=0)
+    # pa_write_kv_forward's arguments with shared_blocks after cached_lens
+    args = args[:12] + (_dev(shared_blocks, "shared_blocks", torch.int32),) + args[12:]
+    return _call("pa_write_kv_forward_shared", args, keep, bind)
 
 
 NOALLOC_MAX_SCRATCH = 64 << 20      # PA_FORWARD_NOALLOC_MAX_SCRATCH

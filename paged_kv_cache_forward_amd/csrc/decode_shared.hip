@@ -66,7 +66,7 @@ struct SharedArgs {
 // Dynamic LDS: tile prefix sums [S + 1], then per sequence its length (0 when
 // it is not a single-token sequence), query row and group prefix F.
 inline size_t shared_dyn_lds(int num_seqs) { return (size_t)(4 * num_seqs + 1) * sizeof(int); }
-inline size_t shared_static_lds(int cg, int ns) { return 3 * 512 + (size_t)cg * 4096 + (size_t)ns * 8192; }
+inline size_t shared_static_lds(int cg, int ns) { return 3 * 512 + 1024 + (size_t)cg * 4096 + (size_t)ns * 8192; }
 
 // Sequences per group: the 16 CG columns hold G query heads of each.
 template <int G, int CG>
@@ -94,7 +94,13 @@ struct ColsState {
   f32x4_t acc[CG][8];   // O^T: column j, dims 16 db + 4 r .. +3
 };
 
-template <int G, int CG, int NS>
+// FW (a fused cache write, k_new / v_new set): the step's new token is not in
+// the cache yet.  A sequence's new K and V rows are copied to LDS with the
+// query rows of its own item, and in that item's last tile the lanes of row
+// (L - 1) mod 16 take them instead of the cache's (K in registers, V patched
+// into the stage before the transpose reads); merge_shared_kernel stores the
+// rows into the cache.  A separate instantiation.
+template <int G, int CG, int NS, bool FW>
 __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
   static_assert(16 % G == 0, "query heads per KV head must divide 16");
   static_assert(NS >= 2 && NS <= 3, "tiles in flight");
@@ -112,6 +118,7 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
   __shared__ int s_sj[2][2][64];
   __shared__ __attribute__((aligned(16))) uint4 s_q[CG * 4 * 64];    // query rows: [cg][ks][lane]
   __shared__ __attribute__((aligned(16))) uint4 s_st[NS][512];       // K [ks][lane], V [db][16 keys][16 dims]
+  __shared__ __attribute__((aligned(16))) uint4 s_new[FW ? 2 : 1][32]; // FW: new K row, then V row, by item parity
   const int Hkv = a.num_kv_heads;
   const int g = blockIdx.x % Hkv, rank = blockIdx.x / Hkv;
   const int lane = threadIdx.x;
@@ -206,9 +213,17 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
   // eight dims of column 16 cg + j (member c / G, head c % G) that k-step ks
   // pairs with this lane's K operand.  The buffer range ends at the item's
   // last query row, so columns past its members read zeros.
-  auto copy_q = [&](int seq_in, int kind_in) {
+  auto copy_q = [&](int seq_in, int kind_in, int par) {
     const int seq = __builtin_amdgcn_readfirstlane(seq_in), kind = __builtin_amdgcn_readfirstlane(kind_in);
     const int q0 = __builtin_amdgcn_readfirstlane(s_q0[seq]);
+    // FW: the sequence's new K / V rows (lanes 0..15 / 16..31) when this range
+    // folds its last tile, which is its own item's (the block holding the new
+    // token is the sequence's own).
+    if (FW && kind == 1 && __builtin_amdgcn_readfirstlane(s_cum[seq + 1]) <= tb + cnt && lane < 32) {
+      const uint8_t* src = (const uint8_t*)(lane < 16 ? a.k_new : a.v_new) +
+                           ((size_t)q0 * Hkv + g) * kRowBytes + (lane & 15) * 16;
+      lds_copy16_global(src, &s_new[FW ? par : 0][0]);
+    }
     const int nq = kind == 0 ? min(P, S - seq) : 1;
     const u32x4_t rq = rsrc_words((const uint8_t*)a.q + (size_t)q0 * a.num_q_heads * kRowBytes,
                                   nq * a.num_q_heads * kRowBytes);
@@ -222,8 +237,9 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
   };
   {
     const int p0 = __builtin_amdgcn_readfirstlane(s_sj[0][1][0]);
-    copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]), (p0 >> 15) & 1);
+    copy_q(__builtin_amdgcn_readfirstlane(s_sj[0][0][0]), (p0 >> 15) & 1, 0);
   }
+  int itm = -1;             // this range's item count - 1: s_new[itm & 1] holds the current item's rows
   int q_tile = -(NS - 1);   // tile whose issue followed the last query copy
 
   const uint8_t* kc = (const uint8_t*)a.k_cache + (size_t)g * kTileBytes;
@@ -322,6 +338,7 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
       if (item != cur) {
         if (cur >= 0) finish();
         cur = item;
+        ++itm;
         cur_seq = seq;
         cur_kind = kind;
         cur_q0 = __builtin_amdgcn_readfirstlane(s_q0[seq]);
@@ -373,7 +390,7 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
           }
         }
         if (nseq != seq || nkind != kind) {
-          copy_q(nseq, nkind);
+          copy_q(nseq, nkind, (itm + 1) & 1);
           q_tile = u;
         }
 #pragma unroll
@@ -398,6 +415,18 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
       uint4 kq[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kq[ks] = __builtin_bit_cast(uint4, src[ks * 64 + lane]);
+      if (FW && cur_kind == 1 && tok0 + kBlock >= key_end) {
+        // The sequence's last tile: row rho = (L - 1) % 16 is the new token.
+        const int rho = (key_end - 1) & (kBlock - 1);
+        const uint4* nr = s_new[FW ? (itm & 1) : 0];
+        if (j == rho) {   // K piece ks: lane (r, j) holds bytes 64 ks + 16 r of row j
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kq[ks] = nr[ks * 4 + r];
+        }
+        if (lane < 16)    // V: chunk `lane` (dims 8 lane .. +8) into row rho of sub-tile lane / 2
+          s_st[sI][256 + (lane >> 1) * 32 + rho * 2 + (lane & 1)] = nr[16 + lane];
+        asm volatile("" ::: "memory");   // the transpose reads below come after the patch
+      }
 
       // Scores of the active column groups, base-2 units, masked past the item's keys.
       float sc[CG][4];
@@ -490,6 +519,15 @@ __global__ __launch_bounds__(256) void merge_shared_kernel(SharedArgs k) {
   if (t >= G * 32) return;
   int q0, len;
   if (!shared_item(a, i, q0, len)) return;
+  if (a.k_new != nullptr && t < 32) {
+    // Fused cache write: the new token's K (threads 0..15) and V (16..31) row
+    // into its slot, position len - 1; the decode kernel took it from k_new / v_new.
+    const int bid = clamp_block(a.block_tables[(size_t)i * a.bt_stride + (len - 1) / kBlock], a.num_blocks);
+    const size_t src = ((size_t)q0 * Hkv + g) * kRowBytes + (t & 15) * 16;
+    const size_t dst = ((size_t)bid * Hkv + g) * kTileBytes + ((len - 1) % kBlock) * kRowBytes + (t & 15) * 16;
+    const uint4 x = ld16((const uint8_t*)(t < 16 ? a.k_new : a.v_new) + src);
+    st16((uint8_t*)(t < 16 ? a.k_cache : a.v_cache) + dst, x);
+  }
   const int F = k.seq_prefix[i];                  // written by this call's decode kernel
   const int T = (len + kBlock - 1) / kBlock;
   const int h = t / 32, db = (t / 4) % 8, r = t % 4;
@@ -552,7 +590,10 @@ template <int G, int CG, int NS>
 pa_status launch_shared_gn(const SharedArgs& k, hipStream_t s) {
   const int W = k.waves_per_head * k.a.num_kv_heads;
   int mark = trace_begin(s);
-  hipLaunchKernelGGL((decode_shared_kernel<G, CG, NS>), dim3(W), dim3(64), shared_dyn_lds(k.a.num_seqs), s, k);
+  if (k.a.k_new != nullptr)
+    hipLaunchKernelGGL((decode_shared_kernel<G, CG, NS, true>), dim3(W), dim3(64), shared_dyn_lds(k.a.num_seqs), s, k);
+  else
+    hipLaunchKernelGGL((decode_shared_kernel<G, CG, NS, false>), dim3(W), dim3(64), shared_dyn_lds(k.a.num_seqs), s, k);
   trace_end(s, mark, "decode_shared");
   pa_status st = launch_status("pa_forward_shared (decode)");
   if (st != PA_OK) return st;

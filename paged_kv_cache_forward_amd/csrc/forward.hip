@@ -382,39 +382,45 @@ extern "C" size_t pa_forward_shared_workspace_size(int32_t num_seqs, int32_t num
   return sp.on ? sp.workspace_bytes() : fs.workspace_bytes();
 }
 
-extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                       const int32_t* block_tables, int32_t block_table_stride,
-                                       const int32_t* seq_lens, const int32_t* query_start_loc,
-                                       const int32_t* cached_lens, const int32_t* shared_blocks, int32_t num_seqs,
-                                       int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
-                                       int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
-                                       void* workspace, size_t workspace_bytes, void* stream) {
+// pa_forward_shared, optionally with the fused cache write (k_new / v_new set;
+// only when the shared-prefix decode takes the batch).
+static pa_status forward_shared_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, int32_t block_table_stride,
+                                     const int32_t* seq_lens, const int32_t* query_start_loc,
+                                     const int32_t* cached_lens, const int32_t* shared_blocks, int32_t num_seqs,
+                                     int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                     int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                                     void* workspace, size_t workspace_bytes, hipStream_t s, const char* who,
+                                     const void* k_new, const void* v_new, const int64_t* slots) {
   ForwardShape fs;
-  pa_status st =
-      shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, "pa_forward_shared", &fs);
+  pa_status st = shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, who, &fs);
   if (st != PA_OK) return st;
   if (num_seqs == 0 || num_tokens == 0 || max_seq_len == 0 || max_query_len == 0) return PA_OK;
   st = check_forward_args(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
-                          cached_lens, scale, causal, "pa_forward_shared");
+                          cached_lens, scale, causal, who);
   if (st != PA_OK) return st;
-  if (shared_blocks == nullptr) return fail(PA_ERR_ARG, "pa_forward_shared: shared_blocks is NULL");
+  if (shared_blocks == nullptr) return fail(PA_ERR_ARG, "%s: shared_blocks is NULL", who);
   const SharedPlan sp = shared_plan_of(num_seqs, num_q_heads, max_seq_len, max_query_len, c);
   const size_t ws_need = sp.on ? sp.workspace_bytes() : fs.workspace_bytes();
   if (ws_need > 0 && (workspace == nullptr || workspace_bytes < ws_need))
-    return fail(PA_ERR_ARG, "pa_forward_shared: workspace of %zu bytes needed, %zu given", ws_need,
+    return fail(PA_ERR_ARG, "%s: workspace of %zu bytes needed, %zu given", who, ws_need,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
-  hipStream_t s = (hipStream_t)stream;
   if (!sp.on)   // not a batch of single-token bf16 head_dim-128 sequences: pa_forward's paths
     return forward_impl(fs, out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
                         cached_lens, num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c, scale,
                         causal, workspace, s);
   if (check_mode()) {
-    if (stream_capturing(s)) return fail(PA_ERR_ARG, "pa_forward_shared: PA_CHECK=1 cannot run on a stream being captured");
+    if (stream_capturing(s)) return fail(PA_ERR_ARG, "%s: PA_CHECK=1 cannot run on a stream being captured", who);
     st = validate_metadata(block_tables, block_table_stride, seq_lens, query_start_loc, cached_lens, num_seqs,
                            num_tokens, max_seq_len, max_query_len, c->num_blocks, s);
     if (st != PA_OK) return st;
     st = validate_shared(block_tables, block_table_stride, seq_lens, shared_blocks, num_seqs, s);
     if (st != PA_OK) return st;
+    if (k_new != nullptr) {
+      st = validate_fused_slots(block_tables, block_table_stride, seq_lens, query_start_loc, slots, num_seqs,
+                                num_tokens, s);
+      if (st != PA_OK) return st;
+    }
   }
   AttnArgs a{};
   a.out = out;
@@ -435,7 +441,51 @@ extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_c
   a.scale_log2 = scale * kLog2e;
   a.causal = causal;
   a.prefill_min_q = 2;
+  a.k_new = k_new;
+  a.v_new = v_new;
   return launch_decode_shared(a, sp, shared_blocks, workspace, s);
+}
+
+extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t block_table_stride,
+                                       const int32_t* seq_lens, const int32_t* query_start_loc,
+                                       const int32_t* cached_lens, const int32_t* shared_blocks, int32_t num_seqs,
+                                       int32_t num_tokens, int32_t num_q_heads, int32_t max_seq_len,
+                                       int32_t max_query_len, const pa_cache_desc* c, float scale, int32_t causal,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return forward_shared_impl(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                             cached_lens, shared_blocks, num_seqs, num_tokens, num_q_heads, max_seq_len,
+                             max_query_len, c, scale, causal, workspace, workspace_bytes, (hipStream_t)stream,
+                             "pa_forward_shared", nullptr, nullptr, nullptr);
+}
+
+extern "C" pa_status pa_write_kv_forward_shared(const void* k, const void* v, const int64_t* slot_mapping,
+                                                void* out, const void* q, void* k_cache, void* v_cache,
+                                                const int32_t* block_tables, int32_t block_table_stride,
+                                                const int32_t* seq_lens, const int32_t* query_start_loc,
+                                                const int32_t* cached_lens, const int32_t* shared_blocks,
+                                                int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads,
+                                                int32_t max_seq_len, int32_t max_query_len, const pa_cache_desc* c,
+                                                float scale, int32_t causal, void* workspace,
+                                                size_t workspace_bytes, void* stream) {
+  ForwardShape fs;
+  pa_status st = shape_of(num_seqs, num_tokens, num_q_heads, max_seq_len, max_query_len, c,
+                          "pa_write_kv_forward_shared", &fs);
+  if (st != PA_OK) return st;
+  const SharedPlan sp = shared_plan_of(num_seqs, num_q_heads, max_seq_len, max_query_len, c);
+  hipStream_t s = (hipStream_t)stream;
+  if (!sp.on || num_tokens == 0) {   // the shared-prefix decode does not take the batch: the two calls
+    st = pa_write_kv(k, v, k_cache, v_cache, slot_mapping, num_tokens, c, stream);
+    if (st != PA_OK) return st;
+    return pa_forward_shared(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                             cached_lens, shared_blocks, num_seqs, num_tokens, num_q_heads, max_seq_len,
+                             max_query_len, c, scale, causal, workspace, workspace_bytes, stream);
+  }
+  if (!k || !v || !slot_mapping) return fail(PA_ERR_ARG, "pa_write_kv_forward_shared: NULL device pointer");
+  return forward_shared_impl(out, q, k_cache, v_cache, block_tables, block_table_stride, seq_lens, query_start_loc,
+                             cached_lens, shared_blocks, num_seqs, num_tokens, num_q_heads, max_seq_len,
+                             max_query_len, c, scale, causal, workspace, workspace_bytes, s,
+                             "pa_write_kv_forward_shared", k, v, slot_mapping);
 }
 
 extern "C" pa_status pa_write_kv_forward(const void* k, const void* v, const int64_t* slot_mapping, void* out,

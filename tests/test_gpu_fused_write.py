@@ -9,7 +9,9 @@ followed by pa_forward, on every decode route (balanced at every depth and
 wave count, the partitioned vector kernel, and the routes that do not fuse),
 on every dtype and head grouping, with the new token on the first, a middle
 and the last row of its block, at full size, and the output must meet the
-oracle.  Check mode refuses a slot that is not the sequence's last position.
+oracle.  pa_write_kv_forward_shared is held to the same bar against
+pa_write_kv + pa_forward_shared.  Check mode refuses a slot that is not the
+sequence's last position.
 """
 
 import numpy as np
@@ -130,4 +132,71 @@ def test_check_mode_refuses_a_wrong_slot(monkeypatch):
         with pytest.raises(pa.PagedAttnError) as e:
             run.step()
         assert e.value.status == pa.PA_ERR_RANGE
+    run.new_slots_d.copy_(good)
+
+
+HEADS = {1: (4, 4), 2: (8, 4), 4: (32, 8), 8: (64, 8)}     # G -> (Hq, Hkv)
+TREE = [(0, 300)] * 5 + [(1, 250), (0, 17), (0, 0), (0, 0), (8, 0), (0, 160), (0, 160)]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_shared_fused_equals_separate(G, monkeypatch):
+    """Fork trees (shared prefixes, copy-on-write) through the shared-prefix decode."""
+    for key in ("PA_SHARED_TOTAL_WAVES", "PA_SHARED_CG", "PA_CHECK"):
+        monkeypatch.delenv(key, raising=False)
+    Hq, Hkv = HEADS[G]
+    wl = workloads.fork_tree(f"tree_g{G}", 500 + G, Hq=Hq, Hkv=Hkv, D=128, dtype="bf16", root=304, forks=TREE,
+                             suffix_max=40)
+    for waves in (None, "7", "65536"):
+        if waves is None:
+            monkeypatch.delenv("PA_SHARED_TOTAL_WAVES", raising=False)
+        else:
+            monkeypatch.setenv("PA_SHARED_TOTAL_WAVES", waves)
+        a, b = _pair(wl, shared=True)
+        assert a.shared_blocks.max() > 0 and a.cow
+        _same(a, b, f"tree_g{G}/{waves}")
+        _oracle(a)
+
+
+def test_shared_fused_minis_and_other_batches(monkeypatch):
+    """The shared mini and CG = 4; batches the shared decode does not take run the two calls."""
+    for key in ("PA_SHARED_TOTAL_WAVES", "PA_SHARED_CG", "PA_CHECK"):
+        monkeypatch.delenv(key, raising=False)
+    a, b = _pair(workloads.mini("shared_bf16"), shared=True)
+    _same(a, b, "shared_bf16")
+    _oracle(a)
+    monkeypatch.setenv("PA_SHARED_CG", "4")
+    a, b = _pair(workloads.mini("shared_bf16"), shared=True)
+    _same(a, b, "shared_bf16/cg4")
+    monkeypatch.delenv("PA_SHARED_CG")
+    for name in ("mixed_bf16", "decode_fp8", "decode_f32", "verify_bf16"):
+        a, b = _pair(workloads.mini(name), shared=True)
+        _same(a, b, name)
+
+
+@pytest.mark.timeout(900)
+def test_shared_fused_full_size(monkeypatch):
+    for key in ("PA_SHARED_TOTAL_WAVES", "PA_SHARED_CG", "PA_CHECK"):
+        monkeypatch.delenv(key, raising=False)
+    a, b = _pair(workloads.shared_prefix_cow(), shared=True)
+    _same(a, b, "shared_prefix_cow")
+    _oracle(a)
+
+
+def test_shared_check_mode_refuses_a_wrong_slot(monkeypatch):
+    import torch
+    import paged_kv_cache_forward_amd as pa
+    for key in ("PA_SHARED_TOTAL_WAVES", "PA_SHARED_CG"):
+        monkeypatch.delenv(key, raising=False)
+    ensure_library()
+    from workloads.device import DeviceRun
+    run = DeviceRun(workloads.mini("shared_bf16"), shared=True)
+    monkeypatch.setenv("PA_CHECK", "1")
+    run.step()                                     # the true slots pass
+    torch.cuda.synchronize()
+    good = run.new_slots_d.clone()
+    run.new_slots_d.copy_(good.flip(0))
+    with pytest.raises(pa.PagedAttnError) as e:
+        run.step()
+    assert e.value.status == pa.PA_ERR_RANGE
     run.new_slots_d.copy_(good)

@@ -146,3 +146,20 @@ def test_write_kv_forward_host_checks_without_a_gpu():
     assert fn(None, None, None, None, None, None, None, None, 1, None, None, None, 0, 0, 32, 0, 0,
               ctypes.byref(desc), 0.1, 1, None, 0, None) == pa.PA_OK
 
+
+def test_write_kv_forward_shared_host_checks_without_a_gpu():
+    """pa_write_kv_forward_shared refuses NULL pointers before any HIP call; an empty batch is a no-op."""
+    import ctypes
+    pa = ensure_library()
+    desc = pa.CacheDesc(100, 8, 128, 16, pa.PA_BF16)
+    fn = pa.lib.pa_write_kv_forward_shared
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: the calls return before launching
+    st = fn(None, fake, fake, fake, fake, fake, fake, fake, 1, fake, fake, fake, fake, 64, 64, 32, 4096, 1,
+            ctypes.byref(desc), 0.1, 1, fake, 1 << 30, None)
+    assert st == pa.PA_ERR_ARG and "NULL" in pa.lib.pa_last_error().decode()
+    st = fn(fake, fake, fake, fake, fake, fake, fake, fake, 1, fake, fake, fake, None, 64, 64, 32, 4096, 1,
+            ctypes.byref(desc), 0.1, 1, fake, 1 << 30, None)
+    assert st == pa.PA_ERR_ARG and "shared_blocks" in pa.lib.pa_last_error().decode()
+    assert fn(None, None, None, None, None, None, None, None, 1, None, None, None, None, 0, 0, 32, 0, 0,
+              ctypes.byref(desc), 0.1, 1, None, 0, None) == pa.PA_OK
+

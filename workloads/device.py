@@ -149,9 +149,10 @@ class DeviceRun:
 
     def step(self, stream=None):
         """One engine step.  With ``fused`` (the default) the new tokens' write and attention are one
-        ``pa_write_kv_forward`` call (the library fuses the write into a single-token batch's decode);
-        otherwise ``pa_write_kv`` then ``pa_forward`` (or ``pa_forward_shared``)."""
-        if self.shared or not self.fused:
+        ``pa_write_kv_forward`` (``pa_write_kv_forward_shared``) call: the library fuses the write into
+        a single-token batch's decode; otherwise ``pa_write_kv`` then ``pa_forward``
+        (``pa_forward_shared``)."""
+        if not self.fused:
             self.step_writes(stream)
             self.forward(stream)
             return
@@ -159,6 +160,13 @@ class DeviceRun:
         if self.pairs_d.shape[0]:
             self._bound("copy", stream, lambda s: pa.pa_copy_blocks(self.k_cache, self.v_cache, self.pairs_d,
                                                                     stream=s, bind=True))()
+        if self.shared:
+            self._bound("fused_shared", stream, lambda s: pa.pa_write_kv_forward_shared(
+                self.k_new, self.v_new, self.new_slots_d, self.out, self.q, self.k_cache, self.v_cache,
+                self.block_tables, self.seq_lens, self.qsl, self.cached_lens, self.shared_blocks_d,
+                self.max_seq_len, wl.max_query_len, wl.scale, wl.causal, workspace=self.workspace, stream=s,
+                bind=True))()
+            return
         self._bound("fused", stream, lambda s: pa.pa_write_kv_forward(
             self.k_new, self.v_new, self.new_slots_d, self.out, self.q, self.k_cache, self.v_cache,
             self.block_tables, self.seq_lens, self.qsl, self.cached_lens, self.max_seq_len, wl.max_query_len,
