@@ -228,8 +228,7 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_PREFILL_ROWS=32 (default) | 64   chunked prefill: (token, head) rows per
  *            wave (64: head_dim 128 only)
  *   PA_PREFILL_WAVES=4|8    chunked prefill (bf16, head_dim 128, 32 rows per
- *            wave): waves per work-group (default 8 when fewer than half of
- *            num_seqs * max_query_len are query tokens, else 4)
+ *            wave): waves per work-group (default 4)
  *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
  *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
  *            max(1024, a quarter of the longest sequence)

@@ -684,19 +684,17 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   if (const char* env = std::getenv("PA_PREFILL_ROWS")) {
     if (std::strcmp(env, "64") == 0 && a.head_dim == 128) rt = 4;
   }
-  // Waves per work-group (bf16, head_dim 128, 32 rows per wave).  The grid
-  // holds a work-group per (query tile, KV head, piece) for every sequence of
-  // the batch, and those of sequences that are not chunks find no rows and
-  // exit -- but each first holds an LDS slot.  When most sequences cannot be
-  // chunks (fewer query tokens than half of num_seqs * max_query_len), eight
-  // waves (256 rows) per work-group halve the query tiles and with them those
-  // empty work-groups; otherwise four waves, two work-groups per CU, keep
-  // the better overlap.  Measured on MI355X: 16 decode sequences + 4 chunks
-  // of 512, prefill 164 us (8 waves) vs 176 us (4); the 4 chunks alone, 158
-  // us vs 149 us.  PA_PREFILL_WAVES=4|8 overrides.
+  // Waves per work-group (bf16, head_dim 128, 32 rows per wave): four (128
+  // rows, two work-groups per CU).  The grid holds a work-group per (query
+  // tile, KV head, piece) for every sequence of the batch, and those of
+  // sequences that are not chunks find no rows and exit; eight waves (256
+  // rows, one work-group per CU) halve those, but measured on MI355X four
+  // waves are faster on both shapes: 16 decode sequences + 4 chunks of 512,
+  // 139.3-139.7 us vs 141.4-141.9 us; the 4 chunks alone, 141-150 us vs
+  // 150-156 us (without the clocks settled first).  PA_PREFILL_WAVES=8
+  // selects eight.
   int nw = 4;
   if (!fp8 && a.head_dim == 128 && rt == 2) {
-    if ((int64_t)a.num_tokens * 2 < (int64_t)a.num_seqs * max_query_len) nw = 8;
     if (const char* env = std::getenv("PA_PREFILL_WAVES")) nw = std::atoi(env) == 8 ? 8 : 4;
   }
   const int TOK = 16 * rt * nw / G;
