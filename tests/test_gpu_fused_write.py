@@ -200,3 +200,21 @@ def test_shared_check_mode_refuses_a_wrong_slot(monkeypatch):
         run.step()
     assert e.value.status == pa.PA_ERR_RANGE
     run.new_slots_d.copy_(good)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_batches(seed, monkeypatch):
+    """Random single-token batches (lengths 1..3000, any group size, 1..80 sequences) on the default
+    route and the vector kernel: the fused call gives the two calls' bits."""
+    rng = np.random.default_rng(7000 + seed)
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.integers(1, 81))
+    cached = rng.integers(0, 3000, size=S).tolist()
+    wl = workloads.independent(f"random_{seed}", 7100 + seed, Hq=G * Hkv, Hkv=Hkv, D=128, dtype="bf16",
+                               cached=cached, new=[1] * S, pool_extra=3)
+    for route in ("default", "valu", "waves7"):
+        _route(monkeypatch, route)
+        a, b = _pair(wl)
+        _same(a, b, f"random_{seed}/G{G}/Hkv{Hkv}/S{S}/{route}")
+    _oracle(a)
