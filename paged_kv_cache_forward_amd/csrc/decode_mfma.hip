@@ -668,23 +668,43 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
   const AttnArgs& a = k.a;
   const int i = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
   const int lane = threadIdx.x, h = lane / LPH, c = lane % LPH;
-  const int q0 = a.qsl[i];
-  if (a.qsl[i + 1] - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
-  const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
+  // Two memory round trips: first everything that depends on i alone (this
+  // call's decode kernel wrote seqinfo for every sequence it took), then the
+  // new rows, their table entry and the parts' partials together.
+  const int q0 = a.qsl[i], q1 = a.qsl[i + 1];
+  const int len = a.seq_lens[i];
+  const int2 si = k.seqinfo[i];
+  // (An empty asm reading all four values keeps the compiler from sinking the
+  // later loads below the checks, which would make them serial round trips.)
+  asm volatile("" ::"s"(q0), "s"(q1), "s"(len), "s"(si.x), "s"(si.y));
+  if (q1 - q0 != 1 || q0 < 0 || q0 >= a.num_tokens) return;
+  const int L = min(len, a.bt_stride * kBlock);
   if (L <= 0) return;
-  if (a.k_new != nullptr && lane < 32) {
-    // Fused cache write: the new token's K (lanes 0..15) and V (16..31) row
-    // into its slot, position L - 1.  The decode kernel, which ran before,
-    // took this row from k_new / v_new, not from the cache.
-    const int bid = clamp_block(a.block_tables[(size_t)i * a.bt_stride + (L - 1) / kBlock], a.num_blocks);
-    const size_t src = ((size_t)q0 * a.num_kv_heads + g) * kRowBytes + (lane & 15) * 16;
-    const size_t dst = ((size_t)bid * a.num_kv_heads + g) * kTileBytes + ((L - 1) % kBlock) * kRowBytes + (lane & 15) * 16;
-    const uint4 x = ld16((const uint8_t*)(lane < 16 ? a.k_new : a.v_new) + src);
-    st16((uint8_t*)(lane < 16 ? a.k_cache : a.v_cache) + dst, x);
+  // Fused cache write: the new token's K (lanes 0..15) and V (16..31) row
+  // into its slot, position L - 1, stored after the partials' loads are
+  // issued.  The decode kernel, which ran before, took this row from k_new /
+  // v_new, not from the cache.
+  // Each of those lanes loads the table entry itself, so nothing waits for
+  // it before the partials' loads are issued.
+  const bool fw = a.k_new != nullptr;
+  uint4 x_new = make_uint4(0u, 0u, 0u, 0u);
+  int bid_new = 0;
+  if (fw && lane < 32) {
+    bid_new = a.block_tables[(size_t)i * a.bt_stride + (L - 1) / kBlock];
+    x_new = ld16((const uint8_t*)(lane < 16 ? a.k_new : a.v_new) + ((size_t)q0 * a.num_kv_heads + g) * kRowBytes +
+                 (lane & 15) * 16);
   }
-  const int2 si = k.seqinfo[i];          // written by this call's decode kernel
+  auto store_new = [&]() {
+    if (!fw || lane >= 32) return;
+    const size_t dst = ((size_t)clamp_block(bid_new, a.num_blocks) * a.num_kv_heads + g) * kTileBytes +
+                       ((L - 1) % kBlock) * kRowBytes + (lane & 15) * 16;
+    st16((uint8_t*)(lane < 16 ? a.k_cache : a.v_cache) + dst, x_new);
+  };
   const int P = si.y;
-  if (P <= 1) return;                    // written out by the decode kernel
+  if (P <= 1) {                          // written out by the decode kernel
+    store_new();
+    return;
+  }
   const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);
   float Mx = -INFINITY, den = 0.0f;
   float num[DPL];
@@ -723,6 +743,7 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
       Mx = Mn;
     }
   }
+  store_new();
   const float inv = 1.0f / den;
   uint32_t wd[DPL / 2];
 #pragma unroll

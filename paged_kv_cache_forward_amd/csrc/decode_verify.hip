@@ -81,13 +81,17 @@ inline size_t verify_dyn_lds(int num_seqs) { return (size_t)(3 * num_seqs + 1) *
 // Static LDS of one instantiation: lookup windows, query rows, NS stages.
 inline size_t verify_static_lds(int cg, int ns) { return 3 * 512 + (size_t)cg * 4096 + (size_t)ns * 8192; }
 
-// True for the sequences this kernel and its merge handle (the same test in both).
+// True for the sequences this kernel and its merge handle (the same test in
+// both), from query_start_loc[i], [i + 1] and seq_lens[i].
+__device__ __forceinline__ bool verify_item_of(const VerifyArgs& k, int qa, int qb, int sl, int& q0, int& n,
+                                               int& len) {
+  q0 = qa;
+  n = qb - qa;
+  len = min(sl, k.a.bt_stride * kBlock);
+  return n >= k.min_q && n <= k.max_q && q0 >= 0 && q0 + n <= k.a.num_tokens && len >= n;
+}
 __device__ __forceinline__ bool verify_item(const VerifyArgs& k, int i, int& q0, int& n, int& len) {
-  const AttnArgs& a = k.a;
-  q0 = a.qsl[i];
-  n = a.qsl[i + 1] - q0;
-  len = min(a.seq_lens[i], a.bt_stride * kBlock);
-  return n >= k.min_q && n <= k.max_q && q0 >= 0 && q0 + n <= a.num_tokens && len >= n;
+  return verify_item_of(k, k.a.qsl[i], k.a.qsl[i + 1], k.a.seq_lens[i], q0, n, len);
 }
 
 // Wait until at most OPS * t vector memory operations (t tiles' copies) are outstanding.
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   static_assert(NS >= 2 && NS <= 5, "tiles in flight");
   constexpr int C = 16 * CG;
   constexpr int TILE = F8 ? kTileBytesF8 : kTileBytes;   // bytes of one (block, KV head) code tile
-  constexpr int OPS = F8 ? 6 : 8;                        // copies per tile
+  constexpr int OPS = F8 ? 5 : 8;                        // copies per tile
   constexpr int STAGE_U4 = F8 ? 260 : 512;               // one LDS stage, in 16-byte units
   extern __shared__ int s_dyn[];
   const AttnArgs& a = k.a;
@@ -286,12 +290,12 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
       for (int p = 0; p < 2; ++p) lds_copy16_nt(rk, dst + p * 64, j * kD + r * 16 + p * 64);
 #pragma unroll
       for (int p = 0; p < 2; ++p) lds_copy16_nt(rv, dst + 128 + p * 64, (p * 64 + lane) * kBlock);
-      const size_t xoff = (size_t)bid * Hkv * kBlock;
-      const u32x4_t rkx = rsrc_words(kx + xoff, real ? kBlock : 0);
-      const u32x4_t rvx = rsrc_words(vx + xoff, real ? kBlock : 0);
-      if (lane < 4) {
-        lds_copy4(rkx, dst + 256, 4 * lane);
-        lds_copy4(rvx, (uint8_t*)(dst + 256) + 16, 4 * lane);
+      // One copy for both: lanes 0..3 the K row exponents, lanes 4..7 the V
+      // ones, by address (a prefetch past the range reads the clamped
+      // tile's, into a stage no fold reads).
+      if (lane < 8) {
+        const size_t xoff = (size_t)bid * Hkv * kBlock + 4 * (lane & 3);
+        lds_copy4_global((lane < 4 ? kx : vx) + xoff, dst + 256);
       }
     } else {
       const int seq = __builtin_amdgcn_readfirstlane(s_sj[w][0][e]);
@@ -555,10 +559,15 @@ __global__ __launch_bounds__(512) void merge_verify_kernel(VerifyArgs k) {
   const AttnArgs& a = k.a;
   const int Hkv = a.num_kv_heads, G = a.num_q_heads / Hkv;
   const int i = blockIdx.x / Hkv, g = blockIdx.x % Hkv, cg = blockIdx.y;
+  // The part table is read with the sequence's metadata, in one memory round
+  // trip (this call's verify kernel wrote it for every sequence it took); the
+  // empty asm keeps the compiler from sinking that load below the checks.
+  const int2 si = k.seqinfo[i];
+  const int qa = a.qsl[i], qb = a.qsl[i + 1], sl = a.seq_lens[i];
+  asm volatile("" ::"s"(si.x), "s"(si.y), "s"(qa), "s"(qb), "s"(sl));
   int q0, n, len;
-  if (!verify_item(k, i, q0, n, len)) return;
+  if (!verify_item_of(k, qa, qb, sl, q0, n, len)) return;
   if (cg * 16 >= n * G) return;          // column group beyond this sequence's rows
-  const int2 si = k.seqinfo[i];          // written by this call's verify kernel
   const int P = si.y;
   if (P <= 1) return;                    // written out by the verify kernel
   const size_t slot0 = (size_t)g * k.slots + (size_t)(i + si.x);

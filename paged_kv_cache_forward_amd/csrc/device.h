@@ -179,6 +179,13 @@ __device__ __forceinline__ void lds_copy16_global(const void* src, const void* l
                : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(src)
                : "memory", "m0");
 }
+// As lds_copy16_global, 4 bytes per lane (to `lds` + 4 * lane).
+__device__ __forceinline__ void lds_copy4_global(const void* src, const void* lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_void_t*)lds)), "v"(src)
+               : "memory", "m0");
+}
 // As lds_copy16, 4 bytes per lane (to `lds` + 4 * lane).
 __device__ __forceinline__ void lds_copy4(u32x4_t rsrc, const void* lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"

@@ -266,7 +266,7 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
   int32_t* v_info = nullptr;
   float* v_acc = nullptr;
   float* v_ml = nullptr;
-  float* pre_o = nullptr;
+  uint16_t* pre_o = nullptr;
   float* pre_ml = nullptr;
   if (ws_need > 0) {
     uint8_t* base = (uint8_t*)workspace;
@@ -278,7 +278,7 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
     v_acc = (float*)(vbase + fs.vplan.info_bytes);
     v_ml = (float*)(vbase + fs.vplan.info_bytes + fs.vplan.acc_bytes);
     uint8_t* pbase = vbase + fs.vplan.workspace_bytes();
-    pre_o = (float*)pbase;
+    pre_o = (uint16_t*)pbase;
     pre_ml = (float*)(pbase + fs.pplan.o_bytes);
   }
   if (fs.use_mfma_prefill) {

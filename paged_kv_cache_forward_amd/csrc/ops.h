@@ -148,10 +148,11 @@ pa_status launch_decode_shared(const AttnArgs& a, const SharedPlan& sp, const in
 // Split-KV plan for the chunked-prefill kernel: the key range of every
 // (sequence, query tile, KV head) work-group is cut into pieces of piece_keys
 // keys (a multiple of 64); work-groups whose range spans more than one piece
-// write fp32 partials per piece and the prefill merge kernel combines them.
+// write partials per piece and the prefill merge kernel combines them.
 // Workspace (after the decode partials, 256-byte aligned):
-//   [partial O: fp32 [num_tokens][Hq][pieces][head_dim]]
-//   [partial (max, sum): fp32 [num_tokens][Hq][pieces][2]]
+//   [partial O: fp16 [num_tokens][Hq][pieces][head_dim], each row normalised
+//    by its piece's weight sum and scaled by 2^-e]
+//   [partial (max, sum, e, 0): fp32 [num_tokens][Hq][pieces][4]]
 struct PrefillPlan {
   int32_t piece_keys;
   int32_t pieces;      // pieces of the longest key range; 1 = no split
@@ -166,7 +167,7 @@ PrefillPlan make_prefill_plan(int32_t num_tokens, int32_t num_q_heads, int32_t h
 // Chunked-prefill (MFMA) kernel for bf16 (or fp8-cache) sequences with more
 // than one query token, followed by its merge when the plan splits key ranges.
 bool prefill_mfma_supported(int32_t dtype, int32_t head_dim, int32_t group);
-pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, float* p_o, float* p_ml,
+pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const PrefillPlan& pp, uint16_t* p_o, float* p_ml,
                          bool fp8, hipStream_t s);
 
 }  // namespace pa
