@@ -69,8 +69,8 @@ struct VerifyArgs {
   int32_t max_q;
   int32_t waves_per_head;   // Wg
   int32_t slots;            // partial slots per KV head: num_seqs + Wg
-  float* p_acc;             // [Hkv][slots][CG][8 db][64 lanes][4]: fragment order (see finish)
-  float* p_ml;              // [Hkv][slots][16 CG][2]  (max in base-2 units, sum)
+  uint16_t* p_acc;          // [Hkv][slots][CG][8 db][64 lanes][4] fp16: fragment order (see finish)
+  float* p_ml;              // [Hkv][slots][16 CG][4]  (max in base-2 units, sum, e, 0)
   int2* seqinfo;            // [num_seqs]: (first rank, parts)
 };
 
@@ -343,16 +343,36 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
               make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
         }
       } else {
-        // Partials in fragment order: dim block db of column group cg is one
-        // contiguous 1 KiB piece, lane l's four values at 16 l, so every store
-        // instruction writes whole cache lines.
-        float* dst = k.p_acc + ((slot * CG + cg) * 8 * 64 + lane) * 4;
+        // Partials: the column's output normalised by its weight sum, times
+        // 2^-e in fp16, e set by the column's largest magnitude (over its four
+        // lanes) so that it lands in [2^14, 2^15): full fp16 precision through
+        // exact power-of-two scalings, half the bytes of fp32.  Fragment order:
+        // dim block db of column group cg is one contiguous 512-byte piece,
+        // lane l's four values at 8 l.  Beside them (max, sum, e); a column
+        // that sees no key of this part has sum 0 and weight 0 in the merge.
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        float amax = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(st.acc[cg][db][e] * inv));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int ex = amax > 0.0f ? max(ilogbf(amax) - 14, -100) : 0;
+        uint16_t* dst = k.p_acc + ((slot * CG + cg) * 8 * 64 + lane) * 4;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const f32x4_t x = st.acc[cg][db];
-          *reinterpret_cast<float4*>(dst + db * 256) = make_float4(x[0], x[1], x[2], x[3]);
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const _Float16 lo = static_cast<_Float16>(ldexpf(st.acc[cg][db][2 * h] * inv, -ex));
+            const _Float16 hi = static_cast<_Float16>(ldexpf(st.acc[cg][db][2 * h + 1] * inv, -ex));
+            w[h] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *reinterpret_cast<uint2*>(dst + db * 256) = make_uint2(w[0], w[1]);
         }
-        if (r == 0) *reinterpret_cast<float2*>(k.p_ml + (slot * C + col) * 2) = make_float2(st.m[cg], lt);
+        if (r == 0)
+          *reinterpret_cast<float4*>(k.p_ml + (slot * C + col) * 4) = make_float4(st.m[cg], lt, (float)ex, 0.0f);
       }
     }
   };
@@ -576,30 +596,35 @@ __global__ __launch_bounds__(512) void merge_verify_kernel(VerifyArgs k) {
     const int ln = it & 63, db = (it >> 6) & 7;
     const int col = 16 * cg + (ln & 15);
     if (col >= n * G) return;
-    const float2* ml = reinterpret_cast<const float2*>(k.p_ml) + slot0 * C + col;
-    const float* acc = k.p_acc + (slot0 * CG * 8 * 64 + it) * 4;
+    const float4* ml = reinterpret_cast<const float4*>(k.p_ml) + slot0 * C + col;
+    const uint16_t* acc = k.p_acc + (slot0 * CG * 8 * 64 + it) * 4;
     float M = -INFINITY, den = 0.0f;
     float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int p0 = 0; p0 < P; p0 += U) {
-      float2 v[U];
-      float4 x[U];
+      float4 v[U];
+      uint2 x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (p0 + u < P) {
           v[u] = ml[(size_t)(p0 + u) * C];
-          x[u] = *reinterpret_cast<const float4*>(acc + (size_t)(p0 + u) * C * kD);   // one slot = C x D floats
+          x[u] = *reinterpret_cast<const uint2*>(acc + (size_t)(p0 + u) * C * kD);   // one slot = C x D values
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (p0 + u >= P) break;
+        // Part u's output is sum * 2^e * (the stored values).
         const float Mn = fmaxf(M, v[u].x);
         const float sa = fast_exp2(M - Mn), sb = fast_exp2(v[u].x - Mn);
         den = fmaf(den, sa, v[u].y * sb);
-        num.x = fmaf(num.x, sa, x[u].x * sb);
-        num.y = fmaf(num.y, sa, x[u].y * sb);
-        num.z = fmaf(num.z, sa, x[u].z * sb);
-        num.w = fmaf(num.w, sa, x[u].w * sb);
+        const float wv = ldexpf(v[u].y * sb, (int)v[u].z);
+        auto h16 = [](uint32_t w, int hi) {
+          return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(hi ? w >> 16 : w & 0xffffu)));
+        };
+        num.x = fmaf(num.x, sa, h16(x[u].x, 0) * wv);
+        num.y = fmaf(num.y, sa, h16(x[u].x, 1) * wv);
+        num.z = fmaf(num.z, sa, h16(x[u].y, 0) * wv);
+        num.w = fmaf(num.w, sa, h16(x[u].y, 1) * wv);
         M = Mn;
       }
     }
@@ -693,12 +718,12 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   }
   const size_t slots = (size_t)num_seqs + (size_t)wg;
   vp.info_bytes = round256((size_t)num_seqs * 2 * sizeof(int32_t));
-  vp.acc_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * head_dim * sizeof(float));
-  vp.ml_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * 2 * sizeof(float));
+  vp.acc_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * head_dim * sizeof(uint16_t));
+  vp.ml_bytes = round256((size_t)num_kv_heads * slots * 16 * cg * 4 * sizeof(float));
   return vp;
 }
 
-pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,
+pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, uint16_t* p_acc, float* p_ml,
                                int32_t* part_table, hipStream_t s) {
   VerifyArgs k{a, vp.min_q, vp.max_q, vp.waves_per_head, a.num_seqs + vp.waves_per_head, p_acc, p_ml, (int2*)part_table};
   const int G = a.num_q_heads / a.num_kv_heads;

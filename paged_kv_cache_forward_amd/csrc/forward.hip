@@ -264,7 +264,7 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
   float* p_acc = nullptr;
   float* p_ml = nullptr;
   int32_t* v_info = nullptr;
-  float* v_acc = nullptr;
+  uint16_t* v_acc = nullptr;
   float* v_ml = nullptr;
   uint16_t* pre_o = nullptr;
   float* pre_ml = nullptr;
@@ -275,7 +275,7 @@ static pa_status forward_impl(const ForwardShape& fs, void* out, const void* q, 
     p_ml = (float*)(base + fs.plan.info_bytes + fs.plan.acc_bytes);
     uint8_t* vbase = base + fs.plan.workspace_bytes();
     v_info = (int32_t*)vbase;
-    v_acc = (float*)(vbase + fs.vplan.info_bytes);
+    v_acc = (uint16_t*)(vbase + fs.vplan.info_bytes);
     v_ml = (float*)(vbase + fs.vplan.info_bytes + fs.vplan.acc_bytes);
     uint8_t* pbase = vbase + fs.vplan.workspace_bytes();
     pre_o = (uint16_t*)pbase;

@@ -104,8 +104,9 @@ pa_status launch_decode_balanced(const AttnArgs& a, const DecodePlan& plan, floa
 // single-token decode, columns = (token, query head) pairs in col_groups
 // groups of 16.  Workspace (offsets 256-byte aligned):
 //   [part table: int32 [num_seqs][2]]
-//   [partial acc: fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][head_dim]]
-//   [partial (max, sum): fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][2]]
+//   [partial acc: fp16 [Hkv][num_seqs + waves_per_head][16 col_groups][head_dim], each
+//    column normalised by its weight sum and scaled by 2^-e]
+//   [partial (max, sum, e, 0): fp32 [Hkv][num_seqs + waves_per_head][16 col_groups][4]]
 struct VerifyPlan {
   bool on;
   bool fp8;                // quantised pools (then it takes every sequence it can)
@@ -121,7 +122,7 @@ struct VerifyPlan {
 bool verify_fp8_supported(int32_t head_dim, int32_t group);
 VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                             int32_t head_dim, int32_t dtype, int32_t max_seq_len, int32_t max_query_len);
-pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, float* p_acc, float* p_ml,
+pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, uint16_t* p_acc, float* p_ml,
                                int32_t* part_table, hipStream_t s);
 
 // Plan for the shared-prefix decode (pa_forward_shared): single-token
