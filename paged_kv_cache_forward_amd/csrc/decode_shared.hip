@@ -57,8 +57,8 @@ struct SharedArgs {
   const int32_t* shared_blocks;   // [num_seqs]
   int32_t waves_per_head;         // Wg
   int32_t slots;                  // partial slots per KV head: 2 num_seqs + Wg
-  float* p_acc;                   // [Hkv][slots][CG][8 db][64 lanes][4]: fragment order
-  float* p_ml;                    // [Hkv][slots][16 CG][2]  (max in base-2 units, sum)
+  uint16_t* p_acc;                // [Hkv][slots][CG][8 db][64 lanes][4] fp16: fragment order
+  float* p_ml;                    // [Hkv][slots][16 CG][4]  (max in base-2 units, sum, e, 0)
   int2* item_info;                // [2 num_seqs]: (first rank, parts) of each item
   int32_t* seq_prefix;            // [num_seqs]: F of the sequence's group (0: none)
 };
@@ -310,13 +310,33 @@ __global__ __launch_bounds__(64) void decode_shared_kernel(SharedArgs k) {
               make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv), pack_bf16x2(x[2] * inv, x[3] * inv));
         }
       } else {
-        float* dst = k.p_acc + ((slot * CG + cg) * 8 * 64 + lane) * 4;
+        // The column's output normalised by its weight sum, times 2^-e in
+        // fp16 (e from the column's largest magnitude over its four lanes:
+        // values in [2^14, 2^15), exact power-of-two scalings), in fragment
+        // order, with (max, sum, e); sum 0 (no key seen) weighs 0 in the merge.
+        const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+        float amax = 0.0f;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(st.acc[cg][db][e] * inv));
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int ex = amax > 0.0f ? max(ilogbf(amax) - 14, -100) : 0;
+        uint16_t* dst = k.p_acc + ((slot * CG + cg) * 8 * 64 + lane) * 4;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const f32x4_t x = st.acc[cg][db];
-          *reinterpret_cast<float4*>(dst + db * 256) = make_float4(x[0], x[1], x[2], x[3]);
+          uint32_t w[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const _Float16 lo = static_cast<_Float16>(ldexpf(st.acc[cg][db][2 * hh] * inv, -ex));
+            const _Float16 hi = static_cast<_Float16>(ldexpf(st.acc[cg][db][2 * hh + 1] * inv, -ex));
+            w[hh] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+          }
+          *reinterpret_cast<uint2*>(dst + db * 256) = make_uint2(w[0], w[1]);
         }
-        if (r == 0) *reinterpret_cast<float2*>(k.p_ml + (slot * C + col) * 2) = make_float2(st.m[cg], lt);
+        if (r == 0)
+          *reinterpret_cast<float4*>(k.p_ml + (slot * C + col) * 4) = make_float4(st.m[cg], lt, (float)ex, 0.0f);
       }
     }
   };
@@ -554,28 +574,33 @@ __global__ __launch_bounds__(256) void merge_shared_kernel(SharedArgs k) {
     }
     const size_t slot0 = (size_t)g * k.slots + item + info.x;
     const int cg = col / 16, ln = 16 * r + col % 16;
-    const float2* ml = reinterpret_cast<const float2*>(k.p_ml) + slot0 * C + col;
-    const float* acc = k.p_acc + (((slot0 * CG + cg) * 8 + db) * 64 + ln) * 4;
+    const float4* ml = reinterpret_cast<const float4*>(k.p_ml) + slot0 * C + col;
+    const uint16_t* acc = k.p_acc + (((slot0 * CG + cg) * 8 + db) * 64 + ln) * 4;
     for (int p0 = 0; p0 < info.y; p0 += U) {
-      float2 v[U];
-      float4 x[U];
+      float4 v[U];
+      uint2 x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (p0 + u < info.y) {
           v[u] = ml[(size_t)(p0 + u) * C];
-          x[u] = *reinterpret_cast<const float4*>(acc + (size_t)(p0 + u) * C * kD);   // one slot = C x D floats
+          x[u] = *reinterpret_cast<const uint2*>(acc + (size_t)(p0 + u) * C * kD);   // one slot = C x D values
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (p0 + u >= info.y) break;
+        // Part u's output is sum * 2^e * (the stored values).
         const float Mn = fmaxf(M, v[u].x);
         const float sa = fast_exp2(M - Mn), sb = fast_exp2(v[u].x - Mn);
         den = fmaf(den, sa, v[u].y * sb);
-        num.x = fmaf(num.x, sa, x[u].x * sb);
-        num.y = fmaf(num.y, sa, x[u].y * sb);
-        num.z = fmaf(num.z, sa, x[u].z * sb);
-        num.w = fmaf(num.w, sa, x[u].w * sb);
+        const float wv = ldexpf(v[u].y * sb, (int)v[u].z);
+        auto h16 = [](uint32_t w, int hi) {
+          return static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(hi ? w >> 16 : w & 0xffffu)));
+        };
+        num.x = fmaf(num.x, sa, h16(x[u].x, 0) * wv);
+        num.y = fmaf(num.y, sa, h16(x[u].x, 1) * wv);
+        num.z = fmaf(num.z, sa, h16(x[u].y, 0) * wv);
+        num.w = fmaf(num.w, sa, h16(x[u].y, 1) * wv);
         M = Mn;
       }
     }
@@ -639,8 +664,8 @@ SharedPlan make_shared_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_k
   const size_t slots = 2 * (size_t)num_seqs + (size_t)wg;
   sp.prefix_bytes = round256s((size_t)num_seqs * sizeof(int32_t));
   sp.info_bytes = round256s((size_t)num_seqs * 2 * sizeof(int2));
-  sp.acc_bytes = round256s((size_t)num_kv_heads * slots * 16 * sp.col_groups * head_dim * sizeof(float));
-  sp.ml_bytes = round256s((size_t)num_kv_heads * slots * 16 * sp.col_groups * 2 * sizeof(float));
+  sp.acc_bytes = round256s((size_t)num_kv_heads * slots * 16 * sp.col_groups * head_dim * sizeof(uint16_t));
+  sp.ml_bytes = round256s((size_t)num_kv_heads * slots * 16 * sp.col_groups * 4 * sizeof(float));
   return sp;
 }
 
@@ -651,7 +676,7 @@ pa_status launch_decode_shared(const AttnArgs& a, const SharedPlan& sp, const in
                shared_blocks,
                sp.waves_per_head,
                2 * a.num_seqs + sp.waves_per_head,
-               (float*)(base + sp.prefix_bytes + sp.info_bytes),
+               (uint16_t*)(base + sp.prefix_bytes + sp.info_bytes),
                (float*)(base + sp.prefix_bytes + sp.info_bytes + sp.acc_bytes),
                (int2*)(base + sp.prefix_bytes),
                (int32_t*)base};

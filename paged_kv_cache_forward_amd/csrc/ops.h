@@ -130,8 +130,9 @@ pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, uint16_t
 // (offsets 256-byte aligned):
 //   [group prefix F per sequence: int32 [num_seqs]]
 //   [item (first rank, parts): int2 [2 num_seqs]]
-//   [partial acc: fp32 [Hkv][2 num_seqs + waves_per_head][col_groups][8][64][4]]
-//   [partial (max, sum): fp32 [Hkv][2 num_seqs + waves_per_head][16 col_groups][2]]
+//   [partial acc: fp16 [Hkv][2 num_seqs + waves_per_head][col_groups][8][64][4], each column
+//    normalised by its weight sum and scaled by 2^-e]
+//   [partial (max, sum, e, 0): fp32 [Hkv][2 num_seqs + waves_per_head][16 col_groups][4]]
 struct SharedPlan {
   bool on;
   int32_t col_groups;      // 2 or 4 groups of 16 MFMA columns
