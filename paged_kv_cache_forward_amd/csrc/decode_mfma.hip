@@ -654,17 +654,22 @@ __global__ __launch_bounds__(64) void decode_balanced_kernel(BalancedArgs k) {
   finish_segment<G>(k, cur, g, rank, cur_j0 == 0 && cur_jl + 1 == T, s_meta[cur] >> 5, st);
 }
 
-// Merge of the balanced decode's parts: one wave per (sequence, KV head), for
-// all G query heads of that head.  A part's G x D partial block is
-// contiguous, so reading a part is one coalesced load of 2G floats per lane
-// (lane = head * 64/G + chunk).  The wave folds the parts in order with the
-// log-sum-exp rule, eight parts' loads in flight per round trip (a sequence
-// has a few parts: one memory round trip), and writes the output.
-template <int G>
-__global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
-  constexpr int LPH = 64 / G;          // lanes per head
-  constexpr int DPL = kD / LPH;        // dims per lane: 2 G
-  constexpr int U = 8;
+// Merge of the balanced decode's parts: one work-group of TPW threads per
+// (sequence, KV head), for all G query heads of that head.  A part's G x D
+// partial block is contiguous, so reading a part is one coalesced load of
+// DPL floats per thread (thread = head * TPW/G + chunk).  The parts are
+// folded in order with the log-sum-exp rule, U parts' loads in flight per
+// round trip, and the output written.  One wave and eight parts in flight
+// when the batch has a work-group per CU or more (its sequences have a few
+// parts); with fewer (a few long sequences, each cut into many parts), up to
+// four waves and sixteen parts in flight, so that each sequence costs one
+// round trip (measured on MI355X on eight 32K-128K sequences cut into ~16
+// parts each: the step 389.6 -> 388.8 us).
+template <int G, int TPW, int U>
+__global__ __launch_bounds__(TPW) void merge_balanced_kernel(BalancedArgs k) {
+  constexpr int LPH = TPW / G;         // threads per head
+  constexpr int DPL = kD / LPH;        // dims per thread
+  static_assert(DPL == 2 || DPL % 4 == 0, "dims per thread");
   const AttnArgs& a = k.a;
   const int i = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
   const int lane = threadIdx.x, h = lane / LPH, c = lane % LPH;
@@ -710,39 +715,43 @@ __global__ __launch_bounds__(64) void merge_balanced_kernel(BalancedArgs k) {
   float num[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) num[e] = 0.0f;
-  for (int p0 = 0; p0 < P; p0 += U) {
+  // Parts p0 .. p0 + U - 1.  All U parts' loads are issued unconditionally
+  // (past the last part they re-read it, unused), so that they are in flight
+  // together; the first batch is straight-line code, so nothing before it
+  // (the new rows' loads) is waited for at a loop head.
+  auto batch = [&](int p0) {
     float2 ml[U];
-    float x[U][DPL];   // this lane's DPL dims of part p0 + u (2 floats at G = 1, else whole float4s)
+    float x[U][DPL];   // this thread's DPL dims of part p0 + u
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (p0 + u < P) {
-        const size_t e = (slot0 + p0 + u) * G + h;
-        ml[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
-        const float* src = k.p_acc + e * kD + c * DPL;
-        if constexpr (DPL % 4 == 0) {
+      const size_t e = (slot0 + min(p0 + u, P - 1)) * G + h;
+      ml[u] = reinterpret_cast<const float2*>(k.p_ml)[e];
+      const float* src = k.p_acc + e * kD + c * DPL;
+      if constexpr (DPL % 4 == 0) {
 #pragma unroll
-          for (int v = 0; v < DPL / 4; ++v) {
-            const float4 t = reinterpret_cast<const float4*>(src)[v];
-            x[u][4 * v] = t.x; x[u][4 * v + 1] = t.y; x[u][4 * v + 2] = t.z; x[u][4 * v + 3] = t.w;
-          }
-        } else {
-          static_assert(DPL == 2, "dims per lane");
-          const float2 t = *reinterpret_cast<const float2*>(src);
-          x[u][0] = t.x; x[u][1] = t.y;
+        for (int v = 0; v < DPL / 4; ++v) {
+          const float4 t = reinterpret_cast<const float4*>(src)[v];
+          x[u][4 * v] = t.x; x[u][4 * v + 1] = t.y; x[u][4 * v + 2] = t.z; x[u][4 * v + 3] = t.w;
         }
+      } else {
+        const float2 t = *reinterpret_cast<const float2*>(src);
+        x[u][0] = t.x; x[u][1] = t.y;
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (p0 + u >= P) break;
-      const float Mn = fmaxf(Mx, ml[u].x);
-      const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(ml[u].x - Mn);
-      den = fmaf(den, sa, ml[u].y * sb);
+      if (p0 + u < P) {
+        const float Mn = fmaxf(Mx, ml[u].x);
+        const float sa = fast_exp2(Mx - Mn), sb = fast_exp2(ml[u].x - Mn);
+        den = fmaf(den, sa, ml[u].y * sb);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) num[e] = fmaf(num[e], sa, x[u][e] * sb);
-      Mx = Mn;
+        for (int e = 0; e < DPL; ++e) num[e] = fmaf(num[e], sa, x[u][e] * sb);
+        Mx = Mn;
+      }
     }
-  }
+  };
+  batch(0);
+  for (int p0 = U; p0 < P; p0 += U) batch(p0);
   store_new();
   const float inv = 1.0f / den;
   uint32_t wd[DPL / 2];
@@ -795,7 +804,12 @@ pa_status launch_balanced_g(const BalancedArgs& k, int depth, hipStream_t s) {
   pa_status st = launch_status("pa_forward (decode, balanced)");
   if (st != PA_OK) return st;
   mark = trace_begin(s);
-  hipLaunchKernelGGL((merge_balanced_kernel<G>), dim3(k.a.num_seqs * k.a.num_kv_heads), dim3(64), 0, s, k);
+  const dim3 mgrid(k.a.num_seqs * k.a.num_kv_heads);
+  constexpr int kWide = 64 * (G < 4 ? G : 4);
+  if (k.a.num_seqs * k.a.num_kv_heads < 256 && G > 1)
+    hipLaunchKernelGGL((merge_balanced_kernel<G, kWide, 16>), mgrid, dim3(kWide), 0, s, k);
+  else
+    hipLaunchKernelGGL((merge_balanced_kernel<G, 64, 8>), mgrid, dim3(64), 0, s, k);
   trace_end(s, mark, "merge");
   return launch_status("pa_forward (decode merge, balanced)");
 }
