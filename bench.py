@@ -852,6 +852,7 @@ def main():
         for route in ("verify", "prefill"):
             if route == "prefill":
                 os.environ["PA_VERIFY"] = "prefill"
+                vrun.ensure_workspace()   # the workspace size follows the route
             try:
                 settle(vrun, stream, with_writes=False, min_ms=100)
                 run_steps(vrun, 3, stream, with_writes=False)

@@ -73,14 +73,25 @@ class DeviceRun:
         self.shared_blocks = self.alloc.shared_blocks([self.ids[h] for h in wl.batch])
         self.shared_blocks_d = torch.from_numpy(self.shared_blocks).to(self.dev)
         self.workspace = None
-        size = pa.pa_forward_shared_workspace_size if shared else pa.pa_forward_workspace_size
-        ws = size(wl.num_seqs, wl.num_tokens, wl.num_q_heads, self.max_seq_len, wl.max_query_len, self.k_cache)
-        if ws:
-            self.workspace = pa.new_workspace(ws, self.dev)
+        self.ensure_workspace()
         self.fill_context()
         self.pools = [(self.k_cache, self.v_cache)]
         for _ in range(1, copies):
             self.pools.append((self.k_cache.clone(), self.v_cache.clone()))
+
+    def ensure_workspace(self):
+        """Size the workspace for the call as the library would make it now.
+
+        The size depends on the routing knobs in the environment (PA_VERIFY,
+        PA_DECODE, ...): call this again after changing them.  A larger
+        workspace replaces the old one (and the calls bound to it).
+        """
+        wl = self.wl
+        size = pa.pa_forward_shared_workspace_size if self.shared else pa.pa_forward_workspace_size
+        ws = size(wl.num_seqs, wl.num_tokens, wl.num_q_heads, self.max_seq_len, wl.max_query_len, self.k_cache)
+        if ws and (self.workspace is None or self.workspace.numel() < ws):
+            self.workspace = pa.new_workspace(ws, self.dev)
+            self._bound_calls = {}
 
     def use(self, copy):
         """Make pool copy ``copy`` the one later calls read and write."""
