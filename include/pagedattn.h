@@ -232,6 +232,12 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_PREFILL_SPLIT=auto (default) | off | <keys>   chunked prefill: keys per
  *            piece of a query tile's key range (rounded up to a multiple of 64); auto uses
  *            max(1024, a quarter of the longest sequence)
+ *   PA_PREFILL_ORDER=auto (default) | pieces | sequences   chunked prefill:
+ *            order of the work-groups -- key-range pieces slowest, or
+ *            sequences slowest (the last sequence of the batch first, so a
+ *            batch that lists its decode sequences before its chunks
+ *            dispatches the chunks' work first); auto: sequences when
+ *            num_seqs * max_query_len > 2 * num_tokens
  * Errors: PA_ERR_ARG (incl. a workspace smaller than required),
  * PA_ERR_UNSUPPORTED, PA_ERR_RANGE (check mode), PA_ERR_HIP.
  */

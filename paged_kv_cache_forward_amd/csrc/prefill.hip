@@ -131,30 +131,43 @@ struct PrefillArgs {
   int32_t pieces;       // pieces of the longest key range
   uint16_t* p_o;        // [num_tokens][Hq][pieces][D] partial outputs: fp16, normalised, scaled by 2^-e
   float* p_ml;          // [num_tokens][Hq][pieces][4] partial (max in base-2 units, sum, e, 0)
+  int32_t seq_major;    // work-group order: sequences slowest (else pieces slowest)
 };
 
 // Which (KV head, query tile, sequence, piece) a work-group handles.  KV head
-// fastest (every work-group of one KV head on one XCD); pieces slowest and in
-// descending order, because only long key ranges have high pieces: the
-// longest work is dispatched first and the short pieces fill the tail.
-// Sequences go in descending batch order: a super-batch puts its decode
+// fastest (every work-group of one KV head on one XCD), then query tiles.
+// Sequences go in descending batch order: a super-batch lists its decode
 // sequences before the prefill chunks, and the work-groups of a decode
 // sequence find no rows and exit, but each holds an LDS slot for a memory
 // round trip first; dispatched after the chunks' work-groups, they fill the
 // tail instead of delaying real work.
+//  - Pieces slowest (descending; the default): the work-groups in flight
+//    together read the same piece of every chunk's key range, a working set
+//    that the L2 of each XCD holds.  But every piece level has the decode
+//    sequences' empty work-groups after its chunks.
+//  - Sequences slowest (seq_major, for batches where most of the grid is
+//    empty): all of a chunk's pieces (ascending) before the next chunk, so
+//    the empty work-groups of a decode-first batch all come last.
 struct PrefillItem {
   int g, p, qt, i;
 };
-__device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces, int qtiles, int num_seqs) {
+__device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces, int qtiles, int num_seqs,
+                                                    bool seq_major) {
   PrefillItem it;
   it.g = wg % Hkv;
   int r = wg / Hkv;
   it.qt = qtiles - 1 - r % qtiles;
   r /= qtiles;
-  it.i = num_seqs - 1 - r % num_seqs;
-  it.p = pieces - 1 - r / num_seqs;
+  if (seq_major) {
+    it.p = r % pieces;
+    it.i = num_seqs - 1 - r / pieces;
+  } else {
+    it.i = num_seqs - 1 - r % num_seqs;
+    it.p = pieces - 1 - r / num_seqs;
+  }
   return it;
 }
+
 
 // RT = 2: 32 rows per wave, two waves per SIMD.  RT = 4: 64 rows per wave --
 // each K/V fragment read from LDS feeds twice the MFMAs -- with the output
@@ -178,15 +191,33 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
   const int TOK = kRowsPerWG / G;
-  const PrefillItem it = prefill_item(blockIdx.x, Hkv, pk.pieces, pk.qtiles, a.num_seqs);
+  const PrefillItem it = prefill_item(blockIdx.x, Hkv, pk.pieces, pk.qtiles, a.num_seqs, pk.seq_major);
   const int g = it.g, qt = it.qt, i = it.i;
+  const int tid = threadIdx.x, lane = tid & 63;
+
+  // The block table of the work-group's key range passes through LDS in
+  // windows of kBtCache entries; a window is refilled (behind a barrier) when
+  // the loads reach it, so no global load sits inside the tile loop.  The
+  // entries of the first window depend only on the sequence and the piece:
+  // one per thread, from the piece's first block, is loaded together with the
+  // sequence's lengths, in one memory round trip (entries past the piece's
+  // range, still inside the table's row, are loaded and not used).
+  const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
+  const int kt0 = it.p * (pk.piece_keys / kKeys);
+  int cur_win = kt0 * (kKeys / kBlock) / kBtCache;
+  const int bt_spec = kt0 * (kKeys / kBlock) - cur_win * kBtCache + tid;   // this thread's entry of the window
+  const int bt_val =
+      bt_spec < kBtCache && cur_win * kBtCache + bt_spec < a.bt_stride ? bt_row[cur_win * kBtCache + bt_spec] : 0;
+  const int c = a.cached_lens[i];
+  const int L_raw = a.seq_lens[i];
   const int q0 = a.qsl[i];
-  const int n = a.qsl[i + 1] - q0;
+  const int q1 = a.qsl[i + 1];
+  asm volatile("" ::"s"(c), "s"(L_raw), "s"(q0), "s"(q1), "v"(bt_val));   // all five loads issued before the checks
+  const int n = q1 - q0;
   if (n < max(a.prefill_min_q, 2) || q0 < 0 || q0 + n > a.num_tokens) return;
   const int tok0 = qt * TOK;
   if (tok0 >= n) return;
-  const int L = min(a.seq_lens[i], a.bt_stride * kBlock);
-  const int c = a.cached_lens[i];
+  const int L = min(L_raw, a.bt_stride * kBlock);
   const int tok_last = min(tok0 + TOK, n) - 1;
   const int kv_end = a.causal ? min(L, c + tok_last + 1) : L;
   if (kv_end <= 0) return;
@@ -196,25 +227,16 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
   if (k_lo >= kv_end) return;
   const int k_hi = it.p == pk.pieces - 1 ? kv_end : min(k_lo + pk.piece_keys, kv_end);
   const bool split = kv_end > pk.piece_keys && pk.pieces > 1;   // partials instead of the output
-  const int kt0 = k_lo / kKeys;
   const int kt_end = (k_hi + kKeys - 1) / kKeys;
-  const int ntiles = kt_end - kt0;
   const int nblk = (k_hi + kBlock - 1) / kBlock;
 
-  const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lq = lane >> 4;
 
-  // The block table of the work-group's key range passes through LDS in
-  // windows of kBtCache entries; a window is refilled (behind a barrier) when
-  // the loads reach it, so no global load sits inside the tile loop.
-  const int32_t* bt_row = a.block_tables + (size_t)i * a.bt_stride;
   auto fill_window = [&](int win) {
     const int b0 = win * kBtCache;
     for (int b = tid; b < min(nblk - b0, kBtCache); b += kThreads) s_bt[b] = clamp_block(bt_row[b0 + b], a.num_blocks);
   };
-  int cur_win = kt0 * (kKeys / kBlock) / kBtCache;
-  fill_window(cur_win);
 
   // Query fragments (B operand of S^T = K Q^T): lane holds 8 head-dim values of
   // its row: dims 32 ks + 8 lq (bf16 cache); 64 (ks / 2) + 16 lq + 8 (ks % 2)
@@ -235,6 +257,15 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
       const uint4 v = ok ? ld16(qp + qoff) : make_uint4(0u, 0u, 0u, 0u);
       qf[rt][ks] = __builtin_bit_cast(bf16x8_t, v);
     }
+  }
+  // The first window's entries, behind the query loads (still in flight): the
+  // one already loaded, then any further ones of a range of more than
+  // kThreads blocks.
+  {
+    const int win_end = min(nblk - cur_win * kBtCache, kBtCache);
+    if (bt_spec < win_end) s_bt[bt_spec] = clamp_block(bt_val, a.num_blocks);
+    for (int b = bt_spec + kThreads; b < win_end; b += kThreads)
+      s_bt[b] = clamp_block(bt_row[cur_win * kBtCache + b], a.num_blocks);
   }
 
   // Exponent arguments are cs * s - m in base-2 units (cs = |scale| log2 e),
@@ -277,15 +308,6 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
   // fp8: the exponent plane after all code tiles, 16 bytes per tile.
   const uint8_t* kx = (const uint8_t*)a.k_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
   const uint8_t* vx = (const uint8_t*)a.v_cache + (size_t)a.num_blocks * block_stride + (size_t)g * kBlock;
-
-  // The query fragments are loaded by ordinary global loads, which the
-  // compiler tracks: without a wait it can see here, it waits for them
-  // (vmcnt(0)) at their first use inside the tile loop, on every iteration,
-  // and that wait also drains the untracked copies of the next tile issued
-  // just before -- serialising copy and compute.  s_waitcnt vmcnt(0)
-  // (simm16 0x0F70: expcnt and lgkmcnt left at their maxima) retires them here.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();   // first block-table window ready
 
   auto block_id = [&](int b) -> int {   // b < nblk, inside the current window, wave-uniform
     return __builtin_amdgcn_readfirstlane(s_bt[b - cur_win * kBtCache]);
@@ -518,8 +540,16 @@ __global__ __launch_bounds__(64 * NW, RT >= 4 || NW >= 8 ? 1 : 2) void prefill_k
   // Pipeline: tile kt+1 is copied into the other LDS stage while tile kt is
   // computed; each wave then waits for its own copies, and the barrier makes
   // every wave's copies visible (and frees the stage just read for refill).
+  __syncthreads();   // first block-table window ready
   dma_tile(kt0, 0);
-  PA_VM_WAIT(0);
+  // The query fragments are loaded by ordinary global loads, which the
+  // compiler tracks: without a wait it can see here, it waits for them
+  // (vmcnt(0)) at their first use inside the tile loop, on every iteration,
+  // and that wait also drains the untracked copies of the next tile issued
+  // just before -- serialising copy and compute.  s_waitcnt vmcnt(0)
+  // (simm16 0x0F70: expcnt and lgkmcnt left at their maxima) retires them
+  // here, together with the first tile's copies: one round trip for both.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (int kt = kt0; kt < kt_end; kt += 2) {
     dma_tile(kt + 1, 1);
@@ -599,7 +629,7 @@ __global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(PrefillArg
   const AttnArgs& a = pk.a;
   const int Hkv = a.num_kv_heads;
   const int G = a.num_q_heads / Hkv;
-  const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.mqtiles, a.num_seqs);
+  const PrefillItem it = prefill_item(blockIdx.x, Hkv, 1, pk.mqtiles, a.num_seqs, false);
   const int q0 = a.qsl[it.i];
   const int n = a.qsl[it.i + 1] - q0;
   if (n < max(a.prefill_min_q, 2) || q0 < 0 || q0 + n > a.num_tokens) return;
@@ -742,7 +772,17 @@ pa_status launch_prefill(const AttnArgs& a, int32_t max_query_len, const Prefill
   // with 256-row prefill tiles that doubles its work-groups.
   const int MTOK = TOK * G > 128 && TOK % 2 == 0 ? TOK / 2 : TOK;
   const int mqtiles = (max_query_len + MTOK - 1) / MTOK;
-  PrefillArgs k{a, TOK, MTOK, mqtiles, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml};
+  // Sequences-slowest order where most of the (sequence, query tile) grid
+  // has no rows (the query tokens would fill fewer than half of it).
+  // Measured on MI355X, 16 decode sequences + 4 chunks of 512 tokens: 154.8
+  // -> 148.7 us (the four chunks alone: 142.8 us in the default order, 149.0
+  // in this one).  PA_PREFILL_ORDER=pieces|sequences overrides.
+  int seq_major = (int64_t)a.num_seqs * max_query_len > 2 * (int64_t)a.num_tokens;
+  if (const char* env = std::getenv("PA_PREFILL_ORDER")) {
+    if (std::strcmp(env, "sequences") == 0) seq_major = 1;
+    else if (std::strcmp(env, "pieces") == 0) seq_major = 0;
+  }
+  PrefillArgs k{a, TOK, MTOK, mqtiles, qtiles, pp.piece_keys, pp.pieces, p_o, p_ml, seq_major};
   if (fp8 && a.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_forward: fp8 prefill head_dim %d", a.head_dim);
   int mark = trace_begin(s);
   const dim3 grid((unsigned)wgs), block(64 * nw);

@@ -12,14 +12,16 @@ pools bit for bit, every output row within the stated tolerance.  The cache
 families rotate over bf16 head_dim 128, bf16 head_dim 64, fp32 and fp8 (bf16
 rows on E4M3 codes); the bf16 and fp32 batches also run with the single-token
 rows kept apart from the multi-token kernel (PA_VERIFY=split) and with the
-multi-token rows sent to the chunked-prefill kernel (PA_VERIFY=prefill).
+multi-token rows sent to the chunked-prefill kernel (PA_VERIFY=prefill).  A
+second pass runs each batch with the chunked-prefill work-groups in both
+orders (PA_PREFILL_ORDER=sequences / pieces).
 """
 
 import numpy as np
 import pytest
 
 import workloads
-from test_gpu_parity import check_parity
+from test_gpu_parity import _device_run, check_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -55,3 +57,23 @@ def test_random_mixed_batch(seed, monkeypatch):
             monkeypatch.setenv("PA_VERIFY", route)
         print(f"[random-mixed] seed {seed}: {what}, route {route or 'default'}", flush=True)
         check_parity(wl)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_prefill_work_group_orders(seed, monkeypatch):
+    """The chunked-prefill work-groups ordered sequences-slowest
+    (PA_PREFILL_ORDER=sequences) and pieces-slowest (=pieces): both meet the
+    tolerance against the oracle, with bit-identical outputs (the same work
+    items, handed to different work-groups).  Multi-token rows go to the
+    prefill kernel (PA_VERIFY=prefill) except on fp8 pools."""
+    wl, what = random_batch(seed)
+    for key in ("PA_VERIFY", "PA_DECODE", "PA_CHECK", "PA_PREFILL_ORDER"):
+        monkeypatch.delenv(key, raising=False)
+    if wl.cache != "fp8":
+        monkeypatch.setenv("PA_VERIFY", "prefill")
+    monkeypatch.setenv("PA_PREFILL_ORDER", "sequences")
+    print(f"[random-mixed] seed {seed}: {what}, prefill work-group orders", flush=True)
+    seq, _ = check_parity(wl)
+    monkeypatch.setenv("PA_PREFILL_ORDER", "pieces")
+    pieces = _device_run(wl)
+    assert np.array_equal(seq.out_f64(), pieces.out_f64())
