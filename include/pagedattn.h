@@ -221,6 +221,10 @@ size_t pa_forward_workspace_size(int32_t num_seqs, int32_t num_tokens, int32_t n
  *   PA_VERIFY=all           send single-token sequences through the multi-token
  *            decode path too (one launch for both kinds)
  *   PA_VERIFY_TOTAL_WAVES=<1..65536>  multi-token decode: waves in all (default 1024)
+ *   PA_VERIFY_FIRST_WEIGHT=<500..2000>  multi-token decode with more waves
+ *            than SIMDs (up to two per SIMD): tiles taken by the waves
+ *            dispatched first on each SIMD, per 1000 taken by the others
+ *            (default 1350; 1000 = equal ranges)
  *   PA_VERIFY_DEPTH=2..5    multi-token decode: K/V tiles in flight per wave
  *            (bf16: default 3, or 2 when four work-groups would not fit a
  *            CU's LDS; 4 and 5 both run 4.  fp8 cache: default 3; 5 runs 5,

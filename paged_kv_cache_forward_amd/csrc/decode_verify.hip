@@ -72,9 +72,30 @@ struct VerifyArgs {
   uint16_t* p_acc;          // [Hkv][slots][CG][8 db][64 lanes][4] fp16: fragment order (see finish)
   float* p_ml;              // [Hkv][slots][16 CG][4]  (max in base-2 units, sum, e, 0)
   int2* seqinfo;            // [num_seqs]: (first rank, parts)
+  int32_t first_ranks;      // ranks dispatched first on their SIMD (the lowest work-group ids) ...
+  int32_t first_weight;     // ... take this many tiles per 1000 of the others' (see make_verify_plan)
 };
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Weighted split of a head's tile stream: ranks below h weigh wa, the others
+// wb, and rank r takes tiles [start(r), start(r + 1)), its share of `total` in
+// proportion to the weights before it.  wa = wb gives stream_start's ranges.
+// Every range is non-empty when total * min(wa, wb) >= the weight sum.
+struct StreamSplit {
+  int64_t total;
+  int Wg, h, wa, wb;
+  __device__ int64_t cum(int r) const {
+    return r <= h ? (int64_t)r * wa : (int64_t)h * wa + (int64_t)(r - h) * wb;
+  }
+  __device__ int64_t start(int r) const { return total * cum(r) / cum(Wg); }
+  // The largest r with start(r) <= t, for 0 <= t < total.
+  __device__ int owner(int64_t t) const {
+    const int64_t x = ((t + 1) * cum(Wg) - 1) / total;   // largest weight prefix with start <= t
+    const int64_t hx = (int64_t)h * wa;
+    return x < hx ? (int)(x / wa) : h + (int)((x - hx) / wb);
+  }
+};
 
 // Dynamic LDS: tile prefix sums [S + 1], query row << 5 | (tokens - 1) [S], length [S].
 inline size_t verify_dyn_lds(int num_seqs) { return (size_t)(3 * num_seqs + 1) * sizeof(int); }
@@ -204,8 +225,13 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
   const int64_t total = carry;
   const int Wg = (int)min((int64_t)k.waves_per_head, total);
   if (rank >= Wg) return;
-  const int tb = (int)stream_start(rank, total, Wg);
-  const int cnt = (int)(stream_start(rank + 1, total, Wg) - tb);
+  // Ranks split the head's tile stream by weight: those of the first-dispatched
+  // waves on each SIMD take first_weight / 1000 times the others' share,
+  // whenever that leaves every range non-empty (else equal ranges).
+  StreamSplit sp{total, Wg, min(k.first_ranks, Wg), k.first_weight, 1000};
+  if (sp.h >= Wg || total * 1000 < 2 * (int64_t)Wg * max(sp.wa, 1000)) sp.wa = sp.wb = 1;
+  const int tb = (int)sp.start(rank);
+  const int cnt = (int)(sp.start(rank + 1) - tb);
 
   const u32x4_t rbt = rsrc_words((const uint8_t*)a.block_tables,
                                  (int)min((int64_t)S * a.bt_stride * 4, (int64_t)0x7fffffff));
@@ -406,7 +432,7 @@ __global__ __launch_bounds__(64) void decode_verify_kernel(VerifyArgs k) {
           col_end[cg] = a.causal ? min(L, L - cur_n + (16 * cg + j) / G + 1) : L;
         cur_j0 = jt;
         if (jt == 0 && g == 0 && lane == 0) {
-          const int last = stream_owner((int64_t)s_cum[seq + 1] - 1, total, Wg);
+          const int last = sp.owner((int64_t)s_cum[seq + 1] - 1);
           k.seqinfo[seq] = make_int2(rank, last - rank + 1);
         }
         // This sequence's query copy was followed by the issues of tiles
@@ -708,6 +734,25 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   const int64_t whole_tiles = ((int64_t)max_seq_len + kBlock - 1) / kBlock;
   const int64_t wg = std::max<int64_t>(1, std::min<int64_t>(target / num_kv_heads, (int64_t)num_seqs * whole_tiles));
   vp.waves_per_head = (int32_t)wg;
+  // With more waves than SIMDs (up to two per SIMD: 256 CUs x 4), the
+  // work-groups dispatched first -- the lowest ids, one per SIMD -- keep the
+  // older wave's issue priority over the second wave on their SIMD for the
+  // whole launch.  Measured on MI355X (fp8 batched decode, 2048 waves, equal
+  // ranges): the first 1024 stream their tiles 1.18x as fast as the others
+  // and finish 7.5 us earlier.  Their ranks take 1.18x the tiles.
+  // PA_VERIFY_FIRST_WEIGHT=<500..2000> (per 1000) overrides the ratio.
+  constexpr int64_t kSimds = 1024;
+  const int64_t waves = wg * num_kv_heads;
+  vp.first_ranks = (int32_t)wg;
+  vp.first_weight = 1000;
+  if (waves > kSimds && waves <= 2 * kSimds) {
+    vp.first_ranks = (int32_t)(kSimds / num_kv_heads);
+    vp.first_weight = 1350;
+  }
+  if (const char* fw = std::getenv("PA_VERIFY_FIRST_WEIGHT")) {
+    const int v = std::atoi(fw);
+    if (v >= 500 && v <= 2000) vp.first_weight = v;
+  }
   // bf16: three tiles in flight while four work-groups still fit in a CU's
   // LDS, else two.  fp8: three (measured on MI355X: deeper rings of the
   // half-size fp8 tiles were slower).  PA_VERIFY_DEPTH=2..5 overrides (fp8: 3 or 5).
@@ -725,7 +770,8 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
 
 pa_status launch_decode_verify(const AttnArgs& a, const VerifyPlan& vp, uint16_t* p_acc, float* p_ml,
                                int32_t* part_table, hipStream_t s) {
-  VerifyArgs k{a, vp.min_q, vp.max_q, vp.waves_per_head, a.num_seqs + vp.waves_per_head, p_acc, p_ml, (int2*)part_table};
+  VerifyArgs k{a, vp.min_q, vp.max_q, vp.waves_per_head, a.num_seqs + vp.waves_per_head, p_acc, p_ml,
+               (int2*)part_table, vp.first_ranks, vp.first_weight};
   const int G = a.num_q_heads / a.num_kv_heads;
   const bool f8 = vp.fp8;
   switch (G * 16 + vp.col_groups) {

@@ -115,6 +115,8 @@ struct VerifyPlan {
   int32_t max_q;           // longest sequence (query tokens) it takes; longer ones go to prefill
   int32_t waves_per_head;
   int32_t depth;           // K/V tiles in flight per wave (2 or 3)
+  int32_t first_ranks;     // ranks of each head whose work-groups are dispatched first on their SIMD
+  int32_t first_weight;    // their share of tiles per 1000 of the other ranks'
   size_t info_bytes, acc_bytes, ml_bytes;
   size_t workspace_bytes() const { return info_bytes + acc_bytes + ml_bytes; }
 };

@@ -185,6 +185,23 @@ def test_multi_token_decode_wave_counts(waves, monkeypatch):
         check_parity(workloads.mini(name), pools=False)
 
 
+@pytest.mark.parametrize("weight", ["500", "1000", "2000"])
+def test_multi_token_decode_first_wave_weights(weight, monkeypatch):
+    """fp8 decode at two waves per SIMD (2048 in all): the ranks of the waves
+    dispatched first on each SIMD take `weight` tiles per 1000 of the others'
+    (PA_VERIFY_FIRST_WEIGHT); any weight meets the tolerance.  16 sequences of
+    1000-3000 tokens, so every rank keeps a non-empty range at each weight."""
+    ensure_library()
+    monkeypatch.delenv("PA_VERIFY", raising=False)
+    monkeypatch.delenv("PA_VERIFY_TOTAL_WAVES", raising=False)
+    monkeypatch.setenv("PA_VERIFY_FIRST_WEIGHT", weight)
+    rng = np.random.default_rng(61)
+    lens = rng.integers(1000, 3001, size=16)
+    wl = workloads.independent("verify_fp8_weights", 61, Hq=32, Hkv=8, D=128, dtype="bf16",
+                               cached=(lens - 1).tolist(), new=[1] * 16, pool_extra=2, cache_dtype="fp8")
+    check_parity(wl, pools=False)
+
+
 def test_multi_token_decode_routes():
     """Sequences of 2 .. 16 query tokens: column groups 1, 2 and 4 (set by the longest
     one), the cap per group size (longer sequences go to prefill in the same call),
