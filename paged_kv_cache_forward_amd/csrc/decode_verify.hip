@@ -739,8 +739,11 @@ VerifyPlan make_verify_plan(int32_t num_seqs, int32_t num_tokens, int32_t num_q_
   // older wave's issue priority over the second wave on their SIMD for the
   // whole launch.  Measured on MI355X (fp8 batched decode, 2048 waves, equal
   // ranges): the first 1024 stream their tiles 1.18x as fast as the others
-  // and finish 7.5 us earlier.  Their ranks take 1.18x the tiles.
-  // PA_VERIFY_FIRST_WEIGHT=<500..2000> (per 1000) overrides the ratio.
+  // and finish 7.5 us earlier.  Their ranks (ids below 1024 are the ranks
+  // below 1024 / Hkv in either work-group mapping, for Hkv dividing 128) take
+  // 1.35x the tiles: swept from 1.0 to 2.0, the kernel was fastest at
+  // 1.35-1.5 (54.8 -> 52.5 us).  PA_VERIFY_FIRST_WEIGHT=<500..2000> (per
+  // 1000) overrides the ratio.
   constexpr int64_t kSimds = 1024;
   const int64_t waves = wg * num_kv_heads;
   vp.first_ranks = (int32_t)wg;

@@ -168,7 +168,6 @@ __device__ __forceinline__ PrefillItem prefill_item(int wg, int Hkv, int pieces,
   return it;
 }
 
-
 // RT = 2: 32 rows per wave, two waves per SIMD.  RT = 4: 64 rows per wave --
 // each K/V fragment read from LDS feeds twice the MFMAs -- with the output
 // accumulators in AGPRs at one wave per SIMD.  NW = 8: 256 rows per
